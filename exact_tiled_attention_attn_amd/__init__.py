@@ -1,0 +1,24 @@
+"""Exact tiled scaled-dot-product attention for MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+``include/attn.h`` (``libattn.so``, built in-tree by
+``python -m exact_tiled_attention_attn_amd.build``).  This package is the
+thin Python binding: ``fwd`` / ``bwd`` / ``debug_tile_map`` marshal torch
+device tensors into the ABI and allocate outputs and workspace with torch.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    MASK_MODES,
+    AttnError,
+    AttnProblem,
+    bwd,
+    debug_tile_map,
+    fwd,
+    load_library,
+    make_problem,
+    workspace_size,
+)
+
+__all__ = ["fwd", "bwd", "debug_tile_map", "workspace_size", "load_library", "AttnError"]

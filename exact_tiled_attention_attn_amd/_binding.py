@@ -1,0 +1,196 @@
+"""ctypes binding of libattn.so (include/attn.h).
+
+Argument marshalling only: torch provides device memory (outputs and
+workspace) and the current HIP stream; every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the library is
+missing or fails to load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+MASK_MODES = {"none": 0, "causal": 1, "bitmask": 2}
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_STRIDE",
+    4: "ATTN_ERR_DTYPE", 5: "ATTN_ERR_MASK", 6: "ATTN_ERR_UNSUPPORTED",
+    7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP",
+}
+EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map",
+           "attn_status_str", "attn_last_error", "attn_version"]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class AttnProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("n", ctypes.c_int64),
+        ("d", ctypes.c_int64), ("v", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("mask_mode", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+        ("mask", ctypes.c_void_p),
+        ("mask_sb", ctypes.c_int64), ("mask_sh", ctypes.c_int64), ("mask_si", ctypes.c_int64),
+        ("sq", ctypes.c_int64 * 3), ("sk", ctypes.c_int64 * 3),
+        ("sv", ctypes.c_int64 * 3), ("so", ctypes.c_int64 * 3),
+        ("deterministic", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libattn.so once; raise if it is absent (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build it with `python -m exact_tiled_attention_attn_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(AttnProblem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.attn_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.attn_debug_tile_map.argtypes = [P, ctypes.c_int, vp, sz, i32p, i32p, i32p, i32p, vp, sz, vp]
+    for f in ("attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != 0:
+        raise AttnError(st, load_library().attn_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, deterministic=False) -> AttnProblem:
+    """Fill the ABI problem struct from [B, H, n, .] tensors (strides in elements)."""
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, n, dim]")
+    B, H, n, d = q.shape
+    p = AttnProblem()
+    p.B, p.H, p.n, p.d, p.v = B, H, n, d, v.shape[-1]
+    p.dtype = _dtype_code(q)
+    p.mask_mode = MASK_MODES[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
+    p.scale = float(scale)
+    for name, t in (("sq", q), ("sk", k), ("sv", v), ("so", o_like)):
+        if t.stride(-1) != 1:
+            raise ValueError("last dimension must be contiguous")
+        arr = getattr(p, name)
+        for i in range(3):
+            arr[i] = t.stride(i)
+    if mask is not None:
+        m = mask
+        if m.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("mask must be int32/uint32 words")
+        if m.dim() == 3:  # [H, n, words]: shared across the batch
+            p.mask_sb, p.mask_sh, p.mask_si = 0, m.stride(0), m.stride(1)
+        elif m.dim() == 4:  # [B, H, n, words]
+            p.mask_sb, p.mask_sh, p.mask_si = m.stride(0), m.stride(1), m.stride(2)
+        else:
+            raise ValueError("mask must be [H, n, words] or [B, H, n, words]")
+        p.mask = m.data_ptr()
+    p.deterministic = int(bool(deterministic))
+    return p
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_size(p: AttnProblem, is_bwd: bool) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.attn_workspace_size(ctypes.byref(p), int(is_bwd), ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, workspace=None):
+    """O [B,H,n,v] (dtype of q) and L [B,H,n] (fp32 natural-log logsumexp)."""
+    lib = load_library()
+    B, H, n, _ = q.shape
+    o = out if out is not None else torch.empty((B, H, n, v.shape[-1]), dtype=q.dtype, device=q.device)
+    L = lse if lse is not None else torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    p = make_problem(q, k, v, o, scale, mask_mode, mask)
+    need = workspace_size(p, False)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
+                        _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel()), _stream()))
+    return o, L
+
+
+def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=None, dv=None,
+        workspace=None):
+    """dQ, dK, dV (dtype of q) from the forward's O and L and the upstream dO."""
+    lib = load_library()
+    if do.stride() != o.stride():
+        if not o.is_contiguous():
+            raise ValueError("dO must have the strides of O")
+        do = do.contiguous()
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("dQ, dK, dV must have the strides of Q, K, V")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, n]")
+    p = make_problem(q, k, v, o, scale, mask_mode, mask)
+    need = workspace_size(p, True)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                        ctypes.c_size_t(0 if ws is None else ws.numel()), _stream()))
+    return dq, dk, dv
+
+
+def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=False):
+    """The kernels' (query tile x key tile) classification as uint8 [units, tq, tk]."""
+    lib = load_library()
+    p = make_problem(q, k, v, v, scale, mask_mode, mask)
+    bq, bk, tq, tk = (ctypes.c_int32() for _ in range(4))
+    _check(lib.attn_debug_tile_map(ctypes.byref(p), int(is_bwd), None, 0, ctypes.byref(bq),
+                                   ctypes.byref(bk), ctypes.byref(tq), ctypes.byref(tk), None, 0,
+                                   _stream()))
+    units = 1 if p.mask_mode != 2 else (p.H if p.mask_sb == 0 else p.B * p.H)
+    out = torch.empty((units, tq.value, tk.value), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_debug_tile_map(ctypes.byref(p), int(is_bwd), _ptr(out), out.numel(),
+                                   ctypes.byref(bq), ctypes.byref(bk), ctypes.byref(tq),
+                                   ctypes.byref(tk), None, 0, _stream()))
+    return out, bq.value, bk.value

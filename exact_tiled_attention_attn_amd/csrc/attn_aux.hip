@@ -1,0 +1,161 @@
+// Memory-bound helper kernels of the attention path.
+//
+// * tile_map_kernel: classifies every (query tile, key tile) pair of an
+//   explicit allowed-key bitmask as empty (skipped), partial (masked inside)
+//   or full, so that the compute kernels skip blocks with no allowed key
+//   (alphabetamath page, forward step 2) and mask only partial ones (ob1
+//   page, part 3).  Integer OR/AND over the mask words: HBM-bound.
+// * bwd_pre_kernel: D_i = <dO_i, O_i> in fp32 (HarshvardhanJ README,
+//   backward section: D costs O(n d) and replaces a pass over P; ob1 page,
+//   part 2) and clears the fp32 dQ accumulator.
+// * bwd_post_kernel: dQ = c * accumulator, converted to the output type.
+#include "attn_internal.h"
+#include "kern_common.h"
+
+namespace eta {
+
+__global__ __launch_bounds__(256) void tile_map_kernel(MapParams p) {
+  const int mu = blockIdx.x / p.tq;
+  const int a = blockIdx.x % p.tq;
+  const int64_t n = p.n;
+  const int64_t q0 = (int64_t)a * p.bq;
+  const int64_t q1 = (q0 + p.bq < n) ? q0 + p.bq : n;
+  uint8_t* out = p.map + ((int64_t)mu * p.tq + a) * p.tk;
+  if (p.mask_mode != kMaskBitmask) {
+    for (int kt = threadIdx.x; kt < p.tk; kt += blockDim.x)
+      out[kt] = classify_analytic(p.mask_mode, q0, p.bq, (int64_t)kt * p.bk, p.bk, n);
+    return;
+  }
+  int64_t base;
+  if (p.units == p.H) {
+    base = (int64_t)mu * p.mask_sh;  // mask shared across the batch
+  } else {
+    base = (int64_t)(mu / p.H) * p.mask_sb + (int64_t)(mu % p.H) * p.mask_sh;
+  }
+  const int64_t W = (n + 31) / 32;
+  const uint32_t tail_bits = (n % 32) ? ((1u << (n % 32)) - 1u) : 0xFFFFFFFFu;
+  const int wpt = p.bk / 32;  // words per key tile
+  for (int kt = threadIdx.x; kt < p.tk; kt += blockDim.x) {
+    uint32_t any = 0;
+    bool all = (int64_t)(kt + 1) * p.bk <= n;
+    for (int64_t r = q0; r < q1; ++r) {
+      const uint32_t* row = p.mask + base + r * p.mask_si;
+      for (int wi = 0; wi < wpt; ++wi) {
+        const int64_t wd = (int64_t)kt * wpt + wi;
+        if (wd < W) {
+          const uint32_t valid = (wd == W - 1) ? tail_bits : 0xFFFFFFFFu;
+          const uint32_t x = row[wd] & valid;
+          any |= x;
+          all = all && (x == valid);
+        }
+      }
+    }
+    out[kt] = any ? (all ? kTileFull : kTilePartial) : kTileEmpty;
+  }
+}
+
+int launch_tile_map(const MapParams& p, void* stream) {
+  const int64_t blocks = (int64_t)p.units * p.tq;
+  if (blocks <= 0) return 0;
+  hipLaunchKernelGGL(tile_map_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int DV>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_n4) {
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int VCH = DV * ES / 16;  // 16-byte chunks per row
+  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  const int64_t row = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+  const int sub = threadIdx.x % 16;
+  float acc = 0.f;
+  if (row < rows) {
+    const int64_t unit = row / p.n, i = row % p.n;
+    const int64_t b = unit / p.H, h = unit % p.H;
+    const int64_t off = (b * p.so[0] + h * p.so[1] + i * p.so[2]) * ES;
+    const char* Op = (const char*)p.O + off;
+    const char* Gp = (const char*)p.dO + off;
+    for (int c = sub; c < VCH; c += 16) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(Op + c * 16);
+      const u32x4 g = *reinterpret_cast<const u32x4*>(Gp + c * 16);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc += bf16_bits_to_f32(x[e] & 0xFFFFu) * bf16_bits_to_f32(g[e] & 0xFFFFu);
+          acc += bf16_bits_to_f32(x[e] >> 16) * bf16_bits_to_f32(g[e] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += __uint_as_float(x[e]) * __uint_as_float(g[e]);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 8, 16);
+  acc += __shfl_xor(acc, 4, 16);
+  acc += __shfl_xor(acc, 2, 16);
+  acc += __shfl_xor(acc, 1, 16);
+  if (row < rows && sub == 0) p.Dv[row] = acc;
+  // Clear the dQ accumulator (grid-stride over float4s).
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < zero_n4; k += stride)
+    reinterpret_cast<f32x4*>(p.dQacc)[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, void* stream) {
+  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  const int64_t blocks = (rows + 15) / 16;
+  const int64_t zero_n4 = rows * d / 4;
+  hipStream_t st = (hipStream_t)stream;
+  dim3 g((unsigned)blocks), b(256);
+#define ETA_PRE(BF, DVV) hipLaunchKernelGGL((bwd_pre_kernel<BF, DVV>), g, b, 0, st, p, zero_n4)
+  if (bf16) {
+    if (v == 64) ETA_PRE(true, 64); else if (v == 80) ETA_PRE(true, 80); else ETA_PRE(true, 128);
+  } else {
+    if (v == 64) ETA_PRE(false, 64); else if (v == 80) ETA_PRE(false, 80); else ETA_PRE(false, 128);
+  }
+#undef ETA_PRE
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_post_kernel(BwdParams p, int d) {
+  const int64_t q4 = d / 4;  // float4 groups per row
+  const int64_t total = (int64_t)p.B * p.H * p.n * q4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < total; k += stride) {
+    const int64_t row = k / q4, c4 = k % q4;
+    const int64_t unit = row / p.n, i = row % p.n;
+    const int64_t b = unit / p.H, h = unit % p.H;
+    const f32x4 x = reinterpret_cast<const f32x4*>(p.dQacc)[k];
+    const int64_t off = b * p.sq[0] + h * p.sq[1] + i * p.sq[2] + 4 * c4;
+    if constexpr (BF16) {
+      u32x2 pk{pack_bf16x2(x[0] * p.scale, x[1] * p.scale), pack_bf16x2(x[2] * p.scale, x[3] * p.scale)};
+      *reinterpret_cast<u32x2*>((char*)p.dQ + off * 2) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>((char*)p.dQ + off * 4) =
+          f32x4{x[0] * p.scale, x[1] * p.scale, x[2] * p.scale, x[3] * p.scale};
+    }
+  }
+}
+
+int launch_bwd_post(const BwdParams& p, int bf16, int d, void* stream) {
+  const int64_t total = (int64_t)p.B * p.H * p.n * (d / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipStream_t st = (hipStream_t)stream;
+  if (bf16)
+    hipLaunchKernelGGL((bwd_post_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, st, p, d);
+  else
+    hipLaunchKernelGGL((bwd_post_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, st, p, d);
+  return (int)hipGetLastError();
+}
+
+const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+int hip_last_launch_error() { return (int)hipGetLastError(); }
+
+}  // namespace eta

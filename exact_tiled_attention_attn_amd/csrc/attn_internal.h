@@ -1,0 +1,86 @@
+// Internal interface between the host entry points (attn_api.cpp) and the
+// kernel launchers (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace eta {
+
+// Tile shapes.  Forward: one workgroup per 128-query tile, streaming 64-key
+// tiles.  Backward: one workgroup per 128-key tile, streaming 64-query tiles.
+constexpr int kFwdBq = 128;
+constexpr int kFwdBk = 64;
+constexpr int kBwdBq = 64;
+constexpr int kBwdBk = 128;
+
+struct FwdParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* L;
+  const uint8_t* map;  // bitmask tile map [mask units][tq][tk], else null
+  const uint32_t* mask;
+  int64_t mask_sb, mask_sh, mask_si;
+  int64_t sq[3], sk[3], sv[3], so[3];
+  int64_t n;
+  int32_t B, H;
+  int32_t tq, tk;
+  int64_t total;     // B * H * tq work items
+  int64_t grid_pad;  // total rounded up to a multiple of 8
+  float scale2;      // c * log2(e): scores kept in the base-2 domain
+};
+
+struct BwdParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* L;
+  float* Dv;     // D_i = <dO_i, O_i>, fp32 [B, H, n]
+  float* dQacc;  // fp32 [B, H, n, d] accumulator (unscaled by c)
+  void* dQ;
+  void* dK;
+  void* dV;
+  const uint8_t* map;
+  const uint32_t* mask;
+  int64_t mask_sb, mask_sh, mask_si;
+  int64_t sq[3], sk[3], sv[3], so[3];
+  int64_t n;
+  int32_t B, H;
+  int32_t tq, tk;  // backward tiling: tq query tiles of kBwdBq, tk key tiles of kBwdBk
+  int64_t total;
+  int64_t grid_pad;
+  float scale;   // c
+  float scale2;  // c * log2(e)
+};
+
+struct MapParams {
+  const uint32_t* mask;
+  int64_t mask_sb, mask_sh, mask_si;
+  uint8_t* map;
+  int64_t n;
+  int32_t B, H;
+  int32_t units;  // distinct masks: H (batch-shared) or B * H
+  int32_t bq, bk, tq, tk;
+  int32_t mask_mode;
+};
+
+// Launchers return a hipError_t value as int (0 = success).
+int launch_fwd(const FwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
+int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
+int launch_tile_map(const MapParams& p, void* stream);
+int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, void* stream);
+int launch_bwd_post(const BwdParams& p, int bf16, int d, void* stream);
+const char* hip_error_string(int err);
+int hip_last_launch_error();
+
+// True when the (d, v) pair has compiled kernels.
+inline bool supported_dims(int64_t d, int64_t v) {
+  return (d == 64 && v == 64) || (d == 80 && v == 80) || (d == 128 && v == 128) ||
+         (d == 64 && v == 128);
+}
+
+}  // namespace eta

@@ -1,0 +1,156 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Layout facts used throughout (checked on the device with an in-bounds
+// probe of each instruction):
+//
+// * v_mfma_f32_32x32x16_bf16  A[m][k]: lane l holds m = l%32, k = 8(l/32)+e
+//   (e = 0..7); B[k][n]: n = l%32, k = 8(l/32)+e; C[m][n]: lane l, register
+//   r holds m = 8(r/4) + 4(l/32) + r%4, n = l%32.
+// * v_mfma_f32_32x32x2_f32    A: m = l%32, k = l/32; B: k = l/32, n = l%32;
+//   C as above.
+// * ds_read_b64_tr_b16: in each 16-lane group the 16 lane addresses name a
+//   16 x 4 block M[r][c] of 16-bit elements (row r = the lane, 4 contiguous
+//   elements); lane i receives M[4t + i/4][i%4] for t = 0..3.  Giving lane i
+//   the address of X[k0 + i/4][n0 + 4(i%4)] of a row-major tile X therefore
+//   hands lane i the column slice X[k0 .. k0+3][n0 + i]: four consecutive
+//   contraction indices of one output column, which is what an MFMA operand
+//   needs when the contraction runs down the rows of X.
+// * Workgroups are dispatched round-robin over the 8 XCDs (XCC id =
+//   blockIdx.x % 8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace eta {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskBitmask = 2 };
+enum : uint8_t { kTileEmpty = 0, kTilePartial = 1, kTileFull = 2 };
+
+// ---------------------------------------------------------------------------
+// Scalars
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 y = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return *reinterpret_cast<uint32_t*>(&y);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Max over the two 32-lane halves holding the same column (lane l and l^32).
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// LDS operand fetches
+// ---------------------------------------------------------------------------
+
+// Row operand: lane reads 8 contiguous bf16 at byte offset `off` of LDS.
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* lds_base, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(lds_base + off);
+}
+
+// Column operand, transposed read: returns X[k0..k0+3][col] where the lane's
+// address (computed by tr_addr) names X[k0 + i/4][n0 + 4(i%4)].
+__device__ __forceinline__ i16x4 lds_read_tr(const char* lds_base, uint32_t off) {
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)(lds_base) + off;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+// Byte offset for a transposed read of the 4 x 16 block of a row-major bf16
+// tile with `stride` bytes per row, rows k0..k0+3, columns n0..n0+15.
+__device__ __forceinline__ uint32_t tr_addr(int lane, int k0, int n0, int stride) {
+  int i = lane & 15;
+  return (uint32_t)((k0 + (i >> 2)) * stride + (n0 + 4 * (i & 3)) * 2);
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  bf16x8 r;
+  i16x4* p = reinterpret_cast<i16x4*>(&r);
+  p[0] = lo;
+  p[1] = hi;
+  return r;
+}
+
+// Pack 8 fp32 accumulator values (registers r0..r0+7 of a 32x32 C block)
+// as a bf16x8 MFMA operand, RNE.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int r0) {
+  u32x4 u;
+  u[0] = pack_bf16x2(c[r0 + 0], c[r0 + 1]);
+  u[1] = pack_bf16x2(c[r0 + 2], c[r0 + 3]);
+  u[2] = pack_bf16x2(c[r0 + 4], c[r0 + 5]);
+  u[3] = pack_bf16x2(c[r0 + 6], c[r0 + 7]);
+  return *reinterpret_cast<bf16x8*>(&u);
+}
+
+// ---------------------------------------------------------------------------
+// Launch mapping
+// ---------------------------------------------------------------------------
+
+// Map the hardware block index to a logical work index so that each XCD
+// receives one contiguous range of logical indices, dispatched in order.
+// The grid is padded to a multiple of 8; returns -1 for padding blocks.
+__device__ __forceinline__ int64_t xcd_logical(int64_t bid, int64_t grid_pad, int64_t total) {
+  int64_t per = grid_pad / kXcds;
+  int64_t l = (bid % kXcds) * per + bid / kXcds;
+  return l < total ? l : -1;
+}
+
+// Classification of a tile from its corners for none/causal masks: the same
+// rule the skip logic and the partial-tile masking follow.
+__device__ __forceinline__ uint8_t classify_analytic(int mask_mode, int64_t q0, int bq, int64_t k0,
+                                                     int bk, int64_t n) {
+  int64_t q_hi = (q0 + bq < n ? q0 + bq : n) - 1;
+  int64_t k_hi = k0 + bk - 1;
+  if (mask_mode == kMaskCausal) {
+    if (k0 > q_hi) return kTileEmpty;
+    if (k_hi <= q0 && k_hi < n) return kTileFull;
+    return kTilePartial;
+  }
+  return (k_hi < n) ? kTileFull : kTilePartial;
+}
+
+}  // namespace eta

@@ -1,0 +1,151 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact tiled attention library.
+ *
+ * The operation (alphabetamath page, "Exact tiled softmax attention with
+ * block-recomputed vector-Jacobian products", Inputs): for every (batch,
+ * head) unit, positive n, d, v; Q, K in R^{n x d}; V in R^{n x v}; a real
+ * scale c; nonempty allowed-key sets A_1..A_n.  With s_ij = c <Q_i, K_j>:
+ *
+ *   forward   O_i = sum_{j in A_i} exp(s_ij - L_i) V_j,
+ *             L_i = ln sum_{j in A_i} exp(s_ij)            (natural log, fp32)
+ *             (online softmax over key tiles, ob1 page part 1; maitreyasuin
+ *             post, the tiled forward returning O and L = m + log l)
+ *   backward  given dO (the upstream G), with D_i = <dO_i, O_i>,
+ *             p_ij = exp(s_ij - L_i), dS_ij = p_ij (<dO_i, V_j> - D_i):
+ *             dQ = c dS K,  dK = c dS^T Q,  dV = P^T dO
+ *             (alphabetamath page, reverse procedure; ob1 page part 2;
+ *             HarshvardhanJ/FlashAttention README, backward section)
+ *
+ * No n x n score or probability matrix is stored: every kernel rebuilds
+ * score tiles on chip.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers.  The caller owns every buffer
+ *   (inputs, outputs, mask, workspace); the library allocates nothing and
+ *   keeps no state between calls except its loaded code objects.
+ * - Q, K, V, O, dO, dQ, dK, dV are [B, H, n, .] with element strides
+ *   (batch, head, row) given in attn_problem and a unit stride on the last
+ *   dimension.  dQ, dK, dV use the strides of Q, K, V; dO uses those of O.
+ *   Pointers must be 16-byte aligned and row/head/batch strides multiples
+ *   of 16 bytes.  L (and the backward's internal D) are contiguous fp32
+ *   [B, H, n].
+ * - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *   asynchronously on it; nothing synchronises.
+ * - Every argument is validated before anything is launched; on an error
+ *   status nothing has been written.  attn_last_error() then returns a
+ *   thread-local message describing the failure.
+ * - Q, K, V may alias each other (self-attention).  Outputs must not
+ *   overlap any input or each other (ATTN_ERR_ALIAS).
+ * - Empty allowed rows are outside the contract (A_i must be nonempty);
+ *   the library still defines them: O_i = 0, L_i = -inf, and such rows
+ *   contribute nothing to dQ, dK, dV.
+ */
+#ifndef EXACT_TILED_ATTN_H
+#define EXACT_TILED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* B, H, n, d or v < 1, or a size overflows */
+  ATTN_ERR_STRIDE = 3,      /* misaligned pointer or stride, or overlapping rows */
+  ATTN_ERR_DTYPE = 4,       /* unknown element type */
+  ATTN_ERR_MASK = 5,        /* unknown mask mode, or bitmask mode without mask */
+  ATTN_ERR_UNSUPPORTED = 6, /* (d, v) pair or option not compiled in */
+  ATTN_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than attn_workspace_size */
+  ATTN_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
+  ATTN_ERR_HIP = 9          /* a HIP launch error (message in attn_last_error) */
+} attn_status;
+
+typedef enum {
+  ATTN_F32 = 0,  /* fp32 inputs and outputs, fp32 MFMA, fp32 accumulation */
+  ATTN_BF16 = 1  /* bf16 inputs and outputs, bf16 MFMA, fp32 accumulation */
+} attn_dtype;
+
+/* The allowed-key sets A_i (alphabetamath page, Inputs: membership read on
+ * demand; a caller-owned mask representation is input storage). */
+typedef enum {
+  ATTN_MASK_NONE = 0,    /* A_i = {0..n-1} */
+  ATTN_MASK_CAUSAL = 1,  /* A_i = {j <= i} (ob1 page, part 3: block causal) */
+  ATTN_MASK_BITMASK = 2  /* explicit: bit (j & 31) of word j >> 5 of row i */
+} attn_mask_mode;
+
+typedef struct {
+  int64_t B, H;           /* batch and head counts */
+  int64_t n;              /* sequence length (queries = keys) */
+  int64_t d, v;           /* key/query dim and value dim; (d, v) in
+                             {(64,64), (80,80), (128,128), (64,128)} */
+  int32_t dtype;          /* attn_dtype */
+  int32_t mask_mode;      /* attn_mask_mode */
+  double scale;           /* c: any finite real, including 0 and negative */
+  const uint32_t* mask;   /* BITMASK only: device words, LSB first, pad bits ignored */
+  int64_t mask_sb;        /* mask strides in uint32 words: batch (0 = shared), */
+  int64_t mask_sh;        /*   head, */
+  int64_t mask_si;        /*   row (>= ceil(n/32)) */
+  int64_t sq[3];          /* element strides [batch, head, row] of Q and dQ */
+  int64_t sk[3];          /* ... of K and dK */
+  int64_t sv[3];          /* ... of V and dV */
+  int64_t so[3];          /* ... of O and dO */
+  int32_t deterministic;  /* bwd: must be 0 (fp32 atomic dQ accumulation) */
+  int32_t reserved;       /* must be 0 */
+} attn_problem;
+
+/* Bytes of device workspace attn_fwd (is_bwd = 0) or attn_bwd (is_bwd = 1)
+ * needs for this problem.  Forward: the tile map of bitmask mode (0 bytes
+ * otherwise).  Backward: D (4 B H n bytes) + the fp32 dQ accumulator
+ * (4 B H n d bytes) + the bitmask tile map; every region 256-byte aligned.
+ * Validates the problem like the compute calls. */
+attn_status attn_workspace_size(const attn_problem* p, int is_bwd, size_t* bytes);
+
+/* Forward: O [B,H,n,v] (dtype) and L [B,H,n] (fp32, natural-log logsumexp
+ * of the scaled allowed scores).  Kernels: bitmask tile classification
+ * (bitmask mode only), then one fused tiled kernel per call. */
+attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const void* V,
+                     void* O, float* L, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Backward: dQ, dK, dV (dtype) from Q, K, V, the forward's O and L, and the
+ * upstream gradient dO.  Kernels: D = rowsum(dO o O) with dQ-accumulator
+ * clearing, bitmask tile classification (bitmask mode), the key-tile-outer
+ * recompute kernel (dK, dV in registers, dQ by fp32 atomics into the
+ * workspace), and the dQ conversion.  dQ's run-to-run result may differ in
+ * the last bits (atomic order). */
+attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const void* V,
+                     const void* O, const void* dO, const float* L,
+                     void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Debug: the (query tile x key tile) classification the forward (is_bwd=0)
+ * or backward (is_bwd=1) kernels use, 0 = empty (skipped), 1 = partial
+ * (masked inside), 2 = full (no masking), as uint8 [units, tq, tk] with
+ * units = 1 for none/causal masks (shared by every head), else the number
+ * of distinct masks (H if mask_sb == 0, else B*H, in (b, h) order).
+ * Writes *bq, *bk (tile sizes) and *tq, *tk; if map_dev is NULL only the
+ * sizes are returned, else map_bytes must hold units*tq*tk bytes.  The
+ * workspace is that of the matching compute call. */
+attn_status attn_debug_tile_map(const attn_problem* p, int is_bwd, uint8_t* map_dev,
+                                size_t map_bytes, int32_t* bq, int32_t* bk, int32_t* tq,
+                                int32_t* tk, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Static description of a status code. */
+const char* attn_status_str(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_TILED_ATTN_H */

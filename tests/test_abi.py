@@ -1,0 +1,160 @@
+"""The C-ABI library on the CPU: it loads, exports what include/attn.h
+declares, and rejects every invalid argument before anything is launched
+(no call here reaches a HIP API)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_attn_amd as E
+from exact_tiled_attention_attn_amd._binding import AttnProblem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = E.load_library()
+    names = declared_functions()
+    assert set(names) == set(E.EXPORTS)
+    for name in names:
+        assert getattr(lib, name) is not None
+    assert lib.attn_version() == 100
+
+
+def problem(B=1, H=2, n=100, d=64, v=64, dtype=1, mask_mode=0, contiguous=True):
+    p = AttnProblem()
+    p.B, p.H, p.n, p.d, p.v = B, H, n, d, v
+    p.dtype, p.mask_mode, p.scale = dtype, mask_mode, 0.125
+    for name, w in (("sq", d), ("sk", d), ("sv", v), ("so", v)):
+        arr = getattr(p, name)
+        arr[0], arr[1], arr[2] = H * n * w, n * w, w
+    return p
+
+
+def call_fwd(p, Q=FAKE, K=FAKE + (1 << 30), V=FAKE + (2 << 30), O=FAKE + (3 << 30),
+             L=FAKE + (4 << 30), ws=None, ws_bytes=0):
+    lib = E.load_library()
+    vp = ctypes.c_void_p
+    return lib.attn_fwd(ctypes.byref(p), vp(Q), vp(K), vp(V), vp(O), vp(L), vp(ws),
+                        ctypes.c_size_t(ws_bytes), None)
+
+
+def call_bwd(p, ptrs=None, ws=None, ws_bytes=0):
+    lib = E.load_library()
+    base = [FAKE + (i << 30) for i in range(9)]
+    if ptrs:
+        base = [ptrs.get(i, x) for i, x in enumerate(base)]
+    vp = ctypes.c_void_p
+    return lib.attn_bwd(ctypes.byref(p), *[vp(x) for x in base], vp(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def err():
+    return E.load_library().attn_last_error().decode()
+
+
+def wsize(p, is_bwd):
+    out = ctypes.c_size_t()
+    st = E.load_library().attn_workspace_size(ctypes.byref(p), is_bwd, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_formula():
+    for dtype in (0, 1):
+        for (B, H, n, d, v) in ((1, 1, 1, 64, 64), (2, 3, 1000, 80, 80), (1, 32, 16384, 128, 128)):
+            p = problem(B, H, n, d, v, dtype)
+            st, fw = wsize(p, 0)
+            assert st == 0 and fw == 0
+            st, bw = wsize(p, 1)
+            al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+            assert st == 0 and bw == al(4 * B * H * n) + al(4 * B * H * n * d)
+    # bitmask: + tile map (units x tq x tk bytes); forward tiles 128 x 64, backward 64 x 128 (bf16)
+    p = problem(2, 8, 8192, 64, 128, 1, 2)
+    p.mask = FAKE
+    p.mask_sb, p.mask_sh, p.mask_si = 0, 8192 * 256, 256
+    st, fw = wsize(p, 0)
+    assert st == 0 and fw == (8 * 64 * 128 + 255) // 256 * 256
+    st, bw = wsize(p, 1)
+    assert bw == 4 * 16 * 8192 + 4 * 16 * 8192 * 64 + 8 * 128 * 64
+
+
+@pytest.mark.parametrize("mut,status", [
+    (lambda p: setattr(p, "n", 0), 2),
+    (lambda p: setattr(p, "B", 0), 2),
+    (lambda p: setattr(p, "d", 96), 6),
+    (lambda p: (setattr(p, "d", 128), setattr(p, "v", 64)), 6),
+    (lambda p: setattr(p, "dtype", 7), 4),
+    (lambda p: setattr(p, "mask_mode", 3), 5),
+    (lambda p: setattr(p, "mask_mode", 2), 5),  # bitmask without mask
+    (lambda p: setattr(p, "deterministic", 1), 6),
+    (lambda p: setattr(p, "reserved", 1), 6),
+    (lambda p: setattr(p, "scale", float("inf")), 2),
+    (lambda p: setattr(p, "scale", float("nan")), 2),
+    (lambda p: p.sq.__setitem__(2, 63), 3),   # row stride not 16-byte multiple / overlapping
+    (lambda p: p.sq.__setitem__(2, 32), 3),   # rows overlap
+    (lambda p: p.sk.__setitem__(1, -6400), 3),
+    (lambda p: p.so.__setitem__(1, 64 * 99), 3),  # heads overlap
+])
+def test_invalid_problem_rejected(mut, status):
+    p = problem()
+    mut(p)
+    assert call_fwd(p) == status, err()
+    assert call_bwd(p) == status, err()
+    assert wsize(p, 0)[0] == status
+    assert err() != ""
+
+
+def test_null_and_misaligned_pointers():
+    p = problem()
+    assert call_fwd(p, Q=0) == 1 and "Q" in err()
+    assert call_fwd(p, L=0) == 1
+    assert call_fwd(p, V=FAKE + 8) == 3 and "aligned" in err()
+    assert call_bwd(p, {4: 0}) == 1 and "dO" in err()
+    lib = E.load_library()
+    assert lib.attn_fwd(None, None, None, None, None, None, None, 0, None) == 1
+
+
+def test_aliasing_outputs_rejected():
+    p = problem()
+    assert call_fwd(p, O=FAKE) == 8  # O on top of Q
+    assert call_fwd(p, L=FAKE + (2 << 30) + 64) == 8  # L inside V
+    assert call_bwd(p, {6: FAKE + (7 << 30)}) == 8  # dQ on dK
+    assert call_bwd(p, {8: FAKE + (3 << 30)}) == 8  # dV on O
+
+
+def test_workspace_checks():
+    p = problem()
+    st, need = wsize(p, 1)
+    assert need > 0
+    assert call_bwd(p) == 7 and "workspace" in err()
+    assert call_bwd(p, ws=FAKE + (20 << 30), ws_bytes=need - 1) == 7
+    assert call_bwd(p, ws=FAKE + (20 << 30) + 16, ws_bytes=need) == 7  # not 256-byte aligned
+    assert call_bwd(p, ws=FAKE, ws_bytes=need) == 8  # workspace overlaps Q
+
+
+def test_status_strings():
+    lib = E.load_library()
+    for s in range(10):
+        assert lib.attn_status_str(s)
+    assert lib.attn_status_str(99) == b"unknown status"
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from exact_tiled_attention_attn_amd import _binding
+    with pytest.raises(RuntimeError, match="not found"):
+        _binding._lib, saved = None, _binding._lib
+        try:
+            _binding.load_library(str(tmp_path / "libattn.so"))
+        finally:
+            _binding._lib = saved
