@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention (forward + backward) on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+attn_fwd (O, L) then attn_bwd (dQ, dK, dV) through the C ABI.  Inputs are
+generated from the workload's seed and are resident in HBM before timing.
+
+Prints one JSON line.  ``value`` is the algorithmic forward+backward
+TFLOP/s, F = 2 #A (d + v) + 2 #A (3d + 2v) per step with #A the number of
+allowed (query, key) pairs; ``roofline`` reports the dominant kernel's
+algorithmic FLOPs per launch over its average launch duration (HIP events
+recorded by the library on the launch stream) against the dense MFMA peak
+of the dtype; ``cpu_baseline`` times the float64 oracle on the host cores on
+a bounded sample (one (batch, head) unit, sub-sized if needed).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # published dense MFMA peaks
+HEADLINE = "bf16_causal_h32_n16384_d128"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=25.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(prob, budget_s: float) -> dict:
+    """The oracle (dense float64 forward + VJP) on one unit of the workload.
+
+    Starts with the first 2048 query rows and keys of unit (0, 0) -- a
+    sub-problem of the same recipe -- and doubles the size while the
+    predicted time stays within the budget, up to the full unit.
+    """
+    import threadpoolctl
+
+    import workloads as W
+    from oracle import dense
+
+    w = prob.w
+    n = w.n
+    Q, K, V, G = (getattr(prob, x)[0, 0].astype(np.float64) for x in "QKVG")
+    ns = min(2048, n)
+    result = None
+    spent = 0.0
+    while True:
+        A = None if w.mask == W.MASK_NONE else prob.allowed(0)[:ns, :ns]
+        if A is not None and not A.any(axis=1).all():
+            A = A.copy()
+            A[np.arange(ns), np.arange(ns)] = True  # keep the sub-problem's rows nonempty
+        pairs = ns * ns if A is None else int(A.sum())
+        t0 = time.perf_counter()
+        dense.forward(Q[:ns], K[:ns], V[:ns], w.scale, A)
+        dense.vjp(Q[:ns], K[:ns], V[:ns], w.scale, A, G[:ns])
+        dt = time.perf_counter() - t0
+        spent += dt
+        flops = 2.0 * pairs * (w.d + w.v) + 2.0 * pairs * (3 * w.d + 2 * w.v)
+        result = (ns, pairs, dt, flops)
+        if ns >= n or spent + 4.2 * dt > budget_s:
+            break
+        ns = min(n, 2 * ns)
+    ns, pairs, dt, flops = result
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"unit (b=0, h=0), query rows and keys 0..{ns - 1} of {n} ({pairs} allowed pairs): "
+                   f"dense float64 forward + VJP, {dt:.2f} s; host has "
+                   f"{len(os.sched_getaffinity(0))} usable cores"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_attn_amd as E
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    E.load_library()  # fail loudly if the HIP library is missing
+    prob = W.generate(args.workload)
+    w = prob.w
+    pairs = W.allowed_pairs(w, prob)
+    f_fwd, f_bwd = W.flops(w, pairs)
+    dev = "cuda:0"
+
+    def up(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(prob.bits[name].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(getattr(prob, name)).to(dev)
+
+    q, k, v, g = (up(x) for x in "QKVG")
+    mask = None
+    if prob.mask_words is not None:
+        mask = torch.from_numpy(prob.mask_words.view(np.int32)).to(dev)
+    o = torch.empty((w.B, w.H, w.n, w.v), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    pf = E.make_problem(q, k, v, o, w.scale, w.mask, mask)
+    ws_f = torch.empty(max(E.workspace_size(pf, False), 256), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(E.workspace_size(pf, True), 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        E.fwd(q, k, v, w.scale, w.mask, mask, out=o, lse=lse, workspace=ws_f)
+        E.bwd(q, k, v, o, g, lse, w.scale, w.mask, mask, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    E.timing_enable(True)
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern = E.timing_read()
+    E.timing_enable(False)
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t.float()).all(), "non-finite output"
+
+    ms_step = total_ms / args.steps
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    avg = {kname: (ms / cnt if cnt else 0.0) for kname, (ms, cnt) in kern.items()}
+    fwd_ms = avg["fwd"] + (avg["tile_map"] if w.mask == W.MASK_BITMASK else 0.0)
+    bwd_ms = avg["bwd_pre"] + avg["bwd"] + avg["bwd_post"] + (avg["tile_map"] if w.mask == W.MASK_BITMASK else 0.0)
+    peak = PEAK_TFLOPS[w.dtype]
+    kflops = {"fwd": f_fwd, "bwd": f_bwd}
+    dominant = max(("fwd", "bwd"), key=lambda kname: kern[kname][0])
+    achieved = kflops[dominant] / (avg[dominant] * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s on 1 MI355X (algorithmic FLOPs over allowed pairs)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) recipe of the workload; no dataset)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "n": w.n, "d": w.d, "v": w.v,
+                   "mask": w.mask, "allowed_pairs": pairs, "scale": w.scale},
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * f_fwd / (fwd_ms * 1e-3) / 1e12 / peak, 2)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * f_bwd / (bwd_ms * 1e-3) / 1e12 / peak, 2)},
+        "kernels_avg_ms": {kname: round(x, 4) for kname, x in avg.items() if kern[kname][1]},
+        "roofline": {"kernel": f"{dominant} (attn_{dominant} main kernel)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(prob, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     fwd,
     load_library,
     make_problem,
+    timing_enable,
+    timing_read,
     workspace_size,
 )
 

@@ -24,7 +24,9 @@ STATUS = {
     7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP",
 }
 EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map",
+           "attn_timing_enable", "attn_timing_read", "attn_timing_reset",
            "attn_status_str", "attn_last_error", "attn_version"]
+KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post"]
 
 
 class AttnError(RuntimeError):
@@ -73,6 +75,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_version.restype = ctypes.c_int32
+    lib.attn_timing_enable.argtypes = [ctypes.c_int]
+    lib.attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    for f in ("attn_timing_enable", "attn_timing_read", "attn_timing_reset"):
+        getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -194,3 +200,17 @@ def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=False):
                                    ctypes.byref(bq), ctypes.byref(bk), ctypes.byref(tq),
                                    ctypes.byref(tk), None, 0, _stream()))
     return out, bq.value, bk.value
+
+
+def timing_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events on its stream."""
+    _check(load_library().attn_timing_enable(int(on)))
+
+
+def timing_read() -> dict:
+    """{kernel: (total ms, launches)} accumulated since the last read; waits for the events."""
+    n = len(KERNELS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(load_library().attn_timing_read(ms, cnt))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNELS)}

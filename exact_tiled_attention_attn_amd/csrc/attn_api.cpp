@@ -200,6 +200,15 @@ eta::MapParams map_params(const attn_problem& p, const Tiles& t, uint8_t* map, i
 
 int64_t pad8(int64_t x) { return (x + 7) / 8 * 8; }
 
+// Launch through `fn`, bracketed by the opt-in timing events of class `kind`.
+template <typename F>
+attn_status timed(int kind, void* stream, const char* what, F&& fn) {
+  eta::timing_begin(kind, stream);
+  const int err = fn();
+  eta::timing_end(kind, stream);
+  return hip_status(err, what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,7 +253,9 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
   uint8_t* map = lay.map_bytes ? reinterpret_cast<uint8_t*>(ws) + lay.off_map : nullptr;
   if (p->mask_mode == ATTN_MASK_BITMASK) {
     const eta::MapParams mp = map_params(*p, t, map, (int)mask_units(*p));
-    if ((st = hip_status(eta::launch_tile_map(mp, stream), "tile map launch")) != ATTN_OK) return st;
+    if ((st = timed(ATTN_KERNEL_TILE_MAP, stream, "tile map launch",
+                    [&] { return eta::launch_tile_map(mp, stream); })) != ATTN_OK)
+      return st;
   }
   eta::FwdParams f{};
   f.Q = Q;
@@ -267,8 +278,9 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
   f.grid_pad = pad8(f.total);
   f.scale2 = (float)(p->scale * 1.4426950408889634);
   if (f.grid_pad > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
-  return hip_status(eta::launch_fwd(f, p->dtype == ATTN_BF16, (int)p->d, (int)p->v, p->mask_mode, stream),
-                    "forward launch");
+  return timed(ATTN_KERNEL_FWD, stream, "forward launch", [&] {
+    return eta::launch_fwd(f, p->dtype == ATTN_BF16, (int)p->d, (int)p->v, p->mask_mode, stream);
+  });
 }
 
 attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const void* V, const void* O,
@@ -338,22 +350,27 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.scale2 = (float)(p->scale * 1.4426950408889634);
   if (b.grid_pad > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
   const int bf = p->dtype == ATTN_BF16;
-  if ((st = hip_status(eta::launch_bwd_pre(b, bf, (int)p->d, (int)p->v, stream), "D preprocess launch")) != ATTN_OK)
+  if ((st = timed(ATTN_KERNEL_BWD_PRE, stream, "D preprocess launch",
+                  [&] { return eta::launch_bwd_pre(b, bf, (int)p->d, (int)p->v, stream); })) != ATTN_OK)
     return st;
   if (p->mask_mode == ATTN_MASK_BITMASK) {
     const eta::MapParams mp = map_params(*p, t, const_cast<uint8_t*>(b.map), (int)mask_units(*p));
-    if ((st = hip_status(eta::launch_tile_map(mp, stream), "tile map launch")) != ATTN_OK) return st;
+    if ((st = timed(ATTN_KERNEL_TILE_MAP, stream, "tile map launch",
+                    [&] { return eta::launch_tile_map(mp, stream); })) != ATTN_OK)
+      return st;
   }
-  if ((st = hip_status(eta::launch_bwd(b, bf, (int)p->d, (int)p->v, p->mask_mode, stream), "backward launch")) !=
-      ATTN_OK)
+  if ((st = timed(ATTN_KERNEL_BWD, stream, "backward launch", [&] {
+         return eta::launch_bwd(b, bf, (int)p->d, (int)p->v, p->mask_mode, stream);
+       })) != ATTN_OK)
     return st;
-  return hip_status(eta::launch_bwd_post(b, bf, (int)p->d, stream), "dQ conversion launch");
+  return timed(ATTN_KERNEL_BWD_POST, stream, "dQ conversion launch",
+               [&] { return eta::launch_bwd_post(b, bf, (int)p->d, stream); });
 }
 
 attn_status attn_debug_tile_map(const attn_problem* p, int is_bwd, uint8_t* map_dev, size_t map_bytes,
                                 int32_t* bq, int32_t* bk, int32_t* tq, int32_t* tk, void* ws,
                                 size_t ws_bytes, void* stream) {
-  (void)ws;
+  (void)ws;  // reserved
   (void)ws_bytes;
   attn_status st = validate_problem(p);
   if (st != ATTN_OK) return st;
@@ -389,6 +406,25 @@ const char* attn_status_str(int s) {
 }
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+attn_status attn_timing_enable(int on) {
+  eta::timing_enable(on);
+  return ATTN_OK;
+}
+
+attn_status attn_timing_read(double* ms, int64_t* launches) {
+  if (!ms || !launches) return fail(ATTN_ERR_NULL, "timing outputs must not be NULL");
+  for (int i = 0; i < ATTN_KERNEL_COUNT; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  return hip_status(eta::timing_read(ms, launches), "timing read");
+}
+
+attn_status attn_timing_reset(void) {
+  eta::timing_reset();
+  return ATTN_OK;
+}
 
 int32_t attn_version(void) { return 100; }
 

@@ -159,3 +159,80 @@ const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err
 int hip_last_launch_error() { return (int)hipGetLastError(); }
 
 }  // namespace eta
+
+// ---------------------------------------------------------------------------
+// Opt-in launch timing: HIP events recorded on the launch stream around each
+// kernel, read back (and recycled) by attn_timing_read.
+// ---------------------------------------------------------------------------
+
+#include <vector>
+
+namespace eta {
+namespace {
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_pending;
+std::vector<hipEvent_t> g_free;
+hipEvent_t take_event() {
+  if (!g_free.empty()) {
+    hipEvent_t e = g_free.back();
+    g_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void timing_begin(int kind, void* stream) {
+  if (!g_timing) return;
+  TimedLaunch t{kind, take_event(), take_event()};
+  if (!t.start || !t.stop) return;
+  hipEventRecord(t.start, (hipStream_t)stream);
+  g_pending.push_back(t);
+}
+
+void timing_end(int kind, void* stream) {
+  if (!g_timing || g_pending.empty() || g_pending.back().kind != kind) return;
+  hipEventRecord(g_pending.back().stop, (hipStream_t)stream);
+}
+
+void timing_reset() {
+  for (auto& t : g_pending) {
+    hipEventSynchronize(t.stop);
+    g_free.push_back(t.start);
+    g_free.push_back(t.stop);
+  }
+  g_pending.clear();
+}
+
+int timing_enable(int on) {
+  timing_reset();
+  g_timing = on != 0;
+  return 0;
+}
+
+int timing_read(double* ms, int64_t* launches) {
+  int err = 0;
+  for (auto& t : g_pending) {
+    float el = 0.f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&el, t.start, t.stop);
+    if (e != hipSuccess) {
+      err = (int)e;
+    } else if (t.kind >= 0 && t.kind < 5) {
+      ms[t.kind] += el;
+      launches[t.kind] += 1;
+    }
+    g_free.push_back(t.start);
+    g_free.push_back(t.stop);
+  }
+  g_pending.clear();
+  return err;
+}
+
+}  // namespace eta

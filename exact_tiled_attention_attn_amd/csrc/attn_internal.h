@@ -77,6 +77,14 @@ int launch_bwd_post(const BwdParams& p, int bf16, int d, void* stream);
 const char* hip_error_string(int err);
 int hip_last_launch_error();
 
+// Opt-in launch timing (attn_timing_*): bracket one launch of kernel class
+// `kind` with events on `stream`.  No-ops while timing is disabled.
+void timing_begin(int kind, void* stream);
+void timing_end(int kind, void* stream);
+int timing_enable(int on);
+int timing_read(double* ms, int64_t* launches);
+void timing_reset();
+
 // True when the (d, v) pair has compiled kernels.
 inline bool supported_dims(int64_t d, int64_t v) {
   return (d == 64 && v == 64) || (d == 80 && v == 80) || (d == 128 && v == 128) ||

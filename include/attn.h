@@ -129,11 +129,32 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
  * of distinct masks (H if mask_sb == 0, else B*H, in (b, h) order).
  * Writes *bq, *bk (tile sizes) and *tq, *tk; if map_dev is NULL only the
  * sizes are returned, else map_bytes must hold units*tq*tk bytes.  The
- * workspace is that of the matching compute call. */
+ * workspace arguments are reserved (pass NULL, 0). */
 attn_status attn_debug_tile_map(const attn_problem* p, int is_bwd, uint8_t* map_dev,
                                 size_t map_bytes, int32_t* bq, int32_t* bk, int32_t* tq,
                                 int32_t* tk, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* Kernel classes reported by the timing facility below. */
+typedef enum {
+  ATTN_KERNEL_TILE_MAP = 0, /* bitmask tile classification */
+  ATTN_KERNEL_FWD = 1,      /* forward */
+  ATTN_KERNEL_BWD_PRE = 2,  /* D = rowsum(dO o O), accumulator clearing */
+  ATTN_KERNEL_BWD = 3,      /* key-tile-outer backward */
+  ATTN_KERNEL_BWD_POST = 4, /* dQ conversion */
+  ATTN_KERNEL_COUNT = 5
+} attn_kernel;
+
+/* Opt-in kernel timing (off by default; not thread-safe; for measurement
+ * tools).  While enabled, every kernel the library launches is bracketed by
+ * two HIP events recorded on the launch stream.  attn_timing_read waits for
+ * the recorded events, adds each launch's duration to ms[kind] and counts it
+ * in launches[kind] (both arrays of ATTN_KERNEL_COUNT entries, accumulated
+ * since the last read or reset), then recycles the events.  Disabling or
+ * resetting discards pending measurements. */
+attn_status attn_timing_enable(int on);
+attn_status attn_timing_read(double* ms, int64_t* launches);
+attn_status attn_timing_reset(void);
 
 /* Static description of a status code. */
 const char* attn_status_str(int status);
