@@ -38,7 +38,7 @@ struct FwdShape {
   static constexpr int NVB = DVP / 32;
   static constexpr int NKB = BK / 32;
   static constexpr int KSTR = D * ES + 16;                  // bytes per K row in LDS
-  static constexpr int VSTR = DVP * ES + (BF16 ? 32 : 16);  // bytes per V row in LDS
+  static constexpr int VSTR = DVP * ES + 16;                // bytes per V row in LDS
   static constexpr int KTILE = BK * KSTR;
   static constexpr int VTILE = BK * VSTR;
   static constexpr int KCH = D * ES / 16;   // 16-byte chunks per K row
@@ -49,8 +49,14 @@ struct FwdShape {
   static constexpr int SMEM = 2 * (KTILE + VTILE);
 };
 
+// Lazy rescaling: the reference maximum m is raised only when a tile's max
+// exceeds it by more than this (base-2 units).  Any reference value gives
+// the same O and L (softmax is shift-invariant); this bound keeps the
+// unnormalised weights <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
 template <bool BF16, int D, int DV, int MASK>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdParams p) {
   using S = FwdShape<BF16, D, DV>;
   __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
 
@@ -72,18 +78,24 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const char* Kb = (const char*)p.K + (b * p.sk[0] + h * p.sk[1]) * S::ES;
   const char* Vb = (const char*)p.V + (b * p.sv[0] + h * p.sv[1]) * S::ES;
 
-  // Q fragments (B operand of S^T = K Q^T).
+  // Q fragments (B operand of S^T = K Q^T).  For c < 0 the rows are negated
+  // (exact) and |c| is used, so the tile max is taken on raw scores.
+  // |c| log2(e) is clamped to >= 1e-30: for c = 0 every score then maps to
+  // exp2(~1e-24) = 1.0f exactly, while masked scores (-inf) stay -inf.
+  const bool neg = p.scale2 < 0.f;
+  const float scale2 = fmaxf(fabsf(p.scale2), 1e-30f);
   typedef typename std::conditional<BF16, bf16x8, float>::type QFrag;
   QFrag qf[S::NQF];
 #pragma unroll
   for (int ks = 0; ks < S::NQF; ++ks) {
     if constexpr (BF16) {
-      if (qvalid)
-        qf[ks] = *reinterpret_cast<const bf16x8*>(Qb + (q * p.sq[2] + 16 * ks + 8 * hh) * 2);
-      else
-        qf[ks] = bf16x8{};
+      u32x4 x = qvalid ? *reinterpret_cast<const u32x4*>(Qb + (q * p.sq[2] + 16 * ks + 8 * hh) * 2)
+                       : u32x4{0, 0, 0, 0};
+      if (neg) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      qf[ks] = *reinterpret_cast<bf16x8*>(&x);
     } else {
-      qf[ks] = qvalid ? *reinterpret_cast<const float*>(Qb + (q * p.sq[2] + 2 * ks + hh) * 4) : 0.f;
+      const float x = qvalid ? *reinterpret_cast<const float*>(Qb + (q * p.sq[2] + 2 * ks + hh) * 4) : 0.f;
+      qf[ks] = neg ? -x : x;
     }
   }
 
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           }
         }
       }
-      // Scale into the base-2 domain, mask partial tiles, tile row max.
+      // Mask partial tiles; tile row max on raw scores (scale2 >= 0).
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < S::NKB; ++kb) {
@@ -215,53 +227,53 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         if constexpr (MASK == kMaskBitmask) {
           if (cls == kTilePartial && qvalid && k0 + 32 * kb < n) word = mrow[(k0 + 32 * kb) >> 5];
         }
+        if (cls == kTilePartial) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float t = s[kb][r] * p.scale2;
-          if (cls == kTilePartial) {
+          for (int r = 0; r < 16; ++r) {
             const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
             const int64_t key = k0 + kk;
             bool ok = key < n;
             if constexpr (MASK == kMaskCausal) ok = ok && key <= q;
-            if constexpr (MASK == kMaskBitmask) {
-              // Rows past n are computed and discarded; their words are not read.
-              ok = ok && ((word >> (kk & 31)) & 1u);
-            }
-            t = ok ? t : -INFINITY;
+            if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> (kk & 31)) & 1u);
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
           }
-          s[kb][r] = t;
-          mx = fmaxf(mx, t);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       }
-      mx = max_halves(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no -inf - -inf
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f, pusum = 0.f;
+      mx = max_halves(mx) * scale2;  // base-2 units; -inf stays -inf (scale2 > 0)
+      // Raise the reference max only when it is exceeded by more than the
+      // slack (wave-uniform decision).
+      if (__ballot(mx > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        l_use *= alpha;
+#pragma unroll
+        for (int vb = 0; vb < S::NVB; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[vb][r] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       uint32_t pk[S::NKB][8];  // bf16 path: weights packed in pairs for the PV MFMA
 #pragma unroll
       for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(s[kb][r] - m_use);
-          const float p1 = fast_exp2(s[kb][r + 1] - m_use);
-          psum += p0 + p1;
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale2, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale2, neg_m));
+          l_run += p0 + p1;
           if constexpr (BF16) {
             const uint32_t u = pack_bf16x2(p0, p1);
             pk[kb][r / 2] = u;
-            pusum += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+            l_use = __builtin_amdgcn_fdot2_f32_bf16(*reinterpret_cast<const bf16x2*>(&u), ones_bf16x2(), l_use, false);
           } else {
             s[kb][r] = p0;
             s[kb][r + 1] = p1;
           }
         }
-      l_run = l_run * alpha + psum;
-      l_use = l_use * alpha + (BF16 ? pusum : psum);
-      m_run = m_new;
-#pragma unroll
-      for (int vb = 0; vb < S::NVB; ++vb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[vb][r] *= alpha;
+      if constexpr (!BF16) l_use = l_run;
 
       // O^T += V^T P^T.
       if constexpr (BF16) {

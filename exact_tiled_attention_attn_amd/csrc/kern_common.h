@@ -61,6 +61,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return *reinterpret_cast<uint32_t*>(&y);
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ bf16x2 ones_bf16x2() {
+  const uint32_t u = 0x3F803F80u;  // (1.0, 1.0)
+  return *reinterpret_cast<const bf16x2*>(&u);
+}
 
 // Max over the two 32-lane halves holding the same column (lane l and l^32).
 __device__ __forceinline__ float max_halves(float x) {
