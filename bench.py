@@ -36,7 +36,24 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A copy kernel of known size: 1 GiB read + 1 GiB written per launch, 3 launches."""
+    import torch
+
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": 3}), flush=True)
 
 
 def cpu_baseline(prob, budget_s: float) -> dict:
@@ -88,6 +105,9 @@ def cpu_baseline(prob, budget_s: float) -> dict:
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "

@@ -111,13 +111,49 @@ __device__ __forceinline__ uint32_t tr_addr(int lane, int k0, int n0, int stride
   return (uint32_t)((k0 + (i >> 2)) * stride + (n0 + 4 * (i & 3)) * 2);
 }
 
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
-  bf16x8 r;
-  i16x4* p = reinterpret_cast<i16x4*>(&r);
-  p[0] = lo;
-  p[1] = hi;
-  return r;
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero (gfx9 descriptor word 3 = 0x00020000, 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes < 0 ? 0 : bytes, 0x00020000);
+}
+
+// Swizzled LDS tile layout.  A tile row holds CPR 16-byte chunks.  LDS has
+// 64 four-byte banks, so a wave's 16-lane b128 row reads (16 rows, one chunk
+// each) and 32-lane transposed b64 reads (4 rows x an aligned quad of chunks)
+// are conflict-free when the chunk index is XORed with a row-dependent value
+// whose low 2 bits spread the 16 rows of a b128 read and whose bits 2..3
+// separate the 4 rows of a transposed read:
+//   256-byte rows (CPR % 16 == 0): c ^ (4 (r % 4) + (r / 4) % 4)
+//   128-byte rows (CPR == 8, two rows per bank line): c ^ (4 ((r / 2) % 2) + (r / 4) % 4)
+// Other widths are padded by one chunk instead.
+template <int CPR>
+struct Swz {
+  static constexpr bool kSwizzle = (CPR % 16 == 0) || CPR == 8;
+  static constexpr int kStride = kSwizzle ? CPR * 16 : CPR * 16 + 16;  // bytes per row
+  static __device__ __forceinline__ int chunk(int r, int c) {
+    if constexpr (CPR % 16 == 0) return c ^ (4 * (r & 3) + ((r >> 2) & 3));
+    else if constexpr (CPR == 8) return c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+    else return c;
+  }
+  // Byte offset of chunk c of row r.
+  static __device__ __forceinline__ uint32_t off(int r, int c) {
+    return (uint32_t)(r * kStride + chunk(r, c) * 16);
+  }
+  // Byte offset of 4-byte element e (fp32 tiles) or the pair holding bf16 2e.
+  static __device__ __forceinline__ uint32_t off_dword(int r, int e) { return off(r, e >> 2) + (e & 3) * 4; }
+  // Lane address of a transposed read of bf16 rows k0..k0+3 (k0 % 4 == 0),
+  // columns n0..n0+15 (n0 % 8 == 0): lane i of its 16-lane group reads the
+  // 8 bytes at row k0 + i/4, column n0 + 4 (i % 4).
+  static __device__ __forceinline__ uint32_t tr(int lane, int k0, int n0) {
+    const int i = lane & 15;
+    return off(k0 + (i >> 2), (n0 >> 3) + ((i & 3) >> 1)) + 8 * (i & 1);
+  }
+};
 
 // Pack 8 fp32 accumulator values (registers r0..r0+7 of a 32x32 C block)
 // as a bf16x8 MFMA operand, RNE.
