@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
+    ap.add_argument("--deterministic", type=int, default=1, choices=(0, 1),
+                    help="backward dQ path: 1 = query-tile-outer kernel (default), 0 = fp32 atomics")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -143,11 +145,13 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     pf = E.make_problem(q, k, v, o, w.scale, w.mask, mask)
     ws_f = torch.empty(max(E.workspace_size(pf, False), 256), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(E.workspace_size(pf, True), 256), dtype=torch.uint8, device=dev)
+    pf_b = E.make_problem(q, k, v, o, w.scale, w.mask, mask, bool(args.deterministic))
+    ws_b = torch.empty(max(E.workspace_size(pf_b, True), 256), dtype=torch.uint8, device=dev)
 
     def step():
         E.fwd(q, k, v, w.scale, w.mask, mask, out=o, lse=lse, workspace=ws_f)
-        E.bwd(q, k, v, o, g, lse, w.scale, w.mask, mask, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        E.bwd(q, k, v, o, g, lse, w.scale, w.mask, mask, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+              deterministic=bool(args.deterministic))
 
     for _ in range(args.warmup):
         step()
@@ -172,10 +176,17 @@ def main():
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     avg = {kname: (ms / cnt if cnt else 0.0) for kname, (ms, cnt) in kern.items()}
     fwd_ms = avg["fwd"] + (avg["tile_map"] if w.mask == W.MASK_BITMASK else 0.0)
-    bwd_ms = avg["bwd_pre"] + avg["bwd"] + avg["bwd_post"] + (avg["tile_map"] if w.mask == W.MASK_BITMASK else 0.0)
+    n_maps_bwd = (2 if args.deterministic else 1) if w.mask == W.MASK_BITMASK else 0
+    bwd_ms = avg["bwd_pre"] + avg["bwd"] + avg["bwd_post"] + avg["bwd_dq"] + n_maps_bwd * avg["tile_map"]
     peak = PEAK_TFLOPS[w.dtype]
-    kflops = {"fwd": f_fwd, "bwd": f_bwd}
-    dominant = max(("fwd", "bwd"), key=lambda kname: kern[kname][0])
+    # Algorithmic FLOPs each main kernel performs per launch: the forward
+    # 2#A(d+v); the key-tile-outer backward 2#A(2d+2v) (S, dP, dV, dK) plus
+    # 2#A d for dQ when fused; the query-tile-outer dQ kernel 2#A(2d+v).
+    pairs_f = float(pairs)
+    kflops = {"fwd": f_fwd,
+              "bwd": 2 * pairs_f * (2 * w.d + 2 * w.v) + (0 if args.deterministic else 2 * pairs_f * w.d),
+              "bwd_dq": 2 * pairs_f * (2 * w.d + w.v)}
+    dominant = max(("fwd", "bwd", "bwd_dq"), key=lambda kname: kern[kname][0])
     achieved = kflops[dominant] / (avg[dominant] * 1e-3) / 1e12
     out = {
         "metric": "attention fwd+bwd TFLOP/s on 1 MI355X (algorithmic FLOPs over allowed pairs)",
@@ -197,7 +208,8 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
                 "pct_peak": round(100 * f_bwd / (bwd_ms * 1e-3) / 1e12 / peak, 2)},
         "kernels_avg_ms": {kname: round(x, 4) for kname, x in avg.items() if kern[kname][1]},
-        "roofline": {"kernel": f"{dominant} (attn_{dominant} main kernel)", "bound": "mfma",
+        "backward_dq_path": "query-tile-outer kernel" if args.deterministic else "fp32 atomics",
+        "roofline": {"kernel": dominant, "flops_per_launch": kflops[dominant], "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": None},
     }

@@ -26,7 +26,7 @@ STATUS = {
 EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map",
            "attn_timing_enable", "attn_timing_read", "attn_timing_reset",
            "attn_status_str", "attn_last_error", "attn_version"]
-KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post"]
+KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post", "bwd_dq"]
 
 
 class AttnError(RuntimeError):
@@ -163,8 +163,12 @@ def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, work
 
 
 def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=None, dv=None,
-        workspace=None):
-    """dQ, dK, dV (dtype of q) from the forward's O and L and the upstream dO."""
+        workspace=None, deterministic=False):
+    """dQ, dK, dV (dtype of q) from the forward's O and L and the upstream dO.
+
+    ``deterministic`` selects the query-tile-outer dQ kernel (bitwise
+    reproducible) instead of fp32 atomics in the key-tile-outer kernel.
+    """
     lib = load_library()
     if do.stride() != o.stride():
         if not o.is_contiguous():
@@ -177,7 +181,7 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
         raise ValueError("dQ, dK, dV must have the strides of Q, K, V")
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, H, n]")
-    p = make_problem(q, k, v, o, scale, mask_mode, mask)
+    p = make_problem(q, k, v, o, scale, mask_mode, mask, deterministic)
     need = workspace_size(p, True)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
@@ -186,8 +190,11 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
     return dq, dk, dv
 
 
-def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=False):
-    """The kernels' (query tile x key tile) classification as uint8 [units, tq, tk]."""
+def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=0):
+    """The kernels' (query tile x key tile) classification as uint8 [units, tq, tk].
+
+    is_bwd: 0 forward, 1 key-tile-outer backward, 2 query-tile-outer dQ.
+    """
     lib = load_library()
     p = make_problem(q, k, v, v, scale, mask_mode, mask)
     bq, bk, tq, tk = (ctypes.c_int32() for _ in range(4))

@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libattn.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_aux.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_aux.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",
@@ -30,6 +30,10 @@ DEVICE = [
     "--offload-arch=gfx950",
     # Never emit packed fp32 VALU ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep MFMA sources and accumulators in VGPRs: with AGPR-form MFMAs the
+    # backward's loop-carried dK/dV accumulators were copied between AGPRs
+    # and VGPRs every iteration.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

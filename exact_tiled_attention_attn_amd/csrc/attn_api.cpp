@@ -47,22 +47,33 @@ Tiles bwd_tiles(const attn_problem& p) {
 
 int64_t mask_units(const attn_problem& p) { return p.mask_sb == 0 ? p.H : p.B * p.H; }
 
+Tiles dq_tiles(const attn_problem& p) {
+  return Tiles{eta::kDqBq, eta::kDqBk, cdiv(p.n, eta::kDqBq), cdiv(p.n, eta::kDqBk)};
+}
+
 struct Layout {
   size_t total = 0;
-  size_t off_D = 0, off_dQ = 0, off_map = 0;
-  size_t map_bytes = 0;
+  size_t off_D = 0, off_dQ = 0, off_map = 0, off_map_dq = 0;
+  size_t map_bytes = 0, map_dq_bytes = 0, dq_bytes = 0;
 };
 
+// Backward workspace: D (fp32 [B,H,n]); the atomic path adds the fp32 dQ
+// accumulator, the deterministic path the bitmask map at the dQ tiling.
 Layout plan(const attn_problem& p, int is_bwd) {
   Layout l;
   const int64_t units = p.B * p.H;
+  const bool bitmask = p.mask_mode == ATTN_MASK_BITMASK;
   if (is_bwd) {
-    const Tiles t = bwd_tiles(p);
+    const Tiles t = bwd_tiles(p), tq = dq_tiles(p);
+    const bool det = p.deterministic != 0;
     l.off_D = 0;
     l.off_dQ = align_up(size_t(4) * units * p.n);
-    l.off_map = l.off_dQ + align_up(size_t(4) * units * p.n * p.d);
-    l.map_bytes = p.mask_mode == ATTN_MASK_BITMASK ? size_t(mask_units(p) * t.tq * t.tk) : 0;
-    l.total = l.off_map + align_up(l.map_bytes);
+    l.dq_bytes = det ? 0 : size_t(4) * units * p.n * p.d;
+    l.off_map = l.off_dQ + align_up(l.dq_bytes);
+    l.map_bytes = bitmask ? size_t(mask_units(p) * t.tq * t.tk) : 0;
+    l.off_map_dq = l.off_map + align_up(l.map_bytes);
+    l.map_dq_bytes = (bitmask && det) ? size_t(mask_units(p) * tq.tq * tq.tk) : 0;
+    l.total = l.off_map_dq + align_up(l.map_dq_bytes);
   } else {
     const Tiles t = fwd_tiles(p);
     l.off_map = 0;
@@ -131,8 +142,8 @@ attn_status validate_problem(const attn_problem* p) {
   if (!eta::supported_dims(p->d, p->v))
     return fail(ATTN_ERR_UNSUPPORTED, "(d, v) = (%lld, %lld) not compiled; supported: (64,64) (80,80) "
                 "(128,128) (64,128)", (long long)p->d, (long long)p->v);
-  if (p->deterministic != 0)
-    return fail(ATTN_ERR_UNSUPPORTED, "deterministic dQ accumulation is not available");
+  if (p->deterministic != 0 && p->deterministic != 1)
+    return fail(ATTN_ERR_UNSUPPORTED, "deterministic must be 0 or 1");
   if (p->reserved != 0) return fail(ATTN_ERR_UNSUPPORTED, "reserved field must be 0");
   if (!std::isfinite(p->scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
   if (p->mask_mode == ATTN_MASK_BITMASK) {
@@ -332,7 +343,7 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.dO = dO;
   b.L = L;
   b.Dv = reinterpret_cast<float*>(wsb + lay.off_D);
-  b.dQacc = reinterpret_cast<float*>(wsb + lay.off_dQ);
+  b.dQacc = lay.dq_bytes ? reinterpret_cast<float*>(wsb + lay.off_dQ) : nullptr;
   b.dQ = dQ;
   b.dK = dK;
   b.dV = dV;
@@ -351,21 +362,36 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.grid_pad = pad8(b.total);
   b.scale = (float)p->scale;
   b.scale2 = (float)(p->scale * 1.4426950408889634);
-  if (b.grid_pad > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
+  const bool det = p->deterministic != 0;
+  const Tiles tdq = dq_tiles(*p);
+  b.map_dq = lay.map_dq_bytes ? reinterpret_cast<uint8_t*>(wsb + lay.off_map_dq) : nullptr;
+  b.tq_dq = (int32_t)tdq.tq;
+  b.total_dq = p->B * p->H * tdq.tq;
+  b.grid_pad_dq = pad8(b.total_dq);
+  if (b.grid_pad > 0x7FFFFFFF || b.grid_pad_dq > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
   const int bf = p->dtype == ATTN_BF16;
   if ((st = timed(ATTN_KERNEL_BWD_PRE, stream, "D preprocess launch",
-                  [&] { return eta::launch_bwd_pre(b, bf, (int)p->d, (int)p->v, stream); })) != ATTN_OK)
+                  [&] { return eta::launch_bwd_pre(b, bf, (int)p->d, (int)p->v, !det, stream); })) != ATTN_OK)
     return st;
   if (p->mask_mode == ATTN_MASK_BITMASK) {
     const eta::MapParams mp = map_params(*p, t, const_cast<uint8_t*>(b.map), (int)mask_units(*p));
     if ((st = timed(ATTN_KERNEL_TILE_MAP, stream, "tile map launch",
                     [&] { return eta::launch_tile_map(mp, stream); })) != ATTN_OK)
       return st;
+    if (det) {
+      const eta::MapParams mq = map_params(*p, tdq, const_cast<uint8_t*>(b.map_dq), (int)mask_units(*p));
+      if ((st = timed(ATTN_KERNEL_TILE_MAP, stream, "tile map launch",
+                      [&] { return eta::launch_tile_map(mq, stream); })) != ATTN_OK)
+        return st;
+    }
   }
   if ((st = timed(ATTN_KERNEL_BWD, stream, "backward launch", [&] {
-         return eta::launch_bwd(b, bf, (int)p->d, (int)p->v, p->mask_mode, stream);
+         return eta::launch_bwd(b, bf, (int)p->d, (int)p->v, p->mask_mode, !det, stream);
        })) != ATTN_OK)
     return st;
+  if (det)
+    return timed(ATTN_KERNEL_BWD_DQ, stream, "dQ launch",
+                 [&] { return eta::launch_bwd_dq(b, bf, (int)p->d, (int)p->v, p->mask_mode, stream); });
   return timed(ATTN_KERNEL_BWD_POST, stream, "dQ conversion launch",
                [&] { return eta::launch_bwd_post(b, bf, (int)p->d, stream); });
 }
@@ -378,7 +404,8 @@ attn_status attn_debug_tile_map(const attn_problem* p, int is_bwd, uint8_t* map_
   attn_status st = validate_problem(p);
   if (st != ATTN_OK) return st;
   if (!bq || !bk || !tq || !tk) return fail(ATTN_ERR_NULL, "size outputs must not be NULL");
-  const Tiles t = is_bwd ? bwd_tiles(*p) : fwd_tiles(*p);
+  if (is_bwd < 0 || is_bwd > 2) return fail(ATTN_ERR_SHAPE, "is_bwd must be 0, 1 or 2");
+  const Tiles t = is_bwd == 2 ? dq_tiles(*p) : is_bwd ? bwd_tiles(*p) : fwd_tiles(*p);
   *bq = t.bq;
   *bk = t.bk;
   *tq = (int32_t)t.tq;

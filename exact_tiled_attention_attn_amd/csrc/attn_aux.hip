@@ -7,8 +7,9 @@
 //   page, part 3).  Integer OR/AND over the mask words: HBM-bound.
 // * bwd_pre_kernel: D_i = <dO_i, O_i> in fp32 (HarshvardhanJ README,
 //   backward section: D costs O(n d) and replaces a pass over P; ob1 page,
-//   part 2) and clears the fp32 dQ accumulator.
+//   part 2) and, on the atomic path, clears the fp32 dQ accumulator.
 // * bwd_post_kernel: dQ = c * accumulator, converted to the output type.
+#include "../../include/attn.h"
 #include "attn_internal.h"
 #include "kern_common.h"
 
@@ -103,10 +104,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_
     reinterpret_cast<f32x4*>(p.dQacc)[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, void* stream) {
+int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, bool clear_dq, void* stream) {
   const int64_t rows = (int64_t)p.B * p.H * p.n;
   const int64_t blocks = (rows + 15) / 16;
-  const int64_t zero_n4 = rows * d / 4;
+  const int64_t zero_n4 = clear_dq ? rows * d / 4 : 0;
   hipStream_t st = (hipStream_t)stream;
   dim3 g((unsigned)blocks), b(256);
 #define ETA_PRE(BF, DVV) hipLaunchKernelGGL((bwd_pre_kernel<BF, DVV>), g, b, 0, st, p, zero_n4)
@@ -224,7 +225,7 @@ int timing_read(double* ms, int64_t* launches) {
     if (e == hipSuccess) e = hipEventElapsedTime(&el, t.start, t.stop);
     if (e != hipSuccess) {
       err = (int)e;
-    } else if (t.kind >= 0 && t.kind < 5) {
+    } else if (t.kind >= 0 && t.kind < ATTN_KERNEL_COUNT) {
       ms[t.kind] += el;
       launches[t.kind] += 1;
     }

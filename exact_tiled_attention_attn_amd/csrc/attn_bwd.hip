@@ -1,26 +1,30 @@
-// Backward kernel: block-recomputed vector-Jacobian product.
+// Backward, key-tile-outer kernel: dK, dV (and, fused, dQ by atomics).
 //
 // Method (alphabetamath page, reverse procedure; ob1 page, part 2;
 // HarshvardhanJ README, backward section): with the forward's L and
 // D_i = <dO_i, O_i>, for each block recompute s_ij = c <Q_i, K_j>,
 // p_ij = exp(s_ij - L_i), dP_ij = <dO_i, V_j>, dS_ij = p_ij (dP_ij - D_i), and
-// accumulate dV_j += p_ij dO_i, dK_j += c dS_ij Q_i, dQ_i += c dS_ij K_j.
+// accumulate dV_j += p_ij dO_i, dK_j += c dS_ij Q_i (and dQ_i += c dS_ij K_j).
 // No score or probability matrix is stored.
 //
-// gfx950 design (key-tile outer).  One workgroup owns 128 keys (32 per
-// wave); each wave keeps its K and V rows in registers as MFMA B operands
-// and its dK^T, dV^T accumulators in registers for the whole loop over
-// query tiles.  Per query tile the workgroup stages Q, dO, L and D through
-// double-buffered LDS.  Scores and dP are formed as S = Q K^T and
-// dP = dO V^T with one key per lane column, so the accumulator registers
-// holding P and dS are directly the B operand of dV^T += dO^T P and
-// dK^T += Q^T dS; the dO^T and Q^T operands come from the row-major LDS
-// tiles through transposed reads whose addresses follow the order in which
-// a lane holds its query rows.  dS is written to LDS (key-major) and read
-// back with transposed reads as the A operand of dQ = dS K, which the
-// workgroup adds into an fp32 accumulator with hardware float atomics
-// (coalesced: consecutive lanes hit consecutive d).  Fully masked query
-// tiles are skipped; only partial ones are masked.
+// gfx950 design.  One workgroup owns 128 keys (32 per wave); each wave keeps
+// its K and V rows in registers as MFMA B operands and its dK^T, dV^T
+// accumulators in registers for the whole loop over query tiles.  Per query
+// tile the workgroup stages Q, dO, L and D through double-buffered,
+// XOR-swizzled LDS (buffer loads: rows past n read as zero).  Scores and dP
+// are formed as S = Q K^T and dP = dO V^T with one key per lane column, so
+// the registers holding P and dS are directly the B operand of
+// dV^T += dO^T P and dK^T += Q^T dS; the dO^T and Q^T operands come from the
+// row-major LDS tiles through transposed reads whose addresses follow the
+// order in which a lane holds its query rows.  Query tiles are visited from
+// the last one down, so the workgroups of one head running together read
+// the same Q and dO tiles.
+//
+// FUSED additionally forms dQ: dS is written to LDS (key-major) and read
+// back with transposed reads as the A operand of dQ = dS K, added into an
+// fp32 accumulator with buffer float atomics (rows past n are dropped by the
+// buffer range check).  Without FUSED, dQ comes from the query-tile-outer
+// kernel instead (deterministic, no atomics).
 #include "attn_internal.h"
 #include "kern_common.h"
 
@@ -38,76 +42,78 @@ struct BwdShape {
   static constexpr int NDB = DP / 32;
   static constexpr int NVB = DVP / 32;
   static constexpr int NQB = BQ / 32;
-  static constexpr int KSTR = DP * ES + (BF16 ? 32 : 16);   // K tile (tr reads for dQ)
-  static constexpr int QSTR = DP * ES + (BF16 ? 32 : 16);   // Q tile (row + tr reads)
-  static constexpr int OSTR = DVP * ES + (BF16 ? 32 : 16);  // dO tile (row + tr reads)
-  static constexpr int SSTR = BQ * ES + (BF16 ? 32 : 16);   // dS^T tile [key][q]
-  static constexpr int KTILE = BK * KSTR;
-  static constexpr int QTILE = BQ * QSTR;
-  static constexpr int OTILE = BQ * OSTR;
-  static constexpr int STILE = BK * SSTR;
+  static constexpr int QCH = D * ES / 16;   // loaded chunks per Q row
+  static constexpr int OCH = DV * ES / 16;  // loaded chunks per dO row
+  using QT = Swz<DP * ES / 16>;
+  using OT = Swz<DVP * ES / 16>;
+  using KTl = Swz<DP * ES / 16>;  // resident K tile (fused dQ phase)
+  using ST = Swz<BQ * ES / 16>;   // dS^T tile [key][query] (fused dQ phase)
+  static constexpr int KTILE = BK * KTl::kStride;
+  static constexpr int QTILE = BQ * QT::kStride;
+  static constexpr int OTILE = BQ * OT::kStride;
+  static constexpr int STILE = BK * ST::kStride;
   static constexpr int MWORDS = BK / 32;  // mask words per query row per key tile
   // Per buffer: Q tile, dO tile, L (base 2), D, mask words.
   static constexpr int BUF = QTILE + OTILE + BQ * 4 * 2 + BQ * MWORDS * 4;
-  static constexpr int SMEM = KTILE + 2 * BUF + STILE;
-  static constexpr int QCH = D * ES / 16;
-  static constexpr int OCH = DV * ES / 16;
   static constexpr int QLD = (BQ * QCH + 255) / 256;
   static constexpr int OLD = (BQ * OCH + 255) / 256;
+  static constexpr int smem(bool fused) { return 2 * BUF + (fused ? KTILE + STILE : 0); }
 };
 
-template <bool BF16, int D, int DV, int MASK>
+template <bool BF16, int D, int DV, int MASK, bool FUSED>
 __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   using S = BwdShape<BF16, D, DV>;
-  __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
-  char* Ks = smem;
-  char* dSs = smem + S::KTILE + 2 * S::BUF;
+  __shared__ __attribute__((aligned(16))) char smem[S::smem(FUSED)];
+  char* bufs = smem;
+  char* Ks = smem + 2 * S::BUF;     // fused only
+  char* dSs = Ks + S::KTILE;        // fused only
 
   const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad, p.total);
   if (logical < 0) return;
-  const int64_t unit = logical / p.tk;
+  const int unit = (int)(logical / p.tk);
   const int kt = (int)(logical % p.tk);  // low key tiles (most causal work) first
-  const int b = (int)(unit / p.H), h = (int)(unit % p.H);
-  const int64_t n = p.n;
-  const int64_t k0 = (int64_t)kt * S::BK;
+  const int b = unit / p.H, h = unit % p.H;
+  const int n = (int)p.n;
+  const int k0 = kt * S::BK;
 
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid % kWave;
-  const int hh = lane / 32;
+  const int hh = lane >> 5;
   const int g1 = (lane >> 4) & 1;
   const int klocal = 32 * w + (lane & 31);
-  const int64_t key = k0 + klocal;
+  const int key = k0 + klocal;
   const bool kvalid = key < n;
 
-  const char* Qb = (const char*)p.Q + (b * p.sq[0] + h * p.sq[1]) * S::ES;
-  const char* Kb = (const char*)p.K + (b * p.sk[0] + h * p.sk[1]) * S::ES;
-  const char* Vb = (const char*)p.V + (b * p.sv[0] + h * p.sv[1]) * S::ES;
-  const char* dOb = (const char*)p.dO + (b * p.so[0] + h * p.so[1]) * S::ES;
-  const float* Lb = p.L + unit * n;
-  const float* Db = p.Dv + unit * n;
-  float* dQa = p.dQacc + unit * n * D;
+  const int qrow = (int)p.sq[2] * S::ES, krow = (int)p.sk[2] * S::ES;
+  const int vrow = (int)p.sv[2] * S::ES, orow = (int)p.so[2] * S::ES;
+  const char* Qb = (const char*)p.Q + ((int64_t)b * p.sq[0] + (int64_t)h * p.sq[1]) * S::ES;
+  const char* Kb = (const char*)p.K + ((int64_t)b * p.sk[0] + (int64_t)h * p.sk[1]) * S::ES;
+  const char* Vb = (const char*)p.V + ((int64_t)b * p.sv[0] + (int64_t)h * p.sv[1]) * S::ES;
+  const char* dOb = (const char*)p.dO + ((int64_t)b * p.so[0] + (int64_t)h * p.so[1]) * S::ES;
+  const float* Lb = p.L + (int64_t)unit * n;
+  const float* Db = p.Dv + (int64_t)unit * n;
 
-  // Resident K tile in LDS (B operand of dQ), padded columns cleared.
-  {
+  if constexpr (FUSED) {
+    // Resident K tile in LDS (B operand of dQ), padded columns cleared.
     constexpr int KCH = S::DP * S::ES / 16;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (n - k0) * krow);
     for (int c = tid; c < S::BK * KCH; c += 256) {
       const int r = c / KCH, cc = c % KCH;
-      const int64_t kr = k0 + r;
       u32x4 x = u32x4{0, 0, 0, 0};
-      if (kr < n && cc * 16 < D * S::ES) x = *reinterpret_cast<const u32x4*>(Kb + kr * p.sk[2] * S::ES + cc * 16);
-      *reinterpret_cast<u32x4*>(Ks + r * S::KSTR + cc * 16) = x;
+      if (cc * 16 < D * S::ES) x = __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow + cc * 16, 0, 0);
+      *reinterpret_cast<u32x4*>(Ks + S::KTl::off(r, cc)) = x;
     }
-    // Clear padded columns of both Q / dO buffers once.
-    if constexpr (S::DP != D || S::DVP != DV) {
-      for (int bufi = 0; bufi < 2; ++bufi) {
-        char* Qs = smem + S::KTILE + bufi * S::BUF;
-        char* Os = Qs + S::QTILE;
-        constexpr int qpc = (S::DP - D) * S::ES / 16, opc = (S::DVP - DV) * S::ES / 16;
-        for (int c = tid; c < S::BQ * qpc; c += 256)
-          *reinterpret_cast<u32x4*>(Qs + (c / qpc) * S::QSTR + D * S::ES + (c % qpc) * 16) = u32x4{0, 0, 0, 0};
-        for (int c = tid; c < S::BQ * opc; c += 256)
-          *reinterpret_cast<u32x4*>(Os + (c / opc) * S::OSTR + DV * S::ES + (c % opc) * 16) = u32x4{0, 0, 0, 0};
-      }
+  }
+  // Clear the padded columns of both Q / dO buffers once.
+  if constexpr (S::DP != D || S::DVP != DV) {
+    for (int bi = 0; bi < 2; ++bi) {
+      char* Qs = bufs + bi * S::BUF;
+      char* Os = Qs + S::QTILE;
+      constexpr int qpc = (S::DP - D) * S::ES / 16, opc = (S::DVP - DV) * S::ES / 16;
+      for (int c = tid; c < S::BQ * qpc; c += 256)
+        *reinterpret_cast<u32x4*>(Qs + S::QT::off(c / qpc, S::QCH + c % qpc)) = u32x4{0, 0, 0, 0};
+      for (int c = tid; c < S::BQ * opc; c += 256)
+        *reinterpret_cast<u32x4*>(Os + S::OT::off(c / opc, S::OCH + c % opc)) = u32x4{0, 0, 0, 0};
     }
   }
 
@@ -115,19 +121,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   typedef typename std::conditional<BF16, bf16x8, float>::type Frag;
   constexpr int NKF = D / S::KSTEP, NVF = DV / S::KSTEP;
   Frag kf[NKF], vf[NVF];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, n * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, n * vrow);
 #pragma unroll
-  for (int s = 0; s < NKF; ++s) {
-    if constexpr (BF16)
-      kf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(Kb + (key * p.sk[2] + 16 * s + 8 * hh) * 2) : bf16x8{};
-    else
-      kf[s] = kvalid ? *reinterpret_cast<const float*>(Kb + (key * p.sk[2] + 2 * s + hh) * 4) : 0.f;
-  }
+    for (int s = 0; s < NKF; ++s) {
+      if constexpr (BF16)
+        kf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * krow + (16 * s + 8 * hh) * 2, 0, 0));
+      else
+        kf[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, key * krow + (2 * s + hh) * 4, 0, 0));
+    }
 #pragma unroll
-  for (int s = 0; s < NVF; ++s) {
-    if constexpr (BF16)
-      vf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(Vb + (key * p.sv[2] + 16 * s + 8 * hh) * 2) : bf16x8{};
-    else
-      vf[s] = kvalid ? *reinterpret_cast<const float*>(Vb + (key * p.sv[2] + 2 * s + hh) * 4) : 0.f;
+    for (int s = 0; s < NVF; ++s) {
+      if constexpr (BF16)
+        vf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, key * vrow + (16 * s + 8 * hh) * 2, 0, 0));
+      else
+        vf[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, key * vrow + (2 * s + hh) * 4, 0, 0));
+    }
   }
 
   f32x16 dk[S::NDB], dv[S::NVB];
@@ -136,9 +146,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < S::NVB; ++i) dv[i] = f32x16{};
 
-  // Query-tile range and classification for this key tile.
-  int qt_begin = 0;
-  if constexpr (MASK == kMaskCausal) qt_begin = (int)(k0 / S::BQ);
+  // Query tiles are visited from the last down to the first one that can
+  // hold an allowed pair (causal: the tile containing row k0).
+  int qt_first = 0;
+  if constexpr (MASK == kMaskCausal) qt_first = k0 / S::BQ;
   const uint8_t* map_col = nullptr;
   const uint32_t* mbase = nullptr;
   if constexpr (MASK == kMaskBitmask) {
@@ -150,37 +161,34 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     if constexpr (MASK == kMaskBitmask) return map_col[(int64_t)qt * p.tk];
     return classify_analytic(MASK, (int64_t)qt * S::BQ, S::BQ, k0, S::BK, n);
   };
-  auto next_tile = [&](int qt) -> int {
-    for (int t = qt + 1; t < p.tq; ++t)
+  auto next_tile = [&](int qt) -> int {  // next (lower) tile with an allowed pair, or -1
+    if constexpr (MASK != kMaskBitmask) return qt - 1 >= qt_first ? qt - 1 : -1;
+    for (int t = qt - 1; t >= qt_first; --t)
       if (tile_class(t) != kTileEmpty) return t;
-    return p.tq;
+    return -1;
   };
 
   u32x4 qreg[S::QLD], oreg[S::OLD];
   float lreg = 0.f, dreg = 0.f;
   uint32_t mreg = 0;
   auto gload = [&](int qt) {
-    const int64_t q0 = (int64_t)qt * S::BQ;
+    const int q0 = qt * S::BQ;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb + (int64_t)q0 * qrow, (n - q0) * qrow);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb + (int64_t)q0 * orow, (n - q0) * orow);
 #pragma unroll
     for (int i = 0; i < S::QLD; ++i) {
       const int c = tid + i * 256;
-      const int r = c / S::QCH, cc = c % S::QCH;
-      const int64_t qq = q0 + r;
-      qreg[i] = (c < S::BQ * S::QCH && qq < n)
-                    ? *reinterpret_cast<const u32x4*>(Qb + qq * p.sq[2] * S::ES + cc * 16)
-                    : u32x4{0, 0, 0, 0};
+      if (S::BQ * S::QCH % 256 == 0 || c < S::BQ * S::QCH)
+        qreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, (c / S::QCH) * qrow + (c % S::QCH) * 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < S::OLD; ++i) {
       const int c = tid + i * 256;
-      const int r = c / S::OCH, cc = c % S::OCH;
-      const int64_t qq = q0 + r;
-      oreg[i] = (c < S::BQ * S::OCH && qq < n)
-                    ? *reinterpret_cast<const u32x4*>(dOb + qq * p.so[2] * S::ES + cc * 16)
-                    : u32x4{0, 0, 0, 0};
+      if (S::BQ * S::OCH % 256 == 0 || c < S::BQ * S::OCH)
+        oreg[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (c / S::OCH) * orow + (c % S::OCH) * 16, 0, 0);
     }
     if (tid < S::BQ) {
-      const int64_t qq = q0 + tid;
+      const int qq = q0 + tid;
       const float Lv = qq < n ? Lb[qq] : -INFINITY;
       // Rows with L = -inf (no allowed key, or past n) get +inf: p = exp2(s - inf) = 0.
       lreg = (Lv == -INFINITY) ? INFINITY : Lv * kLog2e;
@@ -189,14 +197,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     if constexpr (MASK == kMaskBitmask) {
       if (tid < S::BQ * S::MWORDS) {
         const int r = tid / S::MWORDS, wi = tid % S::MWORDS;
-        const int64_t qq = q0 + r;
-        const int64_t wd = (k0 >> 5) + wi;
-        mreg = (qq < n && wd * 32 < n) ? mbase[qq * p.mask_si + wd] : 0u;
+        const int qq = q0 + r;
+        const int wd = (k0 >> 5) + wi;
+        mreg = (qq < n && wd * 32 < n) ? mbase[(int64_t)qq * p.mask_si + wd] : 0u;
       }
     }
   };
-  auto lstore = [&](int bufi) {
-    char* Qs = smem + S::KTILE + bufi * S::BUF;
+  auto lstore = [&](int bi) {
+    char* Qs = bufs + bi * S::BUF;
     char* Os = Qs + S::QTILE;
     float* Ls = reinterpret_cast<float*>(Os + S::OTILE);
     float* Dsv = Ls + S::BQ;
@@ -204,14 +212,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < S::QLD; ++i) {
       const int c = tid + i * 256;
-      if (c < S::BQ * S::QCH)
-        *reinterpret_cast<u32x4*>(Qs + (c / S::QCH) * S::QSTR + (c % S::QCH) * 16) = qreg[i];
+      if (S::BQ * S::QCH % 256 == 0 || c < S::BQ * S::QCH)
+        *reinterpret_cast<u32x4*>(Qs + S::QT::off(c / S::QCH, c % S::QCH)) = qreg[i];
     }
 #pragma unroll
     for (int i = 0; i < S::OLD; ++i) {
       const int c = tid + i * 256;
-      if (c < S::BQ * S::OCH)
-        *reinterpret_cast<u32x4*>(Os + (c / S::OCH) * S::OSTR + (c % S::OCH) * 16) = oreg[i];
+      if (S::BQ * S::OCH % 256 == 0 || c < S::BQ * S::OCH)
+        *reinterpret_cast<u32x4*>(Os + S::OT::off(c / S::OCH, c % S::OCH)) = oreg[i];
     }
     if (tid < S::BQ) {
       Ls[tid] = lreg;
@@ -222,20 +230,25 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     }
   };
 
-  int qt = tile_class(qt_begin) != kTileEmpty ? qt_begin : next_tile(qt_begin);
-  if (qt < p.tq) {
+  __amdgpu_buffer_rsrc_t rdq;  // fused: dQ accumulator rows of this unit
+  if constexpr (FUSED) rdq = make_rsrc(p.dQacc + (int64_t)unit * n * D, n * D * 4);
+
+  int qt = p.tq - 1;
+  if (MASK == kMaskBitmask && qt >= qt_first && tile_class(qt) == kTileEmpty) qt = next_tile(qt);
+  if (qt < qt_first) qt = -1;
+  if (qt >= 0) {
     gload(qt);
     lstore(0);
   }
   __syncthreads();
   int buf = 0;
 
-  while (qt < p.tq) {
+  while (qt >= 0) {
     const int nq = next_tile(qt);
     const uint8_t cls = tile_class(qt);
-    if (nq < p.tq) gload(nq);
-    const int64_t q0 = (int64_t)qt * S::BQ;
-    const char* Qs = smem + S::KTILE + buf * S::BUF;
+    if (nq >= 0) gload(nq);
+    const int q0 = qt * S::BQ;
+    const char* Qs = bufs + buf * S::BUF;
     const char* Os = Qs + S::QTILE;
     const float* Ls = reinterpret_cast<const float*>(Os + S::OTILE);
     const float* Dsv = Ls + S::BQ;
@@ -250,23 +263,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int s = 0; s < NKF; ++s) {
-          if constexpr (BF16) {
-            bf16x8 a = lds_read_b128(Qs, (32 * qb + (lane & 31)) * S::QSTR + (16 * s + 8 * hh) * 2);
-            sc = mfma_bf16(a, kf[s], sc);
-          } else {
-            float a = *reinterpret_cast<const float*>(Qs + (32 * qb + (lane & 31)) * S::QSTR + (2 * s + hh) * 4);
-            sc = mfma_f32(a, kf[s], sc);
-          }
+          if constexpr (BF16)
+            sc = mfma_bf16(lds_read_b128(Qs, S::QT::off(32 * qb + (lane & 31), 2 * s + hh)), kf[s], sc);
+          else
+            sc = mfma_f32(*reinterpret_cast<const float*>(Qs + S::QT::off_dword(32 * qb + (lane & 31), 2 * s + hh)),
+                          kf[s], sc);
         }
 #pragma unroll
         for (int s = 0; s < NVF; ++s) {
-          if constexpr (BF16) {
-            bf16x8 a = lds_read_b128(Os, (32 * qb + (lane & 31)) * S::OSTR + (16 * s + 8 * hh) * 2);
-            dp = mfma_bf16(a, vf[s], dp);
-          } else {
-            float a = *reinterpret_cast<const float*>(Os + (32 * qb + (lane & 31)) * S::OSTR + (2 * s + hh) * 4);
-            dp = mfma_f32(a, vf[s], dp);
-          }
+          if constexpr (BF16)
+            dp = mfma_bf16(lds_read_b128(Os, S::OT::off(32 * qb + (lane & 31), 2 * s + hh)), vf[s], dp);
+          else
+            dp = mfma_f32(*reinterpret_cast<const float*>(Os + S::OT::off_dword(32 * qb + (lane & 31), 2 * s + hh)),
+                          vf[s], dp);
         }
         // P = exp2(s c log2e - L log2e); dS = P (dP - D).  Register r holds
         // query row 32 qb + 8 (r/4) + 4 hh + r%4 of the tile.
@@ -278,9 +287,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float pv = fast_exp2(sc[r] * p.scale2 - l4[e]);
+            float pv = fast_exp2(__builtin_fmaf(sc[r], p.scale2, -l4[e]));
             if (cls == kTilePartial) {
-              const int64_t qq = q0 + ql + e;
+              const int qq = q0 + ql + e;
               bool ok = kvalid;
               if constexpr (MASK == kMaskCausal) ok = ok && key <= qq;
               if constexpr (MASK == kMaskBitmask)
@@ -295,30 +304,37 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
         if constexpr (BF16) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 pb = pack8(sc, 8 * ks);
-            const bf16x8 sb = pack8(dp, 8 * ks);
+            const u32x4 pw{pack_bf16x2(sc[8 * ks], sc[8 * ks + 1]), pack_bf16x2(sc[8 * ks + 2], sc[8 * ks + 3]),
+                           pack_bf16x2(sc[8 * ks + 4], sc[8 * ks + 5]), pack_bf16x2(sc[8 * ks + 6], sc[8 * ks + 7])};
+            const u32x4 sw{pack_bf16x2(dp[8 * ks], dp[8 * ks + 1]), pack_bf16x2(dp[8 * ks + 2], dp[8 * ks + 3]),
+                           pack_bf16x2(dp[8 * ks + 4], dp[8 * ks + 5]), pack_bf16x2(dp[8 * ks + 6], dp[8 * ks + 7])};
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            const bf16x8 sb = __builtin_bit_cast(bf16x8, sw);
             const int kr = 32 * qb + 16 * ks + 4 * hh;
 #pragma unroll
             for (int vb = 0; vb < S::NVB; ++vb) {
               const int n0 = vb * 32 + 16 * g1;
-              i16x4 lo = lds_read_tr(Os, tr_addr(lane, kr, n0, S::OSTR));
-              i16x4 hi = lds_read_tr(Os, tr_addr(lane, kr + 8, n0, S::OSTR));
+              const i16x4 lo = lds_read_tr(Os, S::OT::tr(lane, kr, n0));
+              const i16x4 hi = lds_read_tr(Os, S::OT::tr(lane, kr + 8, n0));
               dv[vb] = mfma_bf16(join_tr(lo, hi), pb, dv[vb]);
             }
 #pragma unroll
             for (int db = 0; db < S::NDB; ++db) {
               const int n0 = db * 32 + 16 * g1;
-              i16x4 lo = lds_read_tr(Qs, tr_addr(lane, kr, n0, S::QSTR));
-              i16x4 hi = lds_read_tr(Qs, tr_addr(lane, kr + 8, n0, S::QSTR));
+              const i16x4 lo = lds_read_tr(Qs, S::QT::tr(lane, kr, n0));
+              const i16x4 hi = lds_read_tr(Qs, S::QT::tr(lane, kr + 8, n0));
               dk[db] = mfma_bf16(join_tr(lo, hi), sb, dk[db]);
             }
-          }
-          // dS^T -> LDS (key-major): 4 consecutive query rows per store.
+            if constexpr (FUSED) {
+              // dS^T -> LDS (key-major): 4 consecutive query rows per 8-byte store.
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ql = 32 * qb + 8 * g + 4 * hh;
-            u32x2 pk{pack_bf16x2(dp[4 * g], dp[4 * g + 1]), pack_bf16x2(dp[4 * g + 2], dp[4 * g + 3])};
-            *reinterpret_cast<u32x2*>(dSs + klocal * S::SSTR + ql * 2) = pk;
+              for (int gg = 0; gg < 2; ++gg) {
+                const int g = 2 * ks + gg;
+                const int ql = 32 * qb + 8 * g + 4 * hh;
+                *reinterpret_cast<u32x2*>(dSs + S::ST::off(klocal, ql >> 3) + 8 * ((ql >> 2) & 1)) =
+                    u32x2{sw[2 * gg], sw[2 * gg + 1]};
+              }
+            }
           }
         } else {
 #pragma unroll
@@ -326,73 +342,70 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
             const int ql = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
 #pragma unroll
             for (int vb = 0; vb < S::NVB; ++vb) {
-              float a = *reinterpret_cast<const float*>(Os + ql * S::OSTR + (vb * 32 + (lane & 31)) * 4);
+              const float a = *reinterpret_cast<const float*>(Os + S::OT::off_dword(ql, vb * 32 + (lane & 31)));
               dv[vb] = mfma_f32(a, sc[r], dv[vb]);
             }
 #pragma unroll
             for (int db = 0; db < S::NDB; ++db) {
-              float a = *reinterpret_cast<const float*>(Qs + ql * S::QSTR + (db * 32 + (lane & 31)) * 4);
+              const float a = *reinterpret_cast<const float*>(Qs + S::QT::off_dword(ql, db * 32 + (lane & 31)));
               dk[db] = mfma_f32(a, dp[r], dk[db]);
             }
           }
+          if constexpr (FUSED) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ql = 32 * qb + 8 * g + 4 * hh;
-            *reinterpret_cast<f32x4*>(dSs + klocal * S::SSTR + ql * 4) =
-                f32x4{dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3]};
+            for (int g = 0; g < 4; ++g) {
+              const int ql = 32 * qb + 8 * g + 4 * hh;
+              *reinterpret_cast<f32x4*>(dSs + S::ST::off(klocal, ql >> 2)) =
+                  f32x4{dp[4 * g], dp[4 * g + 1], dp[4 * g + 2], dp[4 * g + 3]};
+            }
           }
         }
       }
-    } else {
+    } else if constexpr (FUSED) {
       // All of this wave's keys are masked for the tile: its dS rows are zero.
-      if constexpr (BF16) {
-        for (int c = lane; c < 32 * S::BQ / 8; c += kWave) {
-          const int r = c / (S::BQ / 8), cc = c % (S::BQ / 8);
-          *reinterpret_cast<u32x4*>(dSs + (32 * w + r) * S::SSTR + cc * 16) = u32x4{0, 0, 0, 0};
-        }
-      } else {
-        for (int c = lane; c < 32 * S::BQ / 4; c += kWave) {
-          const int r = c / (S::BQ / 4), cc = c % (S::BQ / 4);
-          *reinterpret_cast<u32x4*>(dSs + (32 * w + r) * S::SSTR + cc * 16) = u32x4{0, 0, 0, 0};
-        }
+      for (int c = lane; c < 32 * S::BQ * S::ES / 16; c += kWave) {
+        const int r = c / (S::BQ * S::ES / 16), cc = c % (S::BQ * S::ES / 16);
+        *reinterpret_cast<u32x4*>(dSs + S::ST::off(32 * w + r, cc)) = u32x4{0, 0, 0, 0};
       }
     }
-    __syncthreads();  // dS of all 128 keys in LDS
 
-    // dQ (this query tile, all d) += dS K over the workgroup's 128 keys.
-    for (int blk = w; blk < S::NQB * S::NDB; blk += S::NW) {
-      const int qb = blk % S::NQB, db = blk / S::NQB;
-      f32x16 acc = f32x16{};
-      if constexpr (BF16) {
+    if constexpr (FUSED) {
+      __syncthreads();  // dS of all 128 keys in LDS
+      // dQ (this query tile, all d) += dS K over the workgroup's 128 keys.
+      for (int blk = w; blk < S::NQB * S::NDB; blk += S::NW) {
+        const int qb = blk % S::NQB, db = blk / S::NQB;
+        f32x16 acc = f32x16{};
+        if constexpr (BF16) {
 #pragma unroll
-        for (int ks = 0; ks < S::BK / 16; ++ks) {
-          const int kr = 16 * ks + 8 * hh;
-          i16x4 alo = lds_read_tr(dSs, tr_addr(lane, kr, 32 * qb + 16 * g1, S::SSTR));
-          i16x4 ahi = lds_read_tr(dSs, tr_addr(lane, kr + 4, 32 * qb + 16 * g1, S::SSTR));
-          i16x4 blo = lds_read_tr(Ks, tr_addr(lane, kr, 32 * db + 16 * g1, S::KSTR));
-          i16x4 bhi = lds_read_tr(Ks, tr_addr(lane, kr + 4, 32 * db + 16 * g1, S::KSTR));
-          acc = mfma_bf16(join_tr(alo, ahi), join_tr(blo, bhi), acc);
-        }
-      } else {
+          for (int ks = 0; ks < S::BK / 16; ++ks) {
+            const int kr = 16 * ks + 8 * hh;
+            const i16x4 alo = lds_read_tr(dSs, S::ST::tr(lane, kr, 32 * qb + 16 * g1));
+            const i16x4 ahi = lds_read_tr(dSs, S::ST::tr(lane, kr + 4, 32 * qb + 16 * g1));
+            const i16x4 blo = lds_read_tr(Ks, S::KTl::tr(lane, kr, 32 * db + 16 * g1));
+            const i16x4 bhi = lds_read_tr(Ks, S::KTl::tr(lane, kr + 4, 32 * db + 16 * g1));
+            acc = mfma_bf16(join_tr(alo, ahi), join_tr(blo, bhi), acc);
+          }
+        } else {
 #pragma unroll 8
-        for (int ks = 0; ks < S::BK / 2; ++ks) {
-          const int kr = 2 * ks + hh;
-          float a = *reinterpret_cast<const float*>(dSs + kr * S::SSTR + (32 * qb + (lane & 31)) * 4);
-          float bb = *reinterpret_cast<const float*>(Ks + kr * S::KSTR + (32 * db + (lane & 31)) * 4);
-          acc = mfma_f32(a, bb, acc);
+          for (int ks = 0; ks < S::BK / 2; ++ks) {
+            const int kr = 2 * ks + hh;
+            const float a = *reinterpret_cast<const float*>(dSs + S::ST::off_dword(kr, 32 * qb + (lane & 31)));
+            const float bb = *reinterpret_cast<const float*>(Ks + S::KTl::off_dword(kr, 32 * db + (lane & 31)));
+            acc = mfma_f32(a, bb, acc);
+          }
         }
-      }
-      const int dcol = 32 * db + (lane & 31);
-      if (dcol < D) {
+        const int dcol = 32 * db + (lane & 31);
+        if (dcol < D) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t qq = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (qq < n) unsafeAtomicAdd(dQa + qq * D + dcol, acc[r]);
+          for (int r = 0; r < 16; ++r) {
+            const int qq = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], rdq, (qq * D + dcol) * 4, 0, 0);
+          }
         }
       }
     }
 
-    if (nq < p.tq) lstore(buf ^ 1);
+    if (nq >= 0) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
     qt = nq;
@@ -400,8 +413,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 
   // Epilogue: dK = c dK^T, dV = dV^T (lane = key; 4 consecutive columns per store).
   if (kvalid) {
-    char* dKp = (char*)p.dK + (b * p.sk[0] + h * p.sk[1] + key * p.sk[2]) * S::ES;
-    char* dVp = (char*)p.dV + (b * p.sv[0] + h * p.sv[1] + key * p.sv[2]) * S::ES;
+    char* dKp = (char*)p.dK + ((int64_t)b * p.sk[0] + (int64_t)h * p.sk[1] + (int64_t)key * p.sk[2]) * S::ES;
+    char* dVp = (char*)p.dV + ((int64_t)b * p.sv[0] + (int64_t)h * p.sv[1] + (int64_t)key * p.sv[2]) * S::ES;
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db)
 #pragma unroll
@@ -434,32 +447,36 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 }
 
 template <bool BF16, int D, int DV, int MASK>
-static int launch_one(const BwdParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
+static int launch_one(const BwdParams& p, bool fused, hipStream_t st) {
+  if (fused)
+    hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, true>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, false>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 
 template <bool BF16, int D, int DV>
-static int launch_mask(const BwdParams& p, int mask_mode, hipStream_t st) {
+static int launch_mask(const BwdParams& p, int mask_mode, bool fused, hipStream_t st) {
   switch (mask_mode) {
-    case kMaskNone: return launch_one<BF16, D, DV, kMaskNone>(p, st);
-    case kMaskCausal: return launch_one<BF16, D, DV, kMaskCausal>(p, st);
-    default: return launch_one<BF16, D, DV, kMaskBitmask>(p, st);
+    case kMaskNone: return launch_one<BF16, D, DV, kMaskNone>(p, fused, st);
+    case kMaskCausal: return launch_one<BF16, D, DV, kMaskCausal>(p, fused, st);
+    default: return launch_one<BF16, D, DV, kMaskBitmask>(p, fused, st);
   }
 }
 
 template <bool BF16>
-static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, hipStream_t st) {
-  if (d == 64 && v == 64) return launch_mask<BF16, 64, 64>(p, mask_mode, st);
-  if (d == 80 && v == 80) return launch_mask<BF16, 80, 80>(p, mask_mode, st);
-  if (d == 128 && v == 128) return launch_mask<BF16, 128, 128>(p, mask_mode, st);
-  if (d == 64 && v == 128) return launch_mask<BF16, 64, 128>(p, mask_mode, st);
+static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, bool fused, hipStream_t st) {
+  if (d == 64 && v == 64) return launch_mask<BF16, 64, 64>(p, mask_mode, fused, st);
+  if (d == 80 && v == 80) return launch_mask<BF16, 80, 80>(p, mask_mode, fused, st);
+  if (d == 128 && v == 128) return launch_mask<BF16, 128, 128>(p, mask_mode, fused, st);
+  if (d == 64 && v == 128) return launch_mask<BF16, 64, 128>(p, mask_mode, fused, st);
   return (int)hipErrorInvalidValue;
 }
 
-int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream) {
+int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, bool fused, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  return bf16 ? launch_dims<true>(p, d, v, mask_mode, st) : launch_dims<false>(p, d, v, mask_mode, st);
+  return bf16 ? launch_dims<true>(p, d, v, mask_mode, fused, st)
+              : launch_dims<false>(p, d, v, mask_mode, fused, st);
 }
 
 }  // namespace eta

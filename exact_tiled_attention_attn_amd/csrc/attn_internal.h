@@ -13,6 +13,9 @@ constexpr int kFwdBq = 128;
 constexpr int kFwdBk = 64;
 constexpr int kBwdBq = 64;
 constexpr int kBwdBk = 128;
+// Backward dQ (query-tile outer): the forward's tiling.
+constexpr int kDqBq = 128;
+constexpr int kDqBk = 32;
 
 struct FwdParams {
   const void* Q;
@@ -50,11 +53,16 @@ struct BwdParams {
   int64_t sq[3], sk[3], sv[3], so[3];
   int64_t n;
   int32_t B, H;
-  int32_t tq, tk;  // backward tiling: tq query tiles of kBwdBq, tk key tiles of kBwdBk
+  int32_t tq, tk;  // key-tile-outer tiling: tq query tiles, tk key tiles of kBwdBk
   int64_t total;
   int64_t grid_pad;
   float scale;   // c
   float scale2;  // c * log2(e)
+  // Query-tile-outer dQ kernel (deterministic path): tiles of kDqBq queries.
+  const uint8_t* map_dq;  // bitmask tile map at the dQ tiling, else null
+  int32_t tq_dq;
+  int64_t total_dq;
+  int64_t grid_pad_dq;
 };
 
 struct MapParams {
@@ -70,9 +78,10 @@ struct MapParams {
 
 // Launchers return a hipError_t value as int (0 = success).
 int launch_fwd(const FwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
-int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
+int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, bool fused, void* stream);
+int launch_bwd_dq(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
 int launch_tile_map(const MapParams& p, void* stream);
-int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, void* stream);
+int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, bool clear_dq, void* stream);
 int launch_bwd_post(const BwdParams& p, int bf16, int d, void* stream);
 const char* hip_error_string(int err);
 int hip_last_launch_error();

@@ -93,15 +93,18 @@ typedef struct {
   int64_t sk[3];          /* ... of K and dK */
   int64_t sv[3];          /* ... of V and dV */
   int64_t so[3];          /* ... of O and dO */
-  int32_t deterministic;  /* bwd: must be 0 (fp32 atomic dQ accumulation) */
+  int32_t deterministic;  /* bwd: 0 = dQ by fp32 atomics in the key-tile-outer
+                             kernel; 1 = dQ by a separate query-tile-outer
+                             kernel (bitwise reproducible, no atomics) */
   int32_t reserved;       /* must be 0 */
 } attn_problem;
 
 /* Bytes of device workspace attn_fwd (is_bwd = 0) or attn_bwd (is_bwd = 1)
  * needs for this problem.  Forward: the tile map of bitmask mode (0 bytes
- * otherwise).  Backward: D (4 B H n bytes) + the fp32 dQ accumulator
- * (4 B H n d bytes) + the bitmask tile map; every region 256-byte aligned.
- * Validates the problem like the compute calls. */
+ * otherwise).  Backward: D (4 B H n bytes), plus the fp32 dQ accumulator
+ * (4 B H n d bytes) when deterministic = 0, plus the bitmask tile map(s);
+ * every region 256-byte aligned.  Validates the problem like the compute
+ * calls. */
 attn_status attn_workspace_size(const attn_problem* p, int is_bwd, size_t* bytes);
 
 /* Forward: O [B,H,n,v] (dtype) and L [B,H,n] (fp32, natural-log logsumexp
@@ -112,18 +115,20 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
                      void* stream);
 
 /* Backward: dQ, dK, dV (dtype) from Q, K, V, the forward's O and L, and the
- * upstream gradient dO.  Kernels: D = rowsum(dO o O) with dQ-accumulator
- * clearing, bitmask tile classification (bitmask mode), the key-tile-outer
- * recompute kernel (dK, dV in registers, dQ by fp32 atomics into the
- * workspace), and the dQ conversion.  dQ's run-to-run result may differ in
- * the last bits (atomic order). */
+ * upstream gradient dO.  Kernels: D = rowsum(dO o O) (clearing the dQ
+ * accumulator when deterministic = 0), bitmask tile classification (bitmask
+ * mode), the key-tile-outer recompute kernel (dK, dV in registers), then
+ * either dQ by fp32 atomics in that kernel plus a conversion pass
+ * (deterministic = 0; dQ may differ run to run in the last bits) or a
+ * query-tile-outer dQ kernel (deterministic = 1; bitwise reproducible). */
 attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const void* V,
                      const void* O, const void* dO, const float* L,
                      void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
                      void* stream);
 
-/* Debug: the (query tile x key tile) classification the forward (is_bwd=0)
- * or backward (is_bwd=1) kernels use, 0 = empty (skipped), 1 = partial
+/* Debug: the (query tile x key tile) classification the forward (is_bwd=0),
+ * key-tile-outer backward (is_bwd=1) or query-tile-outer dQ (is_bwd=2)
+ * kernels use, 0 = empty (skipped), 1 = partial
  * (masked inside), 2 = full (no masking), as uint8 [units, tq, tk] with
  * units = 1 for none/causal masks (shared by every head), else the number
  * of distinct masks (H if mask_sb == 0, else B*H, in (b, h) order).
@@ -141,8 +146,9 @@ typedef enum {
   ATTN_KERNEL_FWD = 1,      /* forward */
   ATTN_KERNEL_BWD_PRE = 2,  /* D = rowsum(dO o O), accumulator clearing */
   ATTN_KERNEL_BWD = 3,      /* key-tile-outer backward */
-  ATTN_KERNEL_BWD_POST = 4, /* dQ conversion */
-  ATTN_KERNEL_COUNT = 5
+  ATTN_KERNEL_BWD_POST = 4, /* dQ conversion (deterministic = 0) */
+  ATTN_KERNEL_BWD_DQ = 5,   /* query-tile-outer dQ (deterministic = 1) */
+  ATTN_KERNEL_COUNT = 6
 } attn_kernel;
 
 /* Opt-in kernel timing (off by default; not thread-safe; for measurement

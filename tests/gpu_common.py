@@ -32,7 +32,11 @@ def mask_dev(prob: W.Problem):
 
 
 def run_gpu(prob: W.Problem, want_bwd: bool = True):
-    """Forward and (optionally) backward on the device; results as float64 numpy."""
+    """Forward and backward (both dQ paths) on the device; float64 numpy results.
+
+    Keys dQ/dK/dV come from the atomic path, dQ_det/dK_det/dV_det from the
+    deterministic (query-tile-outer dQ) path.
+    """
     import exact_tiled_attention_attn_amd as E
 
     w = prob.w
@@ -43,6 +47,8 @@ def run_gpu(prob: W.Problem, want_bwd: bool = True):
     if want_bwd:
         dq, dk, dv = E.bwd(q, k, v, o, g, L, w.scale, w.mask, m)
         out.update(dQ=dq, dK=dk, dV=dv)
+        dq, dk, dv = E.bwd(q, k, v, o, g, L, w.scale, w.mask, m, deterministic=True)
+        out.update(dQ_det=dq, dK_det=dk, dV_det=dv)
     torch.cuda.synchronize()
     return {k_: t.float().cpu().numpy().astype(np.float64) for k_, t in out.items()}
 

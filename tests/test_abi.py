@@ -79,6 +79,9 @@ def test_workspace_formula():
             st, bw = wsize(p, 1)
             al = lambda x: (x + 255) // 256 * 256  # noqa: E731
             assert st == 0 and bw == al(4 * B * H * n) + al(4 * B * H * n * d)
+            p.deterministic = 1  # no dQ accumulator
+            st, bw = wsize(p, 1)
+            assert st == 0 and bw == al(4 * B * H * n)
     # bitmask: + tile map (units x tq x tk bytes); forward tiles 128 x 64, backward 64 x 128 (bf16)
     p = problem(2, 8, 8192, 64, 128, 1, 2)
     p.mask = FAKE
@@ -87,6 +90,9 @@ def test_workspace_formula():
     assert st == 0 and fw == (8 * 64 * 128 + 255) // 256 * 256
     st, bw = wsize(p, 1)
     assert bw == 4 * 16 * 8192 + 4 * 16 * 8192 * 64 + 8 * 128 * 64
+    p.deterministic = 1  # D + key-tile-outer map (64 x 128 tiles) + dQ map (128 x 32 tiles)
+    st, bw = wsize(p, 1)
+    assert bw == 4 * 16 * 8192 + 8 * 128 * 64 + 8 * 64 * 256
 
 
 @pytest.mark.parametrize("mut,status", [
@@ -97,7 +103,7 @@ def test_workspace_formula():
     (lambda p: setattr(p, "dtype", 7), 4),
     (lambda p: setattr(p, "mask_mode", 3), 5),
     (lambda p: setattr(p, "mask_mode", 2), 5),  # bitmask without mask
-    (lambda p: setattr(p, "deterministic", 1), 6),
+    (lambda p: setattr(p, "deterministic", 2), 6),
     (lambda p: setattr(p, "reserved", 1), 6),
     (lambda p: setattr(p, "scale", float("inf")), 2),
     (lambda p: setattr(p, "scale", float("nan")), 2),
