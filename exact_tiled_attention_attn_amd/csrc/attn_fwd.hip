@@ -252,10 +252,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       mx = max_halves(mx) * scale2;  // base-2 units; -inf stays -inf (scale2 > 0)
       // Raise the reference max only when it is exceeded by more than the
-      // slack (wave-uniform decision).
-      if (__ballot(mx > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      // slack.  The branch is taken when any lane needs it, but each lane
+      // decides for its own row (others keep m and get alpha = 1 exactly), so
+      // a row's result never depends on the other rows of the wave.
+      const bool raise = mx > m_run + kRescaleSlack;
+      if (__ballot(raise) != 0) {
+        const float m_new = raise ? fmaxf(m_run, mx) : m_run;
+        const float alpha = (!raise || m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
         l_use *= alpha;
 #pragma unroll

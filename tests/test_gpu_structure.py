@@ -1,0 +1,219 @@
+"""Mask/skip structure and edge cases of the HIP path (needs an MI355X).
+
+* the tile classification the kernels use equals the oracle's, bit for bit;
+* a key outside A_i cannot leak into row i: perturbing it leaves O_i, L_i and
+  the deterministic dQ_i bitwise unchanged;
+* keys that no row allows get exactly zero dK, dV;
+* causal row 0 reproduces V_0 bitwise; empty rows are defined;
+* strided layouts give bitwise the same results as contiguous ones;
+* negative and zero scale, and Q = K = V aliasing, against the oracle.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import dense, tilemap
+from tests.gpu_common import DEV, compare, mask_dev, oracle_unit, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _bitmask_problem(n=700, H=2, d=64, v=128, dtype="bf16", seed=5, p=0.2):
+    rng = np.random.default_rng(seed)
+    allowed = rng.random((H, n, n)) < p
+    allowed |= W.window_allowed(n, 64)[None]
+    Q, K, V, G = (rng.standard_normal((1, H, n, x), dtype=np.float32) for x in (d, d, v, v))
+    return W.custom(Q, K, V, G, scale=1 / np.sqrt(d), mask="bitmask", allowed=allowed, dtype=dtype)
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "bitmask"])
+@pytest.mark.parametrize("is_bwd", [0, 1, 2])
+def test_tile_map_matches_oracle(mask, is_bwd):
+    import exact_tiled_attention_attn_amd as E
+
+    if mask == "bitmask":
+        prob = _bitmask_problem(n=1000)
+        # make some tiles fully empty and some fully allowed
+        prob.mask_bool[0, :, 300:500] = False
+        prob.mask_bool[0, np.arange(1000), np.arange(1000)] = True
+        prob.mask_bool[1, 0:256, 0:512] = True
+        prob.mask_words = W.pack_bits(prob.mask_bool)
+    else:
+        rng = np.random.default_rng(6)
+        n = 1000
+        Q, K, V, G = (rng.standard_normal((1, 2, n, 64), dtype=np.float32) for _ in range(4))
+        prob = W.custom(Q, K, V, G, scale=0.125, mask=mask, dtype="bf16")
+    w = prob.w
+    q, k, v = (to_dev(prob, x) for x in "QKV")
+    tmap, bq, bk = E.debug_tile_map(q, k, v, w.scale, w.mask, mask_dev(prob), is_bwd=is_bwd)
+    got = tmap.cpu().numpy()
+    units = got.shape[0]
+    for u in range(units):
+        want = tilemap.tile_map(prob.allowed(u), bq, bk)
+        assert np.array_equal(got[u], want), (mask, is_bwd, u)
+    if mask == "causal":
+        assert np.array_equal(got[0], tilemap.causal_tile_map(w.n, bq, bk))
+    print(mask, is_bwd, "tiles", bq, bk, "nonempty", tilemap.nonempty_tiles(got), flush=True)
+
+
+def _run(prob, deterministic=True):
+    import exact_tiled_attention_attn_amd as E
+
+    w = prob.w
+    q, k, v, g = (to_dev(prob, x) for x in "QKVG")
+    m = mask_dev(prob)
+    o, L = E.fwd(q, k, v, w.scale, w.mask, m)
+    dq, dk, dv = E.bwd(q, k, v, o, g, L, w.scale, w.mask, m, deterministic=deterministic)
+    torch.cuda.synchronize()
+    return [t.cpu() for t in (o, L, dq, dk, dv)]
+
+
+@pytest.mark.parametrize("mask", ["causal", "bitmask"])
+def test_masked_key_perturbation_does_not_leak(mask):
+    if mask == "bitmask":
+        prob = _bitmask_problem(n=700)
+    else:
+        rng = np.random.default_rng(7)
+        n = 700
+        Q, K, V, G = (rng.standard_normal((1, 2, n, 128), dtype=np.float32) for _ in range(4))
+        prob = W.custom(Q, K, V, G, scale=1 / np.sqrt(128), mask="causal", dtype="bf16")
+    base = _run(prob)
+    j = 333
+    K2, V2 = prob.K.copy(), prob.V.copy()
+    rng = np.random.default_rng(8)
+    K2[:, :, j] = 50.0 * rng.standard_normal(K2.shape[-1])
+    V2[:, :, j] = 100.0 * rng.standard_normal(V2.shape[-1])
+    allowed = prob.mask_bool if mask == "bitmask" else None
+    pert = W.custom(prob.Q, K2, V2, prob.G, scale=prob.w.scale, mask=mask, allowed=allowed, dtype="bf16")
+    new = _run(pert)
+    for h in range(prob.w.H):
+        A = prob.allowed(h)
+        out_rows = ~A[:, j]
+        in_rows = A[:, j]
+        assert out_rows.any() and in_rows.any()
+        for idx, name in ((0, "O"), (1, "L"), (2, "dQ")):
+            a, b = base[idx][0, h], new[idx][0, h]
+            assert torch.equal(a[out_rows], b[out_rows]), (mask, h, name)
+        assert not torch.equal(base[0][0, h][in_rows], new[0][0, h][in_rows])
+
+
+def test_unreferenced_keys_get_zero_gradients():
+    prob = _bitmask_problem(n=600)
+    dead = [5, 100, 599]
+    prob.mask_bool[:, :, dead] = False
+    prob.mask_bool[:, np.arange(600), (np.arange(600) + 1) % 600] = True  # keep rows nonempty
+    prob.mask_bool[:, :, dead] = False
+    assert prob.mask_bool.any(axis=2).all()
+    prob.mask_words = W.pack_bits(prob.mask_bool)
+    for det in (True, False):
+        o, L, dq, dk, dv = _run(prob, det)
+        for j in dead:
+            assert torch.all(dk[0, :, j] == 0) and torch.all(dv[0, :, j] == 0), (det, j)
+
+
+def test_causal_row0_is_v0_bitwise():
+    prob = W.generate("bf16_causal_h32_n16384_d128", heads=2, n=300)
+    o, L, *_ = _run(prob)
+    v = to_dev(prob, "V").cpu()
+    assert torch.equal(o[0, :, 0], v[0, :, 0])
+    # L_0 = c <Q_0, K_0>
+    s = prob.w.scale * (prob.Q[0, :, 0].astype(np.float64) * prob.K[0, :, 0]).sum(-1)
+    assert np.abs(L[0, :, 0].numpy() - s).max() < 1e-4 * max(1, np.abs(s).max())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_rows_are_defined(dtype):
+    prob = _bitmask_problem(n=500, dtype=dtype, d=64, v=64)
+    empty = [0, 77, 499]
+    prob.mask_bool[:, empty, :] = False
+    prob.mask_words = W.pack_bits(prob.mask_bool)
+    for det in (True, False):
+        o, L, dq, dk, dv = _run(prob, det)
+        assert torch.all(o[0, :, empty] == 0)
+        assert torch.all(torch.isneginf(L[0, :, empty]))
+        assert torch.all(dq[0, :, empty] == 0)
+        keep = np.setdiff1d(np.arange(500), empty)
+        for h in range(prob.w.H):
+            # Reference: the same problem without the empty rows (they contribute nothing).
+            Q, K, V, G = (getattr(prob, x)[0, h].astype(np.float64) for x in "QKVG")
+            A = prob.mask_bool[h][keep]
+            Y, m, ell, _ = dense.forward(Q[keep], K, V, prob.w.scale, A)
+            from tests.gpu_common import stored
+            from oracle import tiled
+            rdq, rdk, rdv = tiled.reverse(Q[keep], K, V, prob.w.scale, A, 500, stored(Y, dtype), m, ell, G[keep])
+            compare("O", o[0, h][keep].double().numpy(), Y, dtype, ("empty", h))
+            compare("dQ", dq[0, h][keep].double().numpy(), rdq, dtype, ("empty", h, det))
+            compare("dK", dk[0, h].double().numpy(), rdk, dtype, ("empty", h, det))
+            compare("dV", dv[0, h].double().numpy(), rdv, dtype, ("empty", h, det))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strided_layout_matches_contiguous_bitwise(dtype):
+    import exact_tiled_attention_attn_amd as E
+
+    rng = np.random.default_rng(9)
+    B, H, n, d = 2, 3, 333, 128
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    base = [torch.from_numpy(rng.standard_normal((B, n, H, d), dtype=np.float32)).to(DEV).to(tdt)
+            for _ in range(4)]
+    strided = [t.permute(0, 2, 1, 3) for t in base]  # [B, H, n, d] view, row stride H*d
+    contig = [t.contiguous() for t in strided]
+    outs = []
+    for q, k, v, g in (strided, contig):
+        o = torch.empty_like(q)  # preserves the strided layout
+        o, L = E.fwd(q, k, v, 0.1, "causal", out=o)
+        dq, dk, dv = E.bwd(q, k, v, o, g, L, 0.1, "causal", deterministic=True)
+        torch.cuda.synchronize()
+        outs.append([x.contiguous().cpu() for x in (o, L, dq, dk, dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    assert not strided[0].is_contiguous()
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+@pytest.mark.parametrize("mask", ["none", "causal", "bitmask"])
+def test_negative_and_zero_scale(scale, mask):
+    rng = np.random.default_rng(10)
+    n, d = 300, 64
+    Q, K, V, G = (rng.standard_normal((1, 2, n, d), dtype=np.float32) for _ in range(4))
+    allowed = None
+    if mask == "bitmask":
+        allowed = rng.random((2, n, n)) < 0.3
+        allowed[:, np.arange(n), np.arange(n)] = True
+    for dtype in ("f32", "bf16"):
+        prob = W.custom(Q, K, V, G, scale=scale, mask=mask, allowed=allowed, dtype=dtype)
+        got = run_gpu(prob)
+        for h in range(2):
+            ref = oracle_unit(prob, 0, h)
+            for name in ("O", "L", "dQ", "dK", "dV"):
+                if scale == 0.0 and name in ("dQ", "dK"):
+                    assert np.all(got[name][0, h] == 0) and np.all(got[name + "_det"][0, h] == 0)
+                    continue
+                compare(name, got[name][0, h], ref[name], dtype, (scale, mask, dtype, name))
+                if name in ("dQ", "dK", "dV"):
+                    compare(name, got[name + "_det"][0, h], ref[name], dtype, (scale, mask, dtype, name, "det"))
+
+
+def test_self_attention_aliased_inputs():
+    import exact_tiled_attention_attn_amd as E
+
+    rng = np.random.default_rng(11)
+    n, d = 257, 64
+    X = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    G = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    x = torch.from_numpy(X).to(DEV)
+    g = torch.from_numpy(G).to(DEV)
+    o, L = E.fwd(x, x, x, 1.0 / 8, "causal")
+    dq, dk, dv = E.bwd(x, x, x, o, g, L, 1.0 / 8, "causal", deterministic=True)
+    torch.cuda.synchronize()
+    A = W.causal_allowed(n)
+    Y, _, _, Lr = dense.forward(X[0, 0], X[0, 0], X[0, 0], 1 / 8, A)
+    rdq, rdk, rdv = dense.vjp(X[0, 0], X[0, 0], X[0, 0], 1 / 8, A, G[0, 0])
+    compare("O", o[0, 0].cpu().double().numpy(), Y, "f32")
+    compare("L", L[0, 0].cpu().double().numpy(), Lr, "f32")
+    dx = (dq + dk + dv)[0, 0].cpu().double().numpy()
+    compare("dQ", dx, rdq + rdk + rdv, "f32")
