@@ -26,6 +26,41 @@ import numpy as np
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # published dense MFMA peaks
 HEADLINE = "bf16_causal_h32_n16384_d128"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc")
+# Source files each kernel class is built from (a recorded HBM byte count is
+# reported only while these are unchanged).
+KERNEL_SOURCES = {
+    "fwd": ["attn_fwd.hip", "kern_common.h"],
+    "bwd": ["attn_bwd.hip", "kern_common.h"],
+    "bwd_dq": ["attn_bwd_dq.hip", "kern_common.h"],
+    "bwd_pre": ["attn_aux.hip"],
+    "bwd_post": ["attn_aux.hip"],
+    "tile_map": ["attn_aux.hip"],
+}
+
+
+def source_sha(kernel: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, deterministic: int, kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/traffic_*.txt (rocprofv3
+    FETCH_SIZE/WRITE_SIZE scaled by a 1 GiB copy), or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}{'' if deterministic else '_atomic'}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = dict(line.strip().split("=", 1) for line in open(path) if "=" in line)
+    if kv.get(f"{kernel}.source_sha256") != source_sha(kernel):
+        return None
+    b = kv.get(f"{kernel}.bytes")
+    return float(b) if b is not None else None
 
 
 def parse():
@@ -211,7 +246,8 @@ def main():
         "backward_dq_path": "query-tile-outer kernel" if args.deterministic else "fp32 atomics",
         "roofline": {"kernel": dominant, "flops_per_launch": kflops[dominant], "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None},
+                     "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(w.name, args.deterministic, dominant)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_budget_s)
