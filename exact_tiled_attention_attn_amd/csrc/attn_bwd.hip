@@ -57,6 +57,14 @@ struct BwdShape {
   static constexpr int BUF = QTILE + OTILE + BQ * 4 * 2 + BQ * MWORDS * 4;
   static constexpr int QLD = (BQ * QCH + 255) / 256;
   static constexpr int OLD = (BQ * OCH + 255) / 256;
+  // Q and dO tiles go global -> LDS directly (buffer_load ... lds, 1 KiB of
+  // lane-contiguous 16-byte chunks per wave instruction) when their rows are
+  // unpadded and swizzled; each lane then fetches the logical chunk its
+  // physical slot holds.
+  static constexpr int QCPR = DP * ES / 16, OCPR = DVP * ES / 16;
+  static constexpr bool DMA = BF16 && QT::kSwizzle && OT::kSwizzle && QCPR == QCH && OCPR == OCH &&
+                              (BQ * QCPR) % (64 * NW) == 0 && (BQ * OCPR) % (64 * NW) == 0;
+  static constexpr int QDMA = BQ * QCPR / (64 * NW), ODMA = BQ * OCPR / (64 * NW);  // per wave
   static constexpr int smem(bool fused) { return 2 * BUF + (fused ? KTILE + STILE : 0); }
 };
 
@@ -103,6 +111,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
       if (cc * 16 < D * S::ES) x = __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow + cc * 16, 0, 0);
       *reinterpret_cast<u32x4*>(Ks + S::KTl::off(r, cc)) = x;
     }
+  }
+  // Direct-to-LDS staging: start from zeroed buffers, so rows the range
+  // check drops never hold stale non-finite patterns.
+  if constexpr (S::DMA) {
+    for (int c = tid; c < 2 * S::BUF / 16; c += 256) reinterpret_cast<u32x4*>(bufs)[c] = u32x4{0, 0, 0, 0};
+    __syncthreads();  // cleared before any wave's direct loads land
   }
   // Clear the padded columns of both Q / dO buffers once.
   if constexpr (S::DP != D || S::DVP != DV) {
@@ -171,18 +185,36 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   u32x4 qreg[S::QLD], oreg[S::OLD];
   float lreg = 0.f, dreg = 0.f;
   uint32_t mreg = 0;
-  auto gload = [&](int qt) {
+  auto gload = [&](int qt, int bi) {
     const int q0 = qt * S::BQ;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb + (int64_t)q0 * qrow, (n - q0) * qrow);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb + (int64_t)q0 * orow, (n - q0) * orow);
+    if constexpr (S::DMA) {
+      char* Qs = bufs + bi * S::BUF;
+      char* Os = Qs + S::QTILE;
 #pragma unroll
-    for (int i = 0; i < S::QLD; ++i) {
+      for (int j = 0; j < S::QDMA; ++j) {
+        const int inst = w * S::QDMA + j, idx = inst * 64 + lane;
+        const int r = idx / S::QCPR, c = S::QT::chunk(r, idx % S::QCPR);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(Qs + inst * 1024), 16,
+                                                 r * qrow + c * 16, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < S::ODMA; ++j) {
+        const int inst = w * S::ODMA + j, idx = inst * 64 + lane;
+        const int r = idx / S::OCPR, c = S::OT::chunk(r, idx % S::OCPR);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(Os + inst * 1024), 16,
+                                                 r * orow + c * 16, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S::QLD * !S::DMA; ++i) {
       const int c = tid + i * 256;
       if (S::BQ * S::QCH % 256 == 0 || c < S::BQ * S::QCH)
         qreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, (c / S::QCH) * qrow + (c % S::QCH) * 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < S::OLD; ++i) {
+    for (int i = 0; i < S::OLD * !S::DMA; ++i) {
       const int c = tid + i * 256;
       if (S::BQ * S::OCH % 256 == 0 || c < S::BQ * S::OCH)
         oreg[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (c / S::OCH) * orow + (c % S::OCH) * 16, 0, 0);
@@ -210,13 +242,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     float* Dsv = Ls + S::BQ;
     uint32_t* Ms = reinterpret_cast<uint32_t*>(Dsv + S::BQ);
 #pragma unroll
-    for (int i = 0; i < S::QLD; ++i) {
+    for (int i = 0; i < S::QLD * !S::DMA; ++i) {
       const int c = tid + i * 256;
       if (S::BQ * S::QCH % 256 == 0 || c < S::BQ * S::QCH)
         *reinterpret_cast<u32x4*>(Qs + S::QT::off(c / S::QCH, c % S::QCH)) = qreg[i];
     }
 #pragma unroll
-    for (int i = 0; i < S::OLD; ++i) {
+    for (int i = 0; i < S::OLD * !S::DMA; ++i) {
       const int c = tid + i * 256;
       if (S::BQ * S::OCH % 256 == 0 || c < S::BQ * S::OCH)
         *reinterpret_cast<u32x4*>(Os + S::OT::off(c / S::OCH, c % S::OCH)) = oreg[i];
@@ -237,16 +269,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   if (MASK == kMaskBitmask && qt >= qt_first && tile_class(qt) == kTileEmpty) qt = next_tile(qt);
   if (qt < qt_first) qt = -1;
   if (qt >= 0) {
-    gload(qt);
+    gload(qt, 0);
     lstore(0);
   }
+  if constexpr (S::DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct loads landed
   __syncthreads();
   int buf = 0;
 
   while (qt >= 0) {
     const int nq = next_tile(qt);
     const uint8_t cls = tile_class(qt);
-    if (nq >= 0) gload(nq);
+    if (nq >= 0) gload(nq, buf ^ 1);
     const int q0 = qt * S::BQ;
     const char* Qs = bufs + buf * S::BUF;
     const char* Os = Qs + S::QTILE;
@@ -406,6 +439,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     }
 
     if (nq >= 0) lstore(buf ^ 1);
+    if constexpr (S::DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     buf ^= 1;
     qt = nq;

@@ -349,10 +349,350 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined bf16 forward (d, v in {64, 128}).
+//
+// Same tiling, state and arithmetic as fwd_kernel, scheduled differently:
+// the scores of key tile j+1 are formed on the matrix cores while the
+// vector ALUs run the softmax of tile j, and the instruction scheduler is
+// told to interleave the two streams (one MFMA, one LDS read, a run of VALU
+// work).  K and V tiles go from HBM straight into their swizzled LDS slots
+// (buffer_load ... lds), so no registers are spent on staging; K and V have
+// two buffers each: K_{j+2} and V_{j+1} stream in while tile j is consumed.
+// ---------------------------------------------------------------------------
+template <int D, int DV>
+struct FwdPipeShape {
+  static constexpr int BQ = kFwdBq, BK = kFwdBk, NW = 4;
+  static constexpr int NQF = D / 16;   // Q fragments per lane (16 dims each)
+  static constexpr int NVB = DV / 32;  // 32-column blocks of the output
+  static constexpr int NKB = BK / 32;  // 32-key blocks of a tile
+  using KT = Swz<D / 8>;
+  using VT = Swz<DV / 8>;
+  static constexpr int KTILE = BK * KT::kStride, VTILE = BK * VT::kStride;
+  static constexpr int KWIN = KTILE / 1024 / NW, VWIN = VTILE / 1024 / NW;  // 1 KB fills per wave
+  static constexpr int SMEM = 2 * KTILE + 2 * VTILE;
+  static_assert(KTILE % (1024 * NW) == 0 && VTILE % (1024 * NW) == 0, "tile fills");
+};
+
+template <int D, int DV, int MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pipe_kernel(FwdParams p) {
+  using S = FwdPipeShape<D, DV>;
+  // Four distinct LDS objects, so that the compiler can tell reads of one
+  // buffer from the direct fills in flight into another (no false waits).
+  __shared__ __attribute__((aligned(1024))) char kbuf0[S::KTILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[S::KTILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[S::VTILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[S::VTILE];
+
+  const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad, p.total);
+  if (logical < 0) return;
+  const int unit = (int)(logical / p.tq);
+  const int qt = p.tq - 1 - (int)(logical % p.tq);  // heaviest causal tiles first
+  const int b = unit / p.H, h = unit % p.H;
+  const int n = (int)p.n;
+  const int q0 = qt * S::BQ;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int hh = lane >> 5;
+  const int g1 = (lane >> 4) & 1;
+  const int q = q0 + 32 * w + (lane & 31);
+  const bool qvalid = q < n;
+
+  const int qrow = (int)p.sq[2] * 2, krow = (int)p.sk[2] * 2, vrow = (int)p.sv[2] * 2;
+  const char* Qb = (const char*)p.Q + ((int64_t)b * p.sq[0] + (int64_t)h * p.sq[1]) * 2;
+  const char* Kb = (const char*)p.K + ((int64_t)b * p.sk[0] + (int64_t)h * p.sk[1]) * 2;
+  const char* Vb = (const char*)p.V + ((int64_t)b * p.sv[0] + (int64_t)h * p.sv[1]) * 2;
+
+  // Q fragments as the B operand of S^T = K Q^T (negated rows for c < 0;
+  // |c| log2 e clamped to >= 1e-30, as in fwd_kernel).
+  const bool neg = p.scale2 < 0.f;
+  const float scale2 = fmaxf(fabsf(p.scale2), 1e-30f);
+  bf16x8 qf[S::NQF];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, n * qrow);
+    const int qoff = q * qrow;
+#pragma unroll
+    for (int ks = 0; ks < S::NQF; ++ks) {
+      u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + (16 * ks + 8 * hh) * 2, 0, 0);
+      if (neg) x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  int kt_end = p.tk;
+  if constexpr (MASK == kMaskCausal) {
+    const int q_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1;
+    kt_end = q_hi / S::BK + 1;
+  }
+  const uint8_t* map_row = nullptr;
+  const uint32_t* mrow = nullptr;
+  if constexpr (MASK == kMaskBitmask) {
+    const int64_t mu = p.mask_sb == 0 ? h : unit;
+    map_row = p.map + (mu * p.tq + qt) * (int64_t)p.tk;
+    mrow = p.mask + b * p.mask_sb + h * p.mask_sh + (int64_t)(qvalid ? q : 0) * p.mask_si;
+  }
+  auto tile_class = [&](int kt) -> uint8_t {
+    if constexpr (MASK == kMaskBitmask) return map_row[kt];
+    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n);
+  };
+  auto next_tile = [&](int kt) -> int {
+    if constexpr (MASK != kMaskBitmask) return kt + 1;
+    for (int k = kt + 1; k < kt_end; ++k)
+      if (tile_class(k) != kTileEmpty) return k;
+    return kt_end;
+  };
+
+  // Per-lane source offsets of this wave's 1 KB fill windows (fixed per tile).
+  int koff[S::KWIN], voff[S::VWIN];
+#pragma unroll
+  for (int i = 0; i < S::KWIN; ++i) koff[i] = S::KT::dma_src(w * S::KWIN + i, lane, krow);
+#pragma unroll
+  for (int i = 0; i < S::VWIN; ++i) voff[i] = S::VT::dma_src(w * S::VWIN + i, lane, vrow);
+  auto fill_k = [&](int kt, char* buf) {
+    const int k0 = kt * S::BK;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (n - k0) * krow);
+    char* dst = buf + w * S::KWIN * 1024;
+#pragma unroll
+    for (int i = 0; i < S::KWIN; ++i) dma16(r, dst + i * 1024, koff[i]);
+  };
+  auto fill_v = [&](int kt, char* buf) {
+    const int k0 = kt * S::BK;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + (int64_t)k0 * vrow, (n - k0) * vrow);
+    char* dst = buf + w * S::VWIN * 1024;
+#pragma unroll
+    for (int i = 0; i < S::VWIN; ++i) dma16(r, dst + i * 1024, voff[i]);
+  };
+
+  // V rows past n are multiplied by zero weights: clear both V buffers once
+  // so that they never hold non-finite bit patterns.
+  for (int c = tid; c < S::VTILE / 16; c += 256) {
+    reinterpret_cast<u32x4*>(vbuf0)[c] = u32x4{0, 0, 0, 0};
+    reinterpret_cast<u32x4*>(vbuf1)[c] = u32x4{0, 0, 0, 0};
+  }
+
+  float m_run = -INFINITY, l_run = 0.f, l_use = 0.f;
+  f32x16 o[S::NVB];
+#pragma unroll
+  for (int vb = 0; vb < S::NVB; ++vb) o[vb] = f32x16{};
+
+  // S^T (this wave's 32 queries x 64 keys) of the K tile in `kb_s`.
+  auto scores = [&](f32x16 (&sc)[S::NKB], const char* ks_s) {
+#pragma unroll
+    for (int kb = 0; kb < S::NKB; ++kb) sc[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < S::NQF; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < S::NKB; ++kb)
+        sc[kb] = mfma_bf16(lds_read_b128(ks_s, S::KT::off(32 * kb + (lane & 31), 2 * ks + hh)), qf[ks], sc[kb]);
+  };
+
+  // Masking of a partially allowed tile's scores (rows past n, causal, bitmask).
+  auto mask_tile = [&](f32x16 (&sc)[S::NKB], int kt) {
+    const int k0 = kt * S::BK;
+#pragma unroll
+    for (int kb = 0; kb < S::NKB; ++kb) {
+      uint32_t word = 0xFFFFFFFFu;
+      if constexpr (MASK == kMaskBitmask) {
+        if (qvalid && k0 + 32 * kb < n) word = mrow[(k0 + 32 * kb) >> 5];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int key = k0 + kk;
+        bool ok = key < n;
+        if constexpr (MASK == kMaskCausal) ok = ok && key <= q;
+        if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> (kk & 31)) & 1u);
+        sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
+      }
+    }
+  };
+  // Row max of a tile (base-2 units) and the lazy-rescale decision it implies:
+  // the reference max is raised only when exceeded by more than the slack;
+  // each lane decides for its own row.
+  float m_new = -INFINITY, alpha = 1.f;
+  bool raise = false;
+  auto row_max = [&](const f32x16 (&sc)[S::NKB]) {
+    float mx4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16& c = sc[i / 2];
+      const int r0 = 8 * (i % 2);
+      mx4[i] = fmaxf(fmaxf(fmaxf(c[r0], c[r0 + 1]), fmaxf(c[r0 + 2], c[r0 + 3])),
+                     fmaxf(fmaxf(c[r0 + 4], c[r0 + 5]), fmaxf(c[r0 + 6], c[r0 + 7])));
+    }
+    const float mx = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * scale2;
+    raise = mx > m_run + kRescaleSlack;
+    m_new = raise ? fmaxf(m_run, mx) : m_run;
+    alpha = (!raise || m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+  };
+  // Apply a rescale decision to the running state (before the tile's weights
+  // are accumulated).
+  auto apply_rescale = [&]() {
+    if (__ballot(raise) != 0) {
+#pragma unroll
+      for (int vb = 0; vb < S::NVB; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[vb][r] *= alpha;
+    }
+    l_run *= alpha;
+    l_use *= alpha;
+    m_run = m_new;
+  };
+
+  int t0 = 0;
+  if (MASK == kMaskBitmask && t0 < kt_end && tile_class(t0) == kTileEmpty) t0 = next_tile(t0);
+  __syncthreads();  // V buffers cleared
+  if (t0 < kt_end) {  // workgroup-uniform
+    int t1 = next_tile(t0);
+    fill_k(t0, kbuf0);
+    fill_v(t0, vbuf0);
+    if (t1 < kt_end) fill_k(t1, kbuf1);
+    wait_vm();
+    __syncthreads();
+    f32x16 sa[S::NKB], sb[S::NKB];
+    scores(sa, kbuf0);
+    if (tile_class(t0) == kTilePartial) mask_tile(sa, t0);
+    row_max(sa);
+    apply_rescale();
+    __syncthreads();  // K buffer 0 free for tile t2
+
+    // One pipeline step.  On entry cur holds the masked S^T of tile t0 and
+    // the running state is already referenced to t0's max; nxt receives S^T
+    // of tile t1 from knxt.  One scheduling region:
+    //   MFMA S^T(t1)             || VALU exp / pack / sums of t0
+    //   MFMA O^T += V^T P^T(t0)  || VALU row max of t1
+    auto step = [&](f32x16 (&cur)[S::NKB], f32x16 (&nxt)[S::NKB], char* kcur, char* knxt, char* vcur,
+                    char* vnxt) {
+      const int t2 = t1 < kt_end ? next_tile(t1) : kt_end;
+      if (t2 < kt_end) fill_k(t2, kcur);
+      if (t1 < kt_end) fill_v(t1, vnxt);
+
+      // The instruction order below is the schedule: each micro-step is one
+      // MFMA, the LDS reads for a later MFMA, and a slice of VALU work, kept
+      // apart by scheduling barriers.
+      constexpr int NS = S::NQF * S::NKB;      // score MFMAs
+      constexpr int NP = S::NVB * S::BK / 16;  // PV MFMAs
+      constexpr int PF = 4;                    // K reads in flight
+      constexpr int NPAIR = S::NKB * 8;        // weight pairs of the tile
+      auto kread = [&](int i) {  // K fragment of score MFMA i (ks = i / NKB, kb = i % NKB)
+        return lds_read_b128(knxt, S::KT::off(32 * (i % S::NKB) + (lane & 31), 2 * (i / S::NKB) + hh));
+      };
+      auto vread = [&](int i, int half) {  // V^T fragment half of PV MFMA i (ks = i / NVB, vb = i % NVB)
+        const int ks = i / S::NVB, vb = i % S::NVB;
+        return lds_read_tr(vcur, S::VT::tr(lane, 16 * ks + 8 * half + 4 * hh, vb * 32 + 16 * g1));
+      };
+
+      // ---- phase A: S^T(t1) on the MFMA pipe, weights of t0 on the VALU ----
+      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+      u32x4 pk[S::NKB][2];
+      float ls[4] = {0.f, 0.f, 0.f, 0.f}, lu[2] = {0.f, 0.f};
+      auto weights = [&](int pr) {  // pair pr: registers 2 (pr % 8), +1 of block pr / 8
+        const int kb = pr / 8, r = 2 * (pr % 8);
+        const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], scale2, neg_m));
+        const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], scale2, neg_m));
+        ls[pr % 4] += p0 + p1;
+        const uint32_t u = pack_bf16x2(p0, p1);
+        pk[kb][r / 8][(r / 2) % 4] = u;
+        lu[pr % 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), ones_bf16x2(), lu[pr % 2], false);
+      };
+      bf16x8 kfr[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) kfr[i] = kread(i);
+#pragma unroll
+      for (int kb = 0; kb < S::NKB; ++kb) nxt[kb] = f32x16{};
+      i16x4 vfr[4];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        nxt[i % S::NKB] = mfma_bf16(kfr[i % PF], qf[i / S::NKB], nxt[i % S::NKB]);
+        if (i + PF < NS) kfr[i % PF] = kread(i + PF);
+        if (i == NS - 1) {  // first PV operands
+          vfr[0] = vread(0, 0);
+          vfr[1] = vread(0, 1);
+          vfr[2] = vread(1, 0);
+          vfr[3] = vread(1, 1);
+        }
+#pragma unroll
+        for (int pr = i * NPAIR / NS; pr < (i + 1) * NPAIR / NS; ++pr) weights(pr);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      l_use += lu[0] + lu[1];
+
+      // ---- phase B: O^T += V^T P^T(t0) on the MFMA pipe, row max of t1 ----
+      // Max tree over the 32 scores of t1: node 32 + k = max(node 2k, node 2k + 1).
+      float tree[63];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        tree[r] = nxt[0][r];
+        tree[16 + r] = nxt[1][r];
+      }
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[(i / S::NVB) / 2][(i / S::NVB) % 2]);
+        o[i % S::NVB] = mfma_bf16(join_tr(vfr[2 * (i % 2)], vfr[2 * (i % 2) + 1]), pb, o[i % S::NVB]);
+        if (i + 2 < NP) {
+          vfr[2 * (i % 2)] = vread(i + 2, 0);
+          vfr[2 * (i % 2) + 1] = vread(i + 2, 1);
+        }
+#pragma unroll
+        for (int k = i * 31 / NP; k < (i + 1) * 31 / NP; ++k) tree[32 + k] = fmaxf(tree[2 * k], tree[2 * k + 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (t1 < kt_end) {  // else nxt holds scores of stale LDS contents: unused
+        const float mx = max_halves(tree[62]) * scale2;
+        raise = mx > m_run + kRescaleSlack;
+        m_new = raise ? fmaxf(m_run, mx) : m_run;
+        alpha = (!raise || m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        if (tile_class(t1) == kTilePartial) {
+          mask_tile(nxt, t1);
+          row_max(nxt);
+        }
+        apply_rescale();
+      }
+      wait_vm();
+      __syncthreads();
+      t0 = t1;
+      t1 = t2;
+    };
+    while (true) {
+      step(sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
+      if (t0 >= kt_end) break;
+      step(sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
+      if (t0 >= kt_end) break;
+    }
+  }
+
+  const float l_tot = sum_halves(l_run);
+  const float l_norm = sum_halves(l_use);
+  const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
+  if (qvalid) {
+    const int64_t obase = (int64_t)b * p.so[0] + (int64_t)h * p.so[1] + (int64_t)q * p.so[2];
+#pragma unroll
+    for (int vb = 0; vb < S::NVB; ++vb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int vd = vb * 32 + 8 * g + 4 * hh;
+        const u32x2 pk2{pack_bf16x2(o[vb][4 * g] * inv, o[vb][4 * g + 1] * inv),
+                        pack_bf16x2(o[vb][4 * g + 2] * inv, o[vb][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>((char*)p.O + (obase + vd) * 2) = pk2;
+      }
+    if (hh == 0) {
+      const float Lv = (m_run == -INFINITY || l_tot <= 0.f) ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+      p.L[(int64_t)unit * n + q] = Lv;
+    }
+  }
+}
+
 template <bool BF16, int D, int DV, int MASK>
 static int launch_one(const FwdParams& p, hipStream_t st) {
   dim3 grid((unsigned)p.grid_pad), block(256);
-  hipLaunchKernelGGL((fwd_kernel<BF16, D, DV, MASK>), grid, block, 0, st, p);
+  if constexpr (BF16 && (D == 64 || D == 128) && (DV == 64 || DV == 128))
+    hipLaunchKernelGGL((fwd_pipe_kernel<D, DV, MASK>), grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<BF16, D, DV, MASK>), grid, block, 0, st, p);
   return (int)hipGetLastError();
 }
 

@@ -153,7 +153,29 @@ struct Swz {
     const int i = lane & 15;
     return off(k0 + (i >> 2), (n0 >> 3) + ((i & 3) >> 1)) + 8 * (i & 1);
   }
+  // Direct-to-LDS fills (swizzled widths only) write 1 KB windows lane by
+  // lane: lane l of window `win` fills physical chunk l % CPR of row
+  // win * (64 / CPR) + l / CPR, which holds logical chunk chunk(row, l % CPR)
+  // (the XOR is its own inverse).  Returns the source byte offset of that
+  // chunk in a row-major tile with `row_bytes` bytes per row.
+  static __device__ __forceinline__ int dma_src(int win, int lane, int row_bytes) {
+    static_assert(kSwizzle && 1024 % kStride == 0, "direct fills need unpadded rows");
+    const int r = win * (64 / CPR) + lane / CPR;
+    return r * row_bytes + chunk(r, lane % CPR) * 16;
+  }
 };
+
+// Direct global -> LDS copy: the lanes' 16-byte chunks, read at their own
+// byte offsets `voff` of buffer `r`, land lane-contiguously at lds[16 lane]
+// (1 KB per wave).  Completion is tracked by vmcnt: wait_vm() before the
+// barrier that publishes the data.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+enum : int { kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200 };
 
 // Pack 8 fp32 accumulator values (registers r0..r0+7 of a 32x32 C block)
 // as a bf16x8 MFMA operand, RNE.
