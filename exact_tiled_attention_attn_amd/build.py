@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libattn.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_aux.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_dq.hip", "attn_aux.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",
@@ -30,18 +30,21 @@ DEVICE = [
     "--offload-arch=gfx950",
     # Never emit packed fp32 VALU ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # Keep MFMA sources and accumulators in VGPRs: with AGPR-form MFMAs the
-    # backward's loop-carried dK/dV accumulators were copied between AGPRs
-    # and VGPRs every iteration.
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+# Keep MFMA sources and accumulators in VGPRs (files whose kernels fit in 256
+# VGPRs: with AGPR-form MFMAs their loop-carried accumulators were copied
+# between AGPRs and VGPRs every iteration).  The pipelined dK / dV kernel
+# needs more than 256 registers and keeps its dK / dV accumulators in AGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+AGPR_FORM_SOURCES = {"attn_bwd_kv.hip"}
 
 
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
+        form = [] if src in AGPR_FORM_SOURCES else VGPR_FORM
+        cmd = [HIPCC, "-x", "hip", *DEVICE, *form, *COMMON, "-c", path, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-Wall", "-Wextra", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

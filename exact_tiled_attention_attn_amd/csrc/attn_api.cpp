@@ -45,6 +45,8 @@ Tiles bwd_tiles(const attn_problem& p) {
   return Tiles{bq, eta::kBwdBk, cdiv(p.n, bq), cdiv(p.n, eta::kBwdBk)};
 }
 
+int64_t row_pad(int64_t n) { return cdiv(n, eta::kRowPad) * eta::kRowPad; }
+
 int64_t mask_units(const attn_problem& p) { return p.mask_sb == 0 ? p.H : p.B * p.H; }
 
 Tiles dq_tiles(const attn_problem& p) {
@@ -53,12 +55,13 @@ Tiles dq_tiles(const attn_problem& p) {
 
 struct Layout {
   size_t total = 0;
-  size_t off_D = 0, off_dQ = 0, off_map = 0, off_map_dq = 0;
+  size_t off_D = 0, off_L2 = 0, off_dQ = 0, off_map = 0, off_map_dq = 0;
   size_t map_bytes = 0, map_dq_bytes = 0, dq_bytes = 0;
 };
 
-// Backward workspace: D (fp32 [B,H,n]); the atomic path adds the fp32 dQ
-// accumulator, the deterministic path the bitmask map at the dQ tiling.
+// Backward workspace: D and L log2(e) (fp32 [B,H,n_pad] each, n_pad = n
+// rounded up to kRowPad); the atomic path adds the fp32 dQ accumulator, the
+// deterministic path the bitmask map at the dQ tiling.
 Layout plan(const attn_problem& p, int is_bwd) {
   Layout l;
   const int64_t units = p.B * p.H;
@@ -66,8 +69,10 @@ Layout plan(const attn_problem& p, int is_bwd) {
   if (is_bwd) {
     const Tiles t = bwd_tiles(p), tq = dq_tiles(p);
     const bool det = p.deterministic != 0;
+    const size_t rows = size_t(units) * size_t(row_pad(p.n));
     l.off_D = 0;
-    l.off_dQ = align_up(size_t(4) * units * p.n);
+    l.off_L2 = align_up(size_t(4) * rows);
+    l.off_dQ = l.off_L2 + align_up(size_t(4) * rows);
     l.dq_bytes = det ? 0 : size_t(4) * units * p.n * p.d;
     l.off_map = l.off_dQ + align_up(l.dq_bytes);
     l.map_bytes = bitmask ? size_t(mask_units(p) * t.tq * t.tk) : 0;
@@ -343,6 +348,8 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.dO = dO;
   b.L = L;
   b.Dv = reinterpret_cast<float*>(wsb + lay.off_D);
+  b.L2 = reinterpret_cast<float*>(wsb + lay.off_L2);
+  b.n_pad = row_pad(p->n);
   b.dQacc = lay.dq_bytes ? reinterpret_cast<float*>(wsb + lay.off_dQ) : nullptr;
   b.dQ = dQ;
   b.dK = dK;

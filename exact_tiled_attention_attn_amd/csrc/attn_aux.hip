@@ -7,7 +7,8 @@
 //   page, part 3).  Integer OR/AND over the mask words: HBM-bound.
 // * bwd_pre_kernel: D_i = <dO_i, O_i> in fp32 (HarshvardhanJ README,
 //   backward section: D costs O(n d) and replaces a pass over P; ob1 page,
-//   part 2) and, on the atomic path, clears the fp32 dQ accumulator.
+//   part 2), L_i log2(e) for the base-2 exponentials of the backward, and,
+//   on the atomic path, clears the fp32 dQ accumulator.
 // * bwd_post_kernel: dQ = c * accumulator, converted to the output type.
 #include "../../include/attn.h"
 #include "attn_internal.h"
@@ -68,12 +69,12 @@ template <bool BF16, int DV>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_n4) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int VCH = DV * ES / 16;  // 16-byte chunks per row
-  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  const int64_t rows = (int64_t)p.B * p.H * p.n_pad;
   const int64_t row = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
   const int sub = threadIdx.x % 16;
+  const int64_t unit = row / p.n_pad, i = row % p.n_pad;
   float acc = 0.f;
-  if (row < rows) {
-    const int64_t unit = row / p.n, i = row % p.n;
+  if (row < rows && i < p.n) {
     const int64_t b = unit / p.H, h = unit % p.H;
     const int64_t off = (b * p.so[0] + h * p.so[1] + i * p.so[2]) * ES;
     const char* Op = (const char*)p.O + off;
@@ -97,7 +98,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
-  if (row < rows && sub == 0) p.Dv[row] = acc;
+  if (row < rows && sub == 0) {
+    // Padding rows (i >= n): D = 0 and L2 = +inf, i.e. zero weights.
+    float l2 = INFINITY;
+    if (i < p.n) {
+      const float Lv = p.L[unit * p.n + i];
+      l2 = Lv == -INFINITY ? INFINITY : Lv * kLog2e;
+    }
+    p.Dv[row] = acc;
+    p.L2[row] = l2;
+  }
   // Clear the dQ accumulator (grid-stride over float4s).
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < zero_n4; k += stride)
@@ -105,9 +115,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_
 }
 
 int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, bool clear_dq, void* stream) {
-  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  const int64_t rows = (int64_t)p.B * p.H * p.n_pad;
   const int64_t blocks = (rows + 15) / 16;
-  const int64_t zero_n4 = clear_dq ? rows * d / 4 : 0;
+  const int64_t zero_n4 = clear_dq ? (int64_t)p.B * p.H * p.n * d / 4 : 0;
   hipStream_t st = (hipStream_t)stream;
   dim3 g((unsigned)blocks), b(256);
 #define ETA_PRE(BF, DVV) hipLaunchKernelGGL((bwd_pre_kernel<BF, DVV>), g, b, 0, st, p, zero_n4)

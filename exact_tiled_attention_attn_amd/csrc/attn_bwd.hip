@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const char* Vb = (const char*)p.V + ((int64_t)b * p.sv[0] + (int64_t)h * p.sv[1]) * S::ES;
   const char* dOb = (const char*)p.dO + ((int64_t)b * p.so[0] + (int64_t)h * p.so[1]) * S::ES;
   const float* Lb = p.L + (int64_t)unit * n;
-  const float* Db = p.Dv + (int64_t)unit * n;
+  const float* Db = p.Dv + (int64_t)unit * p.n_pad;
 
   if constexpr (FUSED) {
     // Resident K tile in LDS (B operand of dQ), padded columns cleared.
@@ -508,6 +508,7 @@ static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, bool fus
 }
 
 int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, bool fused, void* stream) {
+  if (!fused && bwd_kv_supported(bf16, d, v, mask_mode, p.tq)) return launch_bwd_kv(p, d, v, mask_mode, stream);
   hipStream_t st = (hipStream_t)stream;
   return bf16 ? launch_dims<true>(p, d, v, mask_mode, fused, st)
               : launch_dims<false>(p, d, v, mask_mode, fused, st);

@@ -354,11 +354,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //
 // Same tiling, state and arithmetic as fwd_kernel, scheduled differently:
 // the scores of key tile j+1 are formed on the matrix cores while the
-// vector ALUs run the softmax of tile j, and the instruction scheduler is
-// told to interleave the two streams (one MFMA, one LDS read, a run of VALU
-// work).  K and V tiles go from HBM straight into their swizzled LDS slots
-// (buffer_load ... lds), so no registers are spent on staging; K and V have
-// two buffers each: K_{j+2} and V_{j+1} stream in while tile j is consumed.
+// vector ALUs run the softmax of tile j, and the PV product of tile j runs
+// beside the row max of tile j+1; the instruction order is pinned (one MFMA,
+// its LDS reads issued ahead, a slice of VALU work).  K and V tiles go from
+// HBM straight into padded LDS rows (buffer_load ... lds), so no registers
+// are spent on staging and every LDS read address is a per-lane base plus a
+// constant; K and V have two buffers each: K_{j+2} and V_{j+1} stream in
+// while tile j is consumed.
 // ---------------------------------------------------------------------------
 template <int D, int DV>
 struct FwdPipeShape {
@@ -366,12 +368,13 @@ struct FwdPipeShape {
   static constexpr int NQF = D / 16;   // Q fragments per lane (16 dims each)
   static constexpr int NVB = DV / 32;  // 32-column blocks of the output
   static constexpr int NKB = BK / 32;  // 32-key blocks of a tile
-  using KT = Swz<D / 8>;
-  using VT = Swz<DV / 8>;
-  static constexpr int KTILE = BK * KT::kStride, VTILE = BK * VT::kStride;
-  static constexpr int KWIN = KTILE / 1024 / NW, VWIN = VTILE / 1024 / NW;  // 1 KB fills per wave
-  static constexpr int SMEM = 2 * KTILE + 2 * VTILE;
-  static_assert(KTILE % (1024 * NW) == 0 && VTILE % (1024 * NW) == 0, "tile fills");
+  using KT = PadTile<D * 2, 16>;   // b128 row reads
+  using VT = PadTile<DV * 2, 64>;  // transposed reads
+  static constexpr int KS = KT::kStride, VS = VT::kStride;
+  static constexpr int KTILE = BK * KS, VTILE = BK * VS;
+  static constexpr int KWINS = KTILE / 1024, VWINS = VTILE / 1024;  // 1 KB fill windows per tile
+  static constexpr int KWIN = (KWINS + NW - 1) / NW, VWIN = (VWINS + NW - 1) / NW;  // per wave (max)
+  static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "whole fill windows");
 };
 
 template <int D, int DV, int MASK>
@@ -443,26 +446,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return kt_end;
   };
 
-  // Per-lane source offsets of this wave's 1 KB fill windows (fixed per tile).
+  // Per-lane source offsets of this wave's 1 KB fill windows w, w + 4, ...
+  // (fixed per tile).
   int koff[S::KWIN], voff[S::VWIN];
 #pragma unroll
-  for (int i = 0; i < S::KWIN; ++i) koff[i] = S::KT::dma_src(w * S::KWIN + i, lane, krow);
+  for (int i = 0; i < S::KWIN; ++i) koff[i] = S::KT::fill_src((w + S::NW * i) * 1024 + 16 * lane, krow);
 #pragma unroll
-  for (int i = 0; i < S::VWIN; ++i) voff[i] = S::VT::dma_src(w * S::VWIN + i, lane, vrow);
+  for (int i = 0; i < S::VWIN; ++i) voff[i] = S::VT::fill_src((w + S::NW * i) * 1024 + 16 * lane, vrow);
   auto fill_k = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (n - k0) * krow);
-    char* dst = buf + w * S::KWIN * 1024;
 #pragma unroll
-    for (int i = 0; i < S::KWIN; ++i) dma16(r, dst + i * 1024, koff[i]);
+    for (int i = 0; i < S::KWIN; ++i)
+      if (S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS) dma16(r, buf + (w + S::NW * i) * 1024, koff[i]);
   };
   auto fill_v = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + (int64_t)k0 * vrow, (n - k0) * vrow);
-    char* dst = buf + w * S::VWIN * 1024;
 #pragma unroll
-    for (int i = 0; i < S::VWIN; ++i) dma16(r, dst + i * 1024, voff[i]);
+    for (int i = 0; i < S::VWIN; ++i)
+      if (S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS) dma16(r, buf + (w + S::NW * i) * 1024, voff[i]);
   };
+  // Read bases: K row (lane % 32), chunk hh; V^T slice rows 4 hh + i / 4,
+  // columns 16 g1 + 4 (i % 4) of a 16-lane group's transposed read.
+  const int kbase = (lane & 31) * S::KS + 16 * hh;
+  const int vbase = (4 * hh + ((lane & 15) >> 2)) * S::VS + (16 * g1 + 4 * (lane & 3)) * 2;
 
   // V rows past n are multiplied by zero weights: clear both V buffers once
   // so that they never hold non-finite bit patterns.
@@ -484,7 +492,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < S::NQF; ++ks)
 #pragma unroll
       for (int kb = 0; kb < S::NKB; ++kb)
-        sc[kb] = mfma_bf16(lds_read_b128(ks_s, S::KT::off(32 * kb + (lane & 31), 2 * ks + hh)), qf[ks], sc[kb]);
+        sc[kb] = mfma_bf16(lds_read_b128(ks_s, kbase + 32 * kb * S::KS + 32 * ks), qf[ks], sc[kb]);
   };
 
   // Masking of a partially allowed tile's scores (rows past n, causal, bitmask).
@@ -576,11 +584,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       constexpr int PF = 4;                    // K reads in flight
       constexpr int NPAIR = S::NKB * 8;        // weight pairs of the tile
       auto kread = [&](int i) {  // K fragment of score MFMA i (ks = i / NKB, kb = i % NKB)
-        return lds_read_b128(knxt, S::KT::off(32 * (i % S::NKB) + (lane & 31), 2 * (i / S::NKB) + hh));
+        return lds_read_b128(knxt, kbase + 32 * (i % S::NKB) * S::KS + 32 * (i / S::NKB));
       };
       auto vread = [&](int i, int half) {  // V^T fragment half of PV MFMA i (ks = i / NVB, vb = i % NVB)
         const int ks = i / S::NVB, vb = i % S::NVB;
-        return lds_read_tr(vcur, S::VT::tr(lane, 16 * ks + 8 * half + 4 * hh, vb * 32 + 16 * g1));
+        return lds_read_tr(vcur, vbase + (16 * ks + 8 * half) * S::VS + 64 * vb);
       };
 
       // ---- phase A: S^T(t1) on the MFMA pipe, weights of t0 on the VALU ----
@@ -621,8 +629,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       l_use += lu[0] + lu[1];
 
       // ---- phase B: O^T += V^T P^T(t0) on the MFMA pipe, row max of t1 ----
-      // Max tree over the 32 scores of t1: node 32 + k = max(node 2k, node 2k + 1).
-      float tree[63];
+      // Max over the 32 scores of t1 in three-input steps (v_max3): node
+      // 32 + k = max(node 3k, 3k + 1, 3k + 2) for k = 0..14 covers every
+      // score by node 45 or 46, so the row max is max(node 45, node 46).
+      float tree[47];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         tree[r] = nxt[0][r];
@@ -630,7 +640,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[(i / S::NVB) / 2][(i / S::NVB) % 2]);
         o[i % S::NVB] = mfma_bf16(join_tr(vfr[2 * (i % 2)], vfr[2 * (i % 2) + 1]), pb, o[i % S::NVB]);
         if (i + 2 < NP) {
@@ -638,11 +647,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           vfr[2 * (i % 2) + 1] = vread(i + 2, 1);
         }
 #pragma unroll
-        for (int k = i * 31 / NP; k < (i + 1) * 31 / NP; ++k) tree[32 + k] = fmaxf(tree[2 * k], tree[2 * k + 1]);
+        for (int k = i * 15 / NP; k < (i + 1) * 15 / NP; ++k)
+          tree[32 + k] = fmaxf(fmaxf(tree[3 * k], tree[3 * k + 1]), tree[3 * k + 2]);
+      }
+      // One MFMA, its reads two MFMAs ahead, one max step per group.
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i + 2 < NP) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (t1 < kt_end) {  // else nxt holds scores of stale LDS contents: unused
-        const float mx = max_halves(tree[62]) * scale2;
+        const float mx = max_halves(fmaxf(tree[45], tree[46])) * scale2;
         raise = mx > m_run + kRescaleSlack;
         m_new = raise ? fmaxf(m_run, mx) : m_run;
         alpha = (!raise || m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);

@@ -16,6 +16,9 @@ constexpr int kBwdBk = 128;
 // Backward dQ (query-tile outer): the forward's tiling.
 constexpr int kDqBq = 128;
 constexpr int kDqBk = 32;
+// Per-(batch, head) row padding of the backward's D and L2 arrays (a
+// multiple of every query tile), so that whole tiles can be copied.
+constexpr int kRowPad = 128;
 
 struct FwdParams {
   const void* Q;
@@ -42,7 +45,9 @@ struct BwdParams {
   const void* O;
   const void* dO;
   const float* L;
-  float* Dv;     // D_i = <dO_i, O_i>, fp32 [B, H, n]
+  float* Dv;     // D_i = <dO_i, O_i>, fp32 [B, H, n_pad]
+  float* L2;     // L_i log2(e) (+inf where L_i = -inf), fp32 [B, H, n_pad]
+  int64_t n_pad;  // row stride of Dv and L2: n rounded up to kRowPad; rows >= n hold D = 0, L2 = +inf
   float* dQacc;  // fp32 [B, H, n, d] accumulator (unscaled by c)
   void* dQ;
   void* dK;
@@ -80,6 +85,9 @@ struct MapParams {
 int launch_fwd(const FwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
 int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, bool fused, void* stream);
 int launch_bwd_dq(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
+// Pipelined dK / dV kernel of the deterministic path (bf16, d and v in {64, 128}).
+bool bwd_kv_supported(int bf16, int d, int v, int mask_mode, int64_t tq);
+int launch_bwd_kv(const BwdParams& p, int d, int v, int mask_mode, void* stream);
 int launch_tile_map(const MapParams& p, void* stream);
 int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, bool clear_dq, void* stream);
 int launch_bwd_post(const BwdParams& p, int bf16, int d, void* stream);

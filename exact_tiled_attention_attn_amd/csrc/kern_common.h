@@ -165,6 +165,25 @@ struct Swz {
   }
 };
 
+// Padded LDS tile layout for direct fills: rows of RB data bytes at a stride
+// of RB + PAD bytes (RB a multiple of 16).  With PAD = 16 a wave's b128 row
+// reads (16 rows, one chunk each) spread over all 64 banks for RB = 128 or
+// 256; with PAD = 64 the four rows of a transposed b64 read land on
+// disjoint 64-byte bank spans for RB = 256 (PAD = 64 for RB = 128 as well).
+// Every read address is a per-lane base plus a compile-time offset.
+constexpr int kPastEnd = (int)0x80000000u;  // source offset past any buffer: reads zero
+template <int RB, int PAD>
+struct PadTile {
+  static constexpr int kStride = RB + PAD;
+  // Source offset, in a row-major tile of `row_bytes` bytes per row, of the
+  // 16 bytes a direct fill writes at byte `o` of the LDS tile; padding slots
+  // read zeros.
+  static __device__ __forceinline__ int fill_src(int o, int row_bytes) {
+    const int r = o / kStride, c = o % kStride;
+    return c < RB ? r * row_bytes + c : kPastEnd;
+  }
+};
+
 // Direct global -> LDS copy: the lanes' 16-byte chunks, read at their own
 // byte offsets `voff` of buffer `r`, land lane-contiguously at lds[16 lane]
 // (1 KB per wave).  Completion is tracked by vmcnt: wait_vm() before the

@@ -78,10 +78,11 @@ def test_workspace_formula():
             assert st == 0 and fw == 0
             st, bw = wsize(p, 1)
             al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-            assert st == 0 and bw == al(4 * B * H * n) + al(4 * B * H * n * d)
+            npad = (n + 127) // 128 * 128  # D and L log2(e) rows, padded per head
+            assert st == 0 and bw == 2 * al(4 * B * H * npad) + al(4 * B * H * n * d)
             p.deterministic = 1  # no dQ accumulator
             st, bw = wsize(p, 1)
-            assert st == 0 and bw == al(4 * B * H * n)
+            assert st == 0 and bw == 2 * al(4 * B * H * npad)
     # bitmask: + tile map (units x tq x tk bytes); forward tiles 128 x 64, backward 64 x 128 (bf16)
     p = problem(2, 8, 8192, 64, 128, 1, 2)
     p.mask = FAKE
@@ -89,10 +90,10 @@ def test_workspace_formula():
     st, fw = wsize(p, 0)
     assert st == 0 and fw == (8 * 64 * 128 + 255) // 256 * 256
     st, bw = wsize(p, 1)
-    assert bw == 4 * 16 * 8192 + 4 * 16 * 8192 * 64 + 8 * 128 * 64
-    p.deterministic = 1  # D + key-tile-outer map (64 x 128 tiles) + dQ map (128 x 32 tiles)
+    assert bw == 2 * 4 * 16 * 8192 + 4 * 16 * 8192 * 64 + 8 * 128 * 64
+    p.deterministic = 1  # D, L2 + key-tile-outer map (64 x 128 tiles) + dQ map (128 x 32 tiles)
     st, bw = wsize(p, 1)
-    assert bw == 4 * 16 * 8192 + 8 * 128 * 64 + 8 * 64 * 256
+    assert bw == 2 * 4 * 16 * 8192 + 8 * 128 * 64 + 8 * 64 * 256
 
 
 @pytest.mark.parametrize("mut,status", [
