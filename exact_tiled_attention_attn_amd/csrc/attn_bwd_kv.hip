@@ -71,6 +71,15 @@ __device__ __forceinline__ void wait_vm_n() {
 
 }  // namespace
 
+#ifndef ETA_KV_PREFETCH_A
+#define ETA_KV_PREFETCH_A 4
+#endif
+#ifndef ETA_KV_PREFETCH_B
+#define ETA_KV_PREFETCH_B 2
+#endif
+// LDS operand prefetch depth, in MFMAs, of the two phases.
+constexpr int kPrefetchA = ETA_KV_PREFETCH_A, kPrefetchB = ETA_KV_PREFETCH_B;
+
 template <int D, int DV>
 struct KvShape {
   static constexpr int NW = 4;
@@ -285,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     const float* nds = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_D) + 32 * nc + 4 * hh;
 
     // ---- phase A ----
-    constexpr int PF = 4;  // row operands in flight
+    constexpr int PF = kPrefetchA;  // row operands in flight
     auto aread = [&](int i) -> bf16x8 {  // operand of MFMA i: dP (ks) or S (ks), interleaved
       const int si = (i * S::NQF) / S::NA, next = ((i + 1) * S::NQF) / S::NA;
       if (next > si) return *reinterpret_cast<const bf16x8*>(nqb + qra[si]);
@@ -297,15 +306,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     nsc = f32x16{};
     ndp = f32x16{};
     u32x4 pk[2], sk[2];
-    auto weights = [&](int pr) {  // rows 2 pr, 2 pr + 1 of the chunk's registers
+    // Weights of row pair pr in two halves, issued one slice apart so that
+    // the exponentials' latency is covered: e(pr) = exponentials, f(pr) = dS
+    // and the bf16 packing.
+    float pe[8][2];
+    auto weights_e = [&](int pr) {
       const int r = 2 * pr, g = r >> 2, e = r & 3;
-      const float p0 = fast_exp2(__builtin_fmaf(sc[r], scale2, -lv[g][e]));
-      const float p1 = fast_exp2(__builtin_fmaf(sc[r + 1], scale2, -lv[g][e + 1]));
-      const float d0 = p0 * (dp[r] - dvv[g][e]);
-      const float d1 = p1 * (dp[r + 1] - dvv[g][e + 1]);
-      pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+      pe[pr][0] = fast_exp2(__builtin_fmaf(sc[r], scale2, -lv[g][e]));
+      pe[pr][1] = fast_exp2(__builtin_fmaf(sc[r + 1], scale2, -lv[g][e + 1]));
+    };
+    auto weights_f = [&](int pr) {
+      const int r = 2 * pr, g = r >> 2, e = r & 3;
+      const float d0 = pe[pr][0] * (dp[r] - dvv[g][e]);
+      const float d1 = pe[pr][1] * (dp[r + 1] - dvv[g][e + 1]);
+      pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0], pe[pr][1]);
       sk[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
     };
+    // Slices 0..8 over the NA MFMAs: slice k issues e(k) and f(k - 1).
 #pragma unroll
     for (int i = 0; i < S::NA; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -314,7 +331,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       else ndp = mfma_bf16(afr[i % PF], vf[i - si], ndp);
       if (i + PF < S::NA) afr[i % PF] = aread(i + PF);
 #pragma unroll
-      for (int pr = i * 8 / S::NA; pr < (i + 1) * 8 / S::NA; ++pr) weights(pr);
+      for (int k = i * 9 / S::NA; k < (i + 1) * 9 / S::NA; ++k) {
+        if (k < 8) weights_e(k);
+        if (k > 0) weights_f(k - 1);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -338,18 +358,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       lo = lds_read_tr(base + 16 * ks * stride, a0);
       hi = lds_read_tr(base + 16 * ks * stride, a1);
     };
-    i16x4 tlo[2], thi[2];
-    bread(0, tlo[0], thi[0]);
-    bread(1, tlo[1], thi[1]);
+    constexpr int PB = kPrefetchB;  // transposed operands in flight (MFMAs ahead)
+    i16x4 tlo[PB], thi[PB];
+#pragma unroll
+    for (int j = 0; j < PB; ++j) bread(j, tlo[j], thi[j]);
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) {
       bool is_v;
       int blk, ks;
       bmfma(j, is_v, blk, ks);
-      const bf16x8 a = join_tr(tlo[j % 2], thi[j % 2]);
+      const bf16x8 a = join_tr(tlo[j % PB], thi[j % PB]);
       if (is_v) dv[blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, pk[ks]), dv[blk]);
       else dk[blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, sk[ks]), dk[blk]);
-      if (j + 2 < S::NB) bread(j + 2, tlo[j % 2], thi[j % 2]);
+      if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
       if (j == S::NB - 4) {  // next chunk's L log2(e) and D rows
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -358,11 +379,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         }
       }
     }
-    // One MFMA, the reads two MFMAs ahead, per group.
+    // One MFMA, the reads PB MFMAs ahead, per group.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PB, 0);
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (j + 2 < S::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      if (j + PB < S::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       if (j == S::NB - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
