@@ -31,45 +31,6 @@
 
 namespace eta {
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-namespace {
-
-// Buffer descriptor words (raw 32-bit format): loads at byte offsets >=
-// `bytes` return zero.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const int nb = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
-  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), nb, 0x00020000};
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Direct HBM -> LDS copies: lane l's 16 (4) bytes, read at byte offset
-// `voff` of the buffer, land at LDS byte address lds + 16 l (lds + 4 l).  The
-// compiler does not see these as LDS writes, so it inserts no waits for them;
-// completion is awaited explicitly (wait_vm_n) before the barrier that
-// publishes the data.
-__device__ __forceinline__ void fill16(i32x4 r, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void fill4(i32x4 r, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_n() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-}  // namespace
 
 #ifndef ETA_KV_PREFETCH_A
 #define ETA_KV_PREFETCH_A 4
