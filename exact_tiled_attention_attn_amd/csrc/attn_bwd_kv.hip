@@ -22,10 +22,13 @@
 // the vector ALUs turn chunk k's scores into P and dS, then chunk k's dV / dK
 // products run; the instruction order is pinned with scheduling barriers.
 // Q, dO, L log2(e) and D (and the bitmask words) are copied from HBM
-// straight into a 4-stage ring of XOR-swizzled LDS tiles (buffer_load ...
-// lds, issued from inline assembly and counted with vmcnt), two tiles ahead
-// of their use, with one barrier per tile.  Every LDS read address is a
-// per-lane register plus a constant.
+// straight into a 4-stage ring of LDS tiles (buffer_load ... lds, issued
+// from inline assembly and counted with vmcnt), two tiles ahead of their
+// use, with one barrier per tile.  Tile rows are padded by 16 bytes and the
+// query rows of each group of 16 are taken in transposed order (4 u + v ->
+// u + 4 v) by the score products, so the transposed reads of dO^T and Q^T
+// cover rows 4 apart: both kinds of read are then free of bank conflicts
+// and every LDS read address is one per-lane register plus a constant.
 #include "attn_internal.h"
 #include "kern_common.h"
 
@@ -51,17 +54,21 @@ struct KvShape {
   static constexpr int NDB = D / 32, NVB = DV / 32;  // 32-column blocks of dK^T / dV^T
   static constexpr int NA = NQF + NVF;               // S and dP MFMAs per chunk
   static constexpr int NB = 2 * (NDB + NVB);         // dK and dV MFMAs per chunk
-  using QT = Swz<D / 8>;
-  using OT = Swz<DV / 8>;
-  static constexpr int QTILE = BQ * QT::kStride, OTILE = BQ * OT::kStride;
-  static constexpr int QWIN = QTILE / 1024 / NW, OWIN = OTILE / 1024 / NW;  // 1 KB fills per wave
+  using QT = PadTile<D * 2, 16>;
+  using OT = PadTile<DV * 2, 16>;
+  static constexpr int QS = QT::kStride, OS = OT::kStride;
+  static constexpr int QTILE = BQ * QS, OTILE = BQ * OS;
+  static constexpr int QWINS = QTILE / 1024, OWINS = OTILE / 1024;  // 1 KB fill windows per tile
+  // Windows of wave w: w, w + NW, ... (the counts differ by wave).
+  static constexpr int QWIN = (QWINS + NW - 1) / NW, OWIN = (OWINS + NW - 1) / NW;
+  static constexpr int qwins(int w) { return (QWINS - w + NW - 1) / NW; }
+  static constexpr int owins(int w) { return (OWINS - w + NW - 1) / NW; }
   static constexpr int MWORDS = BK / 32;
   // Per stage: L log2(e) [BQ], D [BQ], mask words [BQ][MWORDS].
   static constexpr int LD_L = 0, LD_D = BQ * 4, LD_M = 2 * BQ * 4;
   static constexpr int LDB = LD_M + BQ * MWORDS * 4;
   static constexpr int MAXTQ = 4096;  // bitmask: query tiles whose classes are staged in LDS
-  static_assert(QT::kSwizzle && OT::kSwizzle && QT::kStride == D * 2 && OT::kStride == DV * 2, "layout");
-  static_assert(QTILE % (1024 * NW) == 0 && OTILE % (1024 * NW) == 0, "tile fills");
+  static_assert(QTILE % 1024 == 0 && OTILE % 1024 == 0, "whole fill windows");
   static_assert(BQ == 64 && BK == 128, "two chunks of 32 queries, 32 keys per wave");
 };
 
@@ -149,26 +156,35 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // ---- tile fills ----------------------------------------------------------
   int qsrc[S::QWIN], osrc[S::OWIN];
 #pragma unroll
-  for (int i = 0; i < S::QWIN; ++i) qsrc[i] = S::QT::dma_src(w * S::QWIN + i, lane, qrow);
+  for (int i = 0; i < S::QWIN; ++i) qsrc[i] = S::QT::fill_src((w + S::NW * i) * 1024 + 16 * lane, qrow);
 #pragma unroll
-  for (int i = 0; i < S::OWIN; ++i) osrc[i] = S::OT::dma_src(w * S::OWIN + i, lane, orow);
+  for (int i = 0; i < S::OWIN; ++i) osrc[i] = S::OT::fill_src((w + S::NW * i) * 1024 + 16 * lane, orow);
+  // Query row of the tile behind LDS slot l of the L / D copies (and behind
+  // lane l % 32 of a score product's A operand): groups of 16 rows taken in
+  // transposed order, 4 u + v -> u + 4 v.
+  auto perm = [](int l) { return (l & ~15) + ((l & 15) >> 2) + 4 * (l & 3); };
   const uint32_t qs_l = lds_address(qs), os_l = lds_address(os), ld_l = lds_address(lds_ld);
-  // Per tile, wave w issues QWIN + OWIN tile fills, waves 0 / 1 one more (L
-  // log2(e) / D rows), and with a bitmask every wave one more (mask words of
-  // 16 query rows).
-  constexpr int kFillsA = S::QWIN + S::OWIN + 1 + (MASK == kMaskBitmask);  // waves 0, 1
-  constexpr int kFillsB = S::QWIN + S::OWIN + (MASK == kMaskBitmask);      // waves 2, 3
+  // Per tile, wave w issues qwins(w) + owins(w) tile fills, waves 0 / 1 one
+  // more (L log2(e) / D rows), and with a bitmask every wave one more (mask
+  // words of 16 query rows).
+  constexpr int kBm = MASK == kMaskBitmask;
+  constexpr int kF0 = S::qwins(0) + S::owins(0) + 1 + kBm, kF1 = S::qwins(1) + S::owins(1) + 1 + kBm;
+  constexpr int kF2 = S::qwins(2) + S::owins(2) + kBm, kF3 = S::qwins(3) + S::owins(3) + kBm;
   auto fill = [&](int qt, int st) {
     const int q0 = qt * S::BQ;
     const i32x4 rq = rsrc_words(Qb + (int64_t)q0 * qrow, (int64_t)(n - q0) * qrow);
     const i32x4 ro = rsrc_words(dOb + (int64_t)q0 * orow, (int64_t)(n - q0) * orow);
 #pragma unroll
-    for (int i = 0; i < S::QWIN; ++i) fill16(rq, qs_l + st * S::QTILE + (w * S::QWIN + i) * 1024, qsrc[i]);
+    for (int i = 0; i < S::QWIN; ++i)
+      if (S::QWINS % S::NW == 0 || w + S::NW * i < S::QWINS)
+        fill16(rq, qs_l + st * S::QTILE + (w + S::NW * i) * 1024, qsrc[i]);
 #pragma unroll
-    for (int i = 0; i < S::OWIN; ++i) fill16(ro, os_l + st * S::OTILE + (w * S::OWIN + i) * 1024, osrc[i]);
-    if (w < 2) {  // padded rows: always in range
+    for (int i = 0; i < S::OWIN; ++i)
+      if (S::OWINS % S::NW == 0 || w + S::NW * i < S::OWINS)
+        fill16(ro, os_l + st * S::OTILE + (w + S::NW * i) * 1024, osrc[i]);
+    if (w < 2) {  // padded rows: always in range; slot l holds row perm(l)
       const float* src = (w == 0 ? L2b : Db) + q0;
-      fill4(rsrc_words(src, S::BQ * 4), ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D), 4 * lane);
+      fill4(rsrc_words(src, S::BQ * 4), ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D), 4 * perm(lane));
     }
     if constexpr (MASK == kMaskBitmask) {
       // Row 16 w + lane / 4 of the tile, word lane % 4 of this key tile.
@@ -179,45 +195,44 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   };
   // Wait until at most k of this wave's tile fills are still in flight.
   auto wait_fills = [&](int k) {
-    if (w < 2) {
-      if (k <= 0) wait_vm_n<0>();
-      else if (k == 1) wait_vm_n<kFillsA>();
-      else wait_vm_n<2 * kFillsA>();
+    if (k <= 0) {
+      wait_vm_n<0>();
+    } else if (k == 1) {
+      if (w == 0) wait_vm_n<kF0>();
+      else if (w == 1) wait_vm_n<kF1>();
+      else if (w == 2) wait_vm_n<kF2>();
+      else wait_vm_n<kF3>();
     } else {
-      if (k <= 0) wait_vm_n<0>();
-      else if (k == 1) wait_vm_n<kFillsB>();
-      else wait_vm_n<2 * kFillsB>();
+      if (w == 0) wait_vm_n<2 * kF0>();
+      else if (w == 1) wait_vm_n<2 * kF1>();
+      else if (w == 2) wait_vm_n<2 * kF2>();
+      else wait_vm_n<2 * kF3>();
     }
   };
 
-  // ---- per-lane LDS read addresses (stage and chunk offsets are constants) --
-  // Row operands (S, dP): row lane % 32 of the chunk, chunk 2 ks + hh.
-  int qra[S::NQF], ora[S::NVF];
-#pragma unroll
-  for (int s = 0; s < S::NQF; ++s) qra[s] = (int)S::QT::off(lane & 31, 2 * s + hh);
-#pragma unroll
-  for (int s = 0; s < S::NVF; ++s) ora[s] = (int)S::OT::off(lane & 31, 2 * s + hh);
-  // Transposed operands (dK, dV): rows 4 hh + 8 half + i / 4, columns 32 blk + 16 g1.
-  int qta[S::NDB][2], ota[S::NVB][2];
-#pragma unroll
-  for (int db = 0; db < S::NDB; ++db)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) qta[db][hf] = (int)S::QT::tr(lane, 8 * hf + 4 * hh, 32 * db + 16 * g1);
-#pragma unroll
-  for (int vb = 0; vb < S::NVB; ++vb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) ota[vb][hf] = (int)S::OT::tr(lane, 8 * hf + 4 * hh, 32 * vb + 16 * g1);
+  // ---- per-lane LDS read bases (everything else is a constant offset) -----
+  // Row operands (S, dP): A-operand lane m = lane % 32 of a 32-row chunk
+  // reads row perm(m), 16-byte chunk 2 ks + hh.
+  const int qrb = perm(lane & 31) * S::QS + 16 * hh, orb = perm(lane & 31) * S::OS + 16 * hh;
+  // Transposed operands (dK, dV): lane r of a 16-lane group gives the address
+  // of row hh + 4 (r / 4) (+ 2 for the upper four contraction indices, + 16
+  // per key step), columns 32 blk + 16 g1 + 4 (r % 4): it then receives
+  // column 32 blk + 16 g1 + r of rows hh, hh + 4, hh + 8, hh + 12, which are
+  // the query rows perm() put at C rows 4 hh + 0..3 (resp. 8 + 4 hh + 0..3).
+  const int r16 = lane & 15;
+  const int qtb = (hh + 4 * (r16 >> 2)) * S::QS + 2 * (16 * g1 + 4 * (r16 & 3));
+  const int otb = (hh + 4 * (r16 >> 2)) * S::OS + 2 * (16 * g1 + 4 * (r16 & 3));
 
   // S and dP of one chunk (32 query rows at tile row 32 c) from stage st.
   auto score_products = [&](f32x16& sc, f32x16& dp, int st, int c) {
-    const char* qb = qs + st * S::QTILE + 32 * c * S::QT::kStride;
-    const char* ob = os + st * S::OTILE + 32 * c * S::OT::kStride;
+    const char* qb = qs + st * S::QTILE + 32 * c * S::QS;
+    const char* ob = os + st * S::OTILE + 32 * c * S::OS;
     sc = f32x16{};
     dp = f32x16{};
 #pragma unroll
-    for (int s = 0; s < S::NQF; ++s) sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qb + qra[s]), kf[s], sc);
+    for (int s = 0; s < S::NQF; ++s) sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qb + qrb + 32 * s), kf[s], sc);
 #pragma unroll
-    for (int s = 0; s < S::NVF; ++s) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(ob + ora[s]), vf[s], dp);
+    for (int s = 0; s < S::NVF; ++s) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(ob + orb + 32 * s), vf[s], dp);
   };
   // Exponent scale: c log2(e), with c = 0 replaced by 1e-30 (every finite
   // score then maps to exactly exp2(-L log2 e), as for c = 0, while the
@@ -225,12 +240,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const float scale2 = p.scale2 == 0.f ? 1e-30f : p.scale2;
   const float masked_score = scale2 > 0.f ? -INFINITY : INFINITY;  // exp2(score * scale2 - l) = 0
   // Partially allowed tile: scores of disallowed pairs -> the sentinel.
-  // Register r of a chunk holds query row 32 c + 8 (r / 4) + 4 hh + r % 4.
+  // Register r of a chunk holds C row m = 8 (r / 4) + 4 hh + r % 4, i.e.
+  // query row 32 c + perm(m) of the tile.
   auto mask_chunk = [&](f32x16& sc, int st, int c, int q0) {
     const uint32_t* ms = reinterpret_cast<const uint32_t*>(lds_ld + st * S::LDB + S::LD_M);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int ql = 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int ql = 32 * c + perm(8 * (r >> 2) + 4 * hh + (r & 3));
       bool ok = kvalid;
       if constexpr (MASK == kMaskCausal) ok = ok && key <= q0 + ql;
       if constexpr (MASK == kMaskBitmask) ok = ok && ((ms[ql * S::MWORDS + w] >> (lane & 31)) & 1u);
@@ -247,10 +263,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // on return they hold those of the next chunk.
   f32x4 lv[4], dvv[4];
   auto step = [&](f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc) {
-    const char* nqb = qs + nst * S::QTILE + 32 * nc * S::QT::kStride;
-    const char* nob = os + nst * S::OTILE + 32 * nc * S::OT::kStride;
-    const char* qb = qs + st * S::QTILE + 32 * c * S::QT::kStride;
-    const char* ob = os + st * S::OTILE + 32 * c * S::OT::kStride;
+    const char* nqb = qs + nst * S::QTILE + 32 * nc * S::QS + qrb;
+    const char* nob = os + nst * S::OTILE + 32 * nc * S::OS + orb;
+    const char* qb = qs + st * S::QTILE + 32 * c * S::QS + qtb;
+    const char* ob = os + st * S::OTILE + 32 * c * S::OS + otb;
     const float* nls = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_L) + 32 * nc + 4 * hh;
     const float* nds = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_D) + 32 * nc + 4 * hh;
 
@@ -258,8 +274,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     constexpr int PF = kPrefetchA;  // row operands in flight
     auto aread = [&](int i) -> bf16x8 {  // operand of MFMA i: dP (ks) or S (ks), interleaved
       const int si = (i * S::NQF) / S::NA, next = ((i + 1) * S::NQF) / S::NA;
-      if (next > si) return *reinterpret_cast<const bf16x8*>(nqb + qra[si]);
-      return *reinterpret_cast<const bf16x8*>(nob + ora[i - si]);
+      if (next > si) return *reinterpret_cast<const bf16x8*>(nqb + 32 * si);
+      return *reinterpret_cast<const bf16x8*>(nob + 32 * (i - si));
     };
     bf16x8 afr[PF];
 #pragma unroll
@@ -314,10 +330,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       int blk, ks;
       bmfma(j, is_v, blk, ks);
       const char* base = is_v ? ob : qb;
-      const int stride = is_v ? S::OT::kStride : S::QT::kStride;
-      const int a0 = is_v ? ota[blk][0] : qta[blk][0], a1 = is_v ? ota[blk][1] : qta[blk][1];
-      lo = lds_read_tr(base + 16 * ks * stride, a0);
-      hi = lds_read_tr(base + 16 * ks * stride, a1);
+      const int stride = is_v ? S::OS : S::QS;
+      lo = lds_read_tr(base + 16 * ks * stride, 64 * blk);
+      hi = lds_read_tr(base + (16 * ks + 2) * stride, 64 * blk);
     };
     constexpr int PB = kPrefetchB;  // transposed operands in flight (MFMAs ahead)
     i16x4 tlo[PB], thi[PB];
