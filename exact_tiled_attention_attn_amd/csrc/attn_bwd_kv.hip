@@ -39,7 +39,7 @@ namespace eta {
 #define ETA_KV_PREFETCH_A 4
 #endif
 #ifndef ETA_KV_PREFETCH_B
-#define ETA_KV_PREFETCH_B 2
+#define ETA_KV_PREFETCH_B 3
 #endif
 // LDS operand prefetch depth, in MFMAs, of the two phases.
 constexpr int kPrefetchA = ETA_KV_PREFETCH_A, kPrefetchB = ETA_KV_PREFETCH_B;
@@ -193,6 +193,40 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       fill4(rm, ld_l + st * S::LDB + S::LD_M + 256 * w, (int)(((int64_t)r * p.mask_si + (k0 >> 5) + (lane & 3)) * 4));
     }
   };
+  // The same copies split in two, for the fill issued inside a pipeline step:
+  // FQ + FO windows that every wave copies (issued one per MFMA of the step's
+  // first phase) and the rest.  qt < 0 copies nothing (empty buffer ranges)
+  // but issues the same instructions, so that the per-wave counts hold.
+  constexpr int FQ = S::QWINS / S::NW, FO = S::OWINS / S::NW;
+  i32x4 frq, fro;
+  int fst = 0;
+  auto fill_begin = [&](int qt, int st) {  // descriptors and the uneven rest
+    const int q0 = qt < 0 ? 0 : qt * S::BQ;
+    const int64_t rows = qt < 0 ? 0 : n - q0;
+    frq = rsrc_words(Qb + (int64_t)q0 * qrow, rows * qrow);
+    fro = rsrc_words(dOb + (int64_t)q0 * orow, rows * orow);
+    fst = st;
+#pragma unroll
+    for (int i = FQ; i < S::QWIN; ++i)
+      if (w + S::NW * i < S::QWINS) fill16(frq, qs_l + st * S::QTILE + (w + S::NW * i) * 1024, qsrc[i]);
+#pragma unroll
+    for (int i = FO; i < S::OWIN; ++i)
+      if (w + S::NW * i < S::OWINS) fill16(fro, os_l + st * S::OTILE + (w + S::NW * i) * 1024, osrc[i]);
+    if (w < 2) {
+      const float* src = (w == 0 ? L2b : Db) + q0;
+      fill4(rsrc_words(src, qt < 0 ? 0 : S::BQ * 4), ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D), 4 * perm(lane));
+    }
+    if constexpr (MASK == kMaskBitmask) {
+      const int r = 16 * w + lane / 4;
+      const i32x4 rm = rsrc_words(mbase + (int64_t)q0 * p.mask_si, rows * p.mask_si * 4);
+      fill4(rm, ld_l + st * S::LDB + S::LD_M + 256 * w, (int)(((int64_t)r * p.mask_si + (k0 >> 5) + (lane & 3)) * 4));
+    }
+  };
+  auto fill_item = [&](int i) {  // i < FQ + FO
+    if (i < FQ) fill16(frq, qs_l + fst * S::QTILE + (w + S::NW * i) * 1024, qsrc[i]);
+    else fill16(fro, os_l + fst * S::OTILE + (w + S::NW * (i - FQ)) * 1024, osrc[i - FQ]);
+  };
+  static_assert(FQ + FO <= S::NQF + S::NVF, "one spread fill per first-phase MFMA at most");
   // Wait until at most k of this wave's tile fills are still in flight.
   auto wait_fills = [&](int k) {
     if (k <= 0) {
@@ -262,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // lv / dvv hold this chunk's L log2(e) and D rows (f32x4 per row group);
   // on return they hold those of the next chunk.
   f32x4 lv[4], dvv[4];
-  auto step = [&](f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc) {
+  auto step = [&](auto dofill, f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc) {
     const char* nqb = qs + nst * S::QTILE + 32 * nc * S::QS + qrb;
     const char* nob = os + nst * S::OTILE + 32 * nc * S::OS + orb;
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS + qtb;
@@ -307,6 +341,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       if (next > si) nsc = mfma_bf16(afr[i % PF], kf[si], nsc);
       else ndp = mfma_bf16(afr[i % PF], vf[i - si], ndp);
       if (i + PF < S::NA) afr[i % PF] = aread(i + PF);
+      if constexpr (decltype(dofill)::value) {
+        if (i < FQ + FO) fill_item(i);
+      }
 #pragma unroll
       for (int k = i * 9 / S::NA; k < (i + 1) * 9 / S::NA; ++k) {
         if (k < 8) weights_e(k);
@@ -347,12 +384,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       if (is_v) dv[blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, pk[ks]), dv[blk]);
       else dk[blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, sk[ks]), dk[blk]);
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
-      if (j == S::NB - 4) {  // next chunk's L log2(e) and D rows
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          lv[g] = *reinterpret_cast<const f32x4*>(nls + 8 * g);
-          dvv[g] = *reinterpret_cast<const f32x4*>(nds + 8 * g);
-        }
+      if (j < 8) {  // next chunk's L log2(e) and D rows, one read per MFMA
+        if (j % 2 == 0) lv[j / 2] = *reinterpret_cast<const f32x4*>(nls + 8 * (j / 2));
+        else dvv[j / 2] = *reinterpret_cast<const f32x4*>(nds + 8 * (j / 2));
       }
     }
     // One MFMA, the reads PB MFMAs ahead, per group.
@@ -361,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     for (int j = 0; j < S::NB; ++j) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       if (j + PB < S::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      if (j == S::NB - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+      if (j < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -397,19 +431,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       const bool partial = tile_class(t0) == kTilePartial;
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, q0);
-      step(sa, pa, sb, pb, st, 0, st, 1);
+      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1);
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3.
       wait_fills(issued - (j + 2 < issued ? j + 2 : issued));
       __syncthreads();
-      if (t3 >= 0) {
-        fill(t3, (j + 3) % S::NSTAGE);
-        ++issued;
-      }
+      // The fill of position j+3 (empty past the last tile) is spread over
+      // chunk 1's first phase.
+      fill_begin(t3, (j + 3) % S::NSTAGE);
+      ++issued;
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, q0);
-      step(sb, pb, sa, pa, st, 1, nst, 0);
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0);
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;
@@ -417,6 +451,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       t3 = next_tile(t2);
       ++j;
     }
+    wait_vm_n<0>();  // copies of empty positions
   }
 
   // Epilogue: dK = c dK^T, dV = dV^T (lane = key; 4 consecutive columns per store).
