@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libattn.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_dq.hip", "attn_aux.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_dq.hip", "attn_bwd_dq_pipe.hip", "attn_aux.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",
@@ -33,10 +33,11 @@ DEVICE = [
 ]
 # Keep MFMA sources and accumulators in VGPRs (files whose kernels fit in 256
 # VGPRs: with AGPR-form MFMAs their loop-carried accumulators were copied
-# between AGPRs and VGPRs every iteration).  The pipelined dK / dV kernel
-# needs more than 256 registers and keeps its dK / dV accumulators in AGPRs.
+# between AGPRs and VGPRs every iteration).  The pipelined dK / dV and dQ
+# kernels need more than 256 registers and keep their gradient accumulators
+# in AGPRs.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-AGPR_FORM_SOURCES = {"attn_bwd_kv.hip"}
+AGPR_FORM_SOURCES = {"attn_bwd_kv.hip", "attn_bwd_dq_pipe.hip"}
 
 
 def _compile(src: str) -> str:

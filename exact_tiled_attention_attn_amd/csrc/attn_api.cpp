@@ -50,6 +50,8 @@ int64_t row_pad(int64_t n) { return cdiv(n, eta::kRowPad) * eta::kRowPad; }
 int64_t mask_units(const attn_problem& p) { return p.mask_sb == 0 ? p.H : p.B * p.H; }
 
 Tiles dq_tiles(const attn_problem& p) {
+  if (eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, p.n))
+    return Tiles{eta::kDqPipeBq, eta::kDqPipeBk, cdiv(p.n, eta::kDqPipeBq), cdiv(p.n, eta::kDqPipeBk)};
   return Tiles{eta::kDqBq, eta::kDqBk, cdiv(p.n, eta::kDqBq), cdiv(p.n, eta::kDqBk)};
 }
 

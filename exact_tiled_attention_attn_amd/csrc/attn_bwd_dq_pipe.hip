@@ -1,0 +1,499 @@
+// Backward, query-tile-outer dQ kernel for bf16 with d, v in {64, 128}: the
+// second kernel of the deterministic backward (dK and dV come from the
+// key-tile-outer kernel).
+//
+// Method (alphabetamath page, reverse procedure; ob1 page, part 2;
+// HarshvardhanJ README, backward section): with the forward's L and
+// D_i = <dO_i, O_i>, for every allowed (i, j) recompute s_ij = c <Q_i, K_j>,
+// p_ij = exp(s_ij - L_i), dS_ij = p_ij (<dO_i, V_j> - D_i) and accumulate
+// dQ_i += c dS_ij K_j.  Each workgroup owns 256 query rows and streams the
+// key tiles in ascending order, so every dQ row is summed by one lane in a
+// fixed order: the result is deterministic and needs no atomics.  Tiles with
+// no allowed pair are skipped; only partially allowed tiles are masked (ob1
+// page, part 3).
+//
+// gfx950 design.  One workgroup per CU; each of its 4 waves owns 64 queries
+// as two halves of 32 (lane column = query) and keeps their Q and dO rows in
+// registers as MFMA B operands and their dQ^T accumulators in AGPRs, so L_i
+// and D_i are per-lane constants.  Key tiles of 64 rows are processed as two
+// chunks of 32 keys.  Per chunk, S^T = K Q^T and dP^T = V dO^T: every K or V
+// row operand read from LDS feeds the MFMAs of both halves, and the dP^T
+// accumulators start from -D_i, so that they come out as dP - D.  The vector
+// ALUs form P = exp2(c log2(e) s - L_i log2(e)) and dS = P (dP - D) in the
+// score registers, whose packed form is the B operand of dQ^T += K^T dS^T;
+// its K^T operand comes from transposed reads of the same K tile.  The
+// chunks form a software pipeline: the S / dP products of chunk k+1 run on
+// the matrix cores while the vector ALUs work on chunk k, then chunk k's dQ
+// products run; the instruction order is pinned with scheduling barriers.
+// K, V (and the bitmask words) are copied from HBM straight into a 4-stage
+// ring of LDS tiles (buffer_load ... lds, issued from inline assembly and
+// counted with vmcnt) two tiles ahead of their use, with one barrier per
+// tile; the copies of a tile are spread over the MFMAs of a chunk.  Tile rows
+// are padded by 16 bytes and the key rows of each group of 16 are taken in
+// transposed order (4 u + v -> u + 4 v) by the score products, so that the
+// transposed K^T reads cover rows 4 apart: both kinds of read are then free
+// of bank conflicts and every LDS read address is one per-lane register plus
+// a constant.
+#include "attn_internal.h"
+#include "kern_common.h"
+
+namespace eta {
+
+#ifndef ETA_DQ_PREFETCH_A
+#define ETA_DQ_PREFETCH_A 3
+#endif
+#ifndef ETA_DQ_PREFETCH_B
+#define ETA_DQ_PREFETCH_B 3
+#endif
+// LDS operand prefetch depth, in operands (each feeds two MFMAs), of the two phases.
+constexpr int kDqPrefetchA = ETA_DQ_PREFETCH_A, kDqPrefetchB = ETA_DQ_PREFETCH_B;
+
+template <int D, int DV>
+struct DqPipeShape {
+  static constexpr int NW = 4;
+  static constexpr int BQ = kDqPipeBq;  // queries per workgroup: 64 per wave, two halves of 32
+  static constexpr int BK = kDqPipeBk;  // keys per tile: two chunks of 32
+  static constexpr int NSTAGE = 4;      // LDS ring: tiles j .. j+2 resident or in flight
+  static constexpr int NQF = D / 16, NVF = DV / 16;  // Q / dO fragments per lane and half
+  static constexpr int NDB = D / 32;                 // 32-row blocks of dQ^T
+  static constexpr int NR = NQF + NVF;               // K / V row operands per chunk (2 MFMAs each)
+  static constexpr int NB = 2 * NDB;                 // K^T operands per chunk (2 key steps; 2 MFMAs each)
+  using KT = PadTile<D * 2, 16>;
+  using VT = PadTile<DV * 2, 16>;
+  static constexpr int KS = KT::kStride, VS = VT::kStride;
+  static constexpr int KTILE = BK * KS, VTILE = BK * VS;
+  static constexpr int KWINS = KTILE / 1024, VWINS = VTILE / 1024;  // 1 KB fill windows per tile
+  // Windows of wave w: w, w + NW, ... (the counts differ by wave).
+  static constexpr int KWIN = (KWINS + NW - 1) / NW, VWIN = (VWINS + NW - 1) / NW;
+  static constexpr int kwins(int w) { return (KWINS - w + NW - 1) / NW; }
+  static constexpr int vwins(int w) { return (VWINS - w + NW - 1) / NW; }
+  static constexpr int MWORDS = BK / 32;         // bitmask words per query row and tile
+  static constexpr int MTILE = BQ * MWORDS * 4;  // bitmask bytes per stage
+  static constexpr int MAXTK = 4096;             // bitmask: key tiles whose classes are staged in LDS
+  static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "whole fill windows");
+  static_assert(BQ == 256 && BK == 64, "64 queries per wave, two chunks of 32 keys");
+  static_assert(MTILE == NW * 2 * 256, "two 256-byte mask-word copies per wave");
+};
+
+template <int D, int DV, int MASK>
+__global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
+  using S = DqPipeShape<D, DV>;
+  __shared__ __attribute__((aligned(1024))) char kts[S::NSTAGE * S::KTILE];
+  __shared__ __attribute__((aligned(1024))) char vts[S::NSTAGE * S::VTILE];
+  __shared__ __attribute__((aligned(16))) char mws[MASK == kMaskBitmask ? S::NSTAGE * S::MTILE : 16];
+  __shared__ uint8_t cls_s[MASK == kMaskBitmask ? S::MAXTK : 1];
+
+  const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad_dq, p.total_dq);
+  if (logical < 0) return;
+  const int unit = (int)(logical / p.tq_dq);
+  const int qt = p.tq_dq - 1 - (int)(logical % p.tq_dq);  // heaviest causal tiles first
+  const int b = unit / p.H, h = unit % p.H;
+  const int n = (int)p.n;
+  const int q0 = qt * S::BQ;
+  const int tk = (n + S::BK - 1) / S::BK;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int hh = lane >> 5;
+  const int g1 = (lane >> 4) & 1;
+  const int qa = q0 + 64 * w + (lane & 31);  // query of half 0; half 1: qa + 32
+
+  const int qrow = (int)p.sq[2] * 2, krow = (int)p.sk[2] * 2;
+  const int vrow = (int)p.sv[2] * 2, orow = (int)p.so[2] * 2;
+  const char* Qb = (const char*)p.Q + ((int64_t)b * p.sq[0] + (int64_t)h * p.sq[1]) * 2;
+  const char* Kb = (const char*)p.K + ((int64_t)b * p.sk[0] + (int64_t)h * p.sk[1]) * 2;
+  const char* Vb = (const char*)p.V + ((int64_t)b * p.sv[0] + (int64_t)h * p.sv[1]) * 2;
+  const char* dOb = (const char*)p.dO + ((int64_t)b * p.so[0] + (int64_t)h * p.so[1]) * 2;
+  const uint32_t* mbase = nullptr;
+  if constexpr (MASK == kMaskBitmask) mbase = p.mask + b * p.mask_sb + h * p.mask_sh;
+
+  // Per-lane row statistics of the two halves: L log2(e) (+inf for rows past
+  // n or with L = -inf, so that p = 0) and D.
+  float l2[2], dd[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = qa + 32 * u;
+    l2[u] = q < n ? p.L2[(int64_t)unit * p.n_pad + q] : INFINITY;
+    dd[u] = q < n ? p.Dv[(int64_t)unit * p.n_pad + q] : 0.f;
+  }
+
+  // Key-tile sequence: ascending, up to the last tile that can hold an
+  // allowed pair (causal: the tile containing the last query row); bitmask
+  // tiles come from the tile map, staged in LDS so that the loop issues no
+  // loads of its own.
+  int kt_end = tk;
+  if constexpr (MASK == kMaskCausal) {
+    const int q_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1;
+    kt_end = q_hi / S::BK + 1;
+  }
+  if constexpr (MASK == kMaskBitmask) {
+    const int64_t mu = p.mask_sb == 0 ? h : unit;
+    const uint8_t* map_row = p.map_dq + (mu * p.tq_dq + qt) * (int64_t)tk;
+    for (int t = tid; t < tk; t += 256) cls_s[t] = map_row[t];
+  }
+  auto tile_class = [&](int kt) -> uint8_t {
+    if constexpr (MASK == kMaskBitmask) return cls_s[kt];
+    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n);
+  };
+  auto next_tile = [&](int kt) -> int {  // next (higher) tile with an allowed pair, or -1
+    if (kt < 0) return -1;
+    if constexpr (MASK != kMaskBitmask) return kt + 1 < kt_end ? kt + 1 : -1;
+    for (int t = kt + 1; t < kt_end; ++t)
+      if (tile_class(t) != kTileEmpty) return t;
+    return -1;
+  };
+
+  // Q and dO rows of the wave's queries (B operands; lane column = query).
+  bf16x8 qf[2][S::NQF], of[2][S::NVF];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, n * qrow);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb, n * orow);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int s = 0; s < S::NQF; ++s)
+        qf[u][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, (qa + 32 * u) * qrow + (16 * s + 8 * hh) * 2, 0, 0));
+#pragma unroll
+      for (int s = 0; s < S::NVF; ++s)
+        of[u][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, (qa + 32 * u) * orow + (16 * s + 8 * hh) * 2, 0, 0));
+    }
+  }
+  f32x16 dq[2][S::NDB], dinit[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int i = 0; i < S::NDB; ++i) dq[u][i] = f32x16{};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dinit[u][r] = -dd[u];
+  }
+
+  // ---- tile fills ----------------------------------------------------------
+  int ksrc[S::KWIN], vsrc[S::VWIN];
+#pragma unroll
+  for (int i = 0; i < S::KWIN; ++i) ksrc[i] = S::KT::fill_src((w + S::NW * i) * 1024 + 16 * lane, krow);
+#pragma unroll
+  for (int i = 0; i < S::VWIN; ++i) vsrc[i] = S::VT::fill_src((w + S::NW * i) * 1024 + 16 * lane, vrow);
+  // Key row of the tile behind lane m % 32 of a score product's A operand:
+  // groups of 16 rows taken in transposed order, 4 u + v -> u + 4 v.
+  auto perm = [](int l) { return (l & ~15) + ((l & 15) >> 2) + 4 * (l & 3); };
+  const uint32_t ks_l = lds_address(kts), vs_l = lds_address(vts), ms_l = lds_address(mws);
+  // Per tile, wave w issues kwins(w) + vwins(w) tile copies and, with a
+  // bitmask, two more (mask words of 32 query rows each).
+  constexpr int kBm = MASK == kMaskBitmask;
+  constexpr int kF0 = S::kwins(0) + S::vwins(0) + 2 * kBm, kF1 = S::kwins(1) + S::vwins(1) + 2 * kBm;
+  constexpr int kF2 = S::kwins(2) + S::vwins(2) + 2 * kBm, kF3 = S::kwins(3) + S::vwins(3) + 2 * kBm;
+  // Mask words: copy i of wave w covers query rows 64 w + 32 i + lane / 2 of
+  // the tile, word lane % 2 of the key tile; row r lands at bytes 8 r.
+  auto fill_mask = [&](const i32x4& rm, int st, int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 64 * w + 32 * i + lane / 2;
+      fill4(rm, ms_l + st * S::MTILE + (64 * w + 32 * i) * 8,
+            (int)(((int64_t)r * p.mask_si + (k0 >> 5) + (lane & 1)) * 4));
+    }
+  };
+  auto mask_rsrc = [&](int64_t rows) { return rsrc_words(mbase + (int64_t)q0 * p.mask_si, rows * p.mask_si * 4); };
+  auto fill = [&](int kt, int st) {
+    const int k0 = kt * S::BK;
+    const i32x4 rk = rsrc_words(Kb + (int64_t)k0 * krow, (int64_t)(n - k0) * krow);
+    const i32x4 rv = rsrc_words(Vb + (int64_t)k0 * vrow, (int64_t)(n - k0) * vrow);
+#pragma unroll
+    for (int i = 0; i < S::KWIN; ++i)
+      if (S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS)
+        fill16(rk, ks_l + st * S::KTILE + (w + S::NW * i) * 1024, ksrc[i]);
+#pragma unroll
+    for (int i = 0; i < S::VWIN; ++i)
+      if (S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS)
+        fill16(rv, vs_l + st * S::VTILE + (w + S::NW * i) * 1024, vsrc[i]);
+    if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(n - q0), st, k0);
+  };
+  // The same copies split in two, for the fill issued inside a pipeline step:
+  // FK + FV windows that every wave copies (issued one per operand of the
+  // step's first phase) and the rest.  kt < 0 copies nothing (empty buffer
+  // ranges) but issues the same instructions, so that the per-wave counts hold.
+  constexpr int FK = S::KWINS / S::NW, FV = S::VWINS / S::NW;
+  static_assert(FK + FV <= S::NR, "one spread copy per first-phase operand at most");
+  i32x4 frk, frv;
+  int fst = 0;
+  auto fill_begin = [&](int kt, int st) {  // descriptors and the uneven rest
+    const int k0 = kt < 0 ? 0 : kt * S::BK;
+    const int64_t rows = kt < 0 ? 0 : n - k0;
+    frk = rsrc_words(Kb + (int64_t)k0 * krow, rows * krow);
+    frv = rsrc_words(Vb + (int64_t)k0 * vrow, rows * vrow);
+    fst = st;
+#pragma unroll
+    for (int i = FK; i < S::KWIN; ++i)
+      if (w + S::NW * i < S::KWINS) fill16(frk, ks_l + st * S::KTILE + (w + S::NW * i) * 1024, ksrc[i]);
+#pragma unroll
+    for (int i = FV; i < S::VWIN; ++i)
+      if (w + S::NW * i < S::VWINS) fill16(frv, vs_l + st * S::VTILE + (w + S::NW * i) * 1024, vsrc[i]);
+    if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(kt < 0 ? 0 : n - q0), st, k0);
+  };
+  auto fill_item = [&](int i) {  // i < FK + FV
+    if (i < FK) fill16(frk, ks_l + fst * S::KTILE + (w + S::NW * i) * 1024, ksrc[i]);
+    else fill16(frv, vs_l + fst * S::VTILE + (w + S::NW * (i - FK)) * 1024, vsrc[i - FK]);
+  };
+  // Wait until at most k of this wave's tile fills are still in flight.
+  auto wait_fills = [&](int k) {
+    if (k <= 0) {
+      wait_vm_n<0>();
+    } else if (k == 1) {
+      if (w == 0) wait_vm_n<kF0>();
+      else if (w == 1) wait_vm_n<kF1>();
+      else if (w == 2) wait_vm_n<kF2>();
+      else wait_vm_n<kF3>();
+    } else {
+      if (w == 0) wait_vm_n<2 * kF0>();
+      else if (w == 1) wait_vm_n<2 * kF1>();
+      else if (w == 2) wait_vm_n<2 * kF2>();
+      else wait_vm_n<2 * kF3>();
+    }
+  };
+
+  // ---- per-lane LDS read bases (everything else is a constant offset) -----
+  // Row operands (S^T, dP^T): A-operand lane m = lane % 32 of a 32-key chunk
+  // reads key row perm(m), 16-byte chunk 2 s + hh.
+  const int krb = perm(lane & 31) * S::KS + 16 * hh, vrb = perm(lane & 31) * S::VS + 16 * hh;
+  // Transposed operand (K^T): lane r of a 16-lane group gives the address of
+  // key row hh + 4 (r / 4) (+ 2 for the upper four contraction indices, + 16
+  // per key step), columns 32 blk + 16 g1 + 4 (r % 4): it then receives
+  // column 32 blk + 16 g1 + r of key rows hh, hh + 4, hh + 8, hh + 12, which
+  // are the rows perm() put at C rows 4 hh + 0..3 (resp. 8 + 4 hh + 0..3).
+  const int r16 = lane & 15;
+  const int ktb = (hh + 4 * (r16 >> 2)) * S::KS + 2 * (16 * g1 + 4 * (r16 & 3));
+
+  // Exponent scale: c log2(e), with c = 0 replaced by 1e-30 (every finite
+  // score then maps to exactly exp2(-L log2 e), as for c = 0, while the
+  // masking sentinel below still maps to zero).
+  const float scale2 = p.scale2 == 0.f ? 1e-30f : p.scale2;
+  const float masked_score = scale2 > 0.f ? -INFINITY : INFINITY;  // exp2(score * scale2 - l) = 0
+  // Partially allowed tile: scores of disallowed pairs -> the sentinel.
+  // Register r of a half holds C row m = 8 (r / 4) + 4 hh + r % 4, i.e. key
+  // row 32 c + perm(m) of the tile, for query qa + 32 u.
+  auto mask_chunk = [&](f32x16 (&sc)[2], int st, int c, int k0) {
+    const uint32_t* ms = reinterpret_cast<const uint32_t*>(mws + st * S::MTILE);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = qa + 32 * u;
+      uint32_t word = 0xFFFFFFFFu;
+      if constexpr (MASK == kMaskBitmask) word = ms[(64 * w + 32 * u + (lane & 31)) * S::MWORDS + c];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = perm(8 * (r >> 2) + 4 * hh + (r & 3));
+        const int key = k0 + 32 * c + kk;
+        bool ok = key < n;
+        if constexpr (MASK == kMaskCausal) ok = ok && key <= q;
+        if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> kk) & 1u);
+        sc[u][r] = ok ? sc[u][r] : masked_score;
+      }
+    }
+  };
+
+  // S^T and dP^T - D of one chunk (32 keys at tile row 32 c) from stage st.
+  auto score_products = [&](f32x16 (&sc)[2], f32x16 (&dp)[2], int st, int c) {
+    const char* kb = kts + st * S::KTILE + 32 * c * S::KS + krb;
+    const char* vb = vts + st * S::VTILE + 32 * c * S::VS + vrb;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sc[u] = f32x16{};
+      dp[u] = dinit[u];
+    }
+#pragma unroll
+    for (int s = 0; s < S::NQF; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 32 * s);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) sc[u] = mfma_bf16(a, qf[u][s], sc[u]);
+    }
+#pragma unroll
+    for (int s = 0; s < S::NVF; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + 32 * s);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dp[u] = mfma_bf16(a, of[u][s], dp[u]);
+    }
+  };
+
+  // One pipeline step for chunk (st, c): sc, dp hold its S^T and dP^T - D
+  // (masked); nsc, ndp receive those of the next chunk (stage nst, chunk nc),
+  // computed from whatever that stage holds (unused after the last chunk).
+  //   phase A: MFMA S^T, dP^T (next chunk)   || VALU P, dS (this chunk)
+  //   phase B: MFMA dQ^T (this chunk) with transposed K reads
+  auto step = [&](auto dofill, f32x16 (&sc)[2], f32x16 (&dp)[2], f32x16 (&nsc)[2], f32x16 (&ndp)[2], int st, int c,
+                  int nst, int nc) {
+    const char* nkb = kts + nst * S::KTILE + 32 * nc * S::KS + krb;
+    const char* nvb = vts + nst * S::VTILE + 32 * nc * S::VS + vrb;
+    const char* kb = kts + st * S::KTILE + 32 * c * S::KS + ktb;
+
+    // ---- phase A ----
+    constexpr int PF = kDqPrefetchA;  // row operands in flight
+    auto is_k = [](int i) { return ((i + 1) * S::NQF) / S::NR > (i * S::NQF) / S::NR; };
+    auto aread = [&](int i) -> bf16x8 {  // operand i: K (fragment si) or V, interleaved
+      const int si = (i * S::NQF) / S::NR;
+      if (is_k(i)) return *reinterpret_cast<const bf16x8*>(nkb + 32 * si);
+      return *reinterpret_cast<const bf16x8*>(nvb + 32 * (i - si));
+    };
+    bf16x8 afr[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) afr[i] = aread(i);
+    u32x4 sk[2][2];
+    // Weights of row pair pr (half pr / 8, registers 2 (pr % 8) and +1) in
+    // two halves, issued one slice apart so that the exponentials' latency
+    // is covered: e(pr) = exponentials, f(pr) = dS and the bf16 packing.
+    float pe[16][2];
+    auto weights_e = [&](int pr) {
+      const int u = pr >> 3, r = 2 * (pr & 7);
+      pe[pr][0] = fast_exp2(__builtin_fmaf(sc[u][r], scale2, -l2[u]));
+      pe[pr][1] = fast_exp2(__builtin_fmaf(sc[u][r + 1], scale2, -l2[u]));
+    };
+    auto weights_f = [&](int pr) {
+      const int u = pr >> 3, r = 2 * (pr & 7);
+      sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0] * dp[u][r], pe[pr][1] * dp[u][r + 1]);
+    };
+    // Slices 0..16 over the NR operands: slice k issues e(k) and f(k - 1).
+    constexpr int NSL = 17;
+#pragma unroll
+    for (int i = 0; i < S::NR; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int si = (i * S::NQF) / S::NR;
+      if (is_k(i)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) nsc[u] = mfma_bf16(afr[i % PF], qf[u][si], si == 0 ? f32x16{} : nsc[u]);
+      } else {
+        const int vi = i - si;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) ndp[u] = mfma_bf16(afr[i % PF], of[u][vi], vi == 0 ? dinit[u] : ndp[u]);
+      }
+      if (i + PF < S::NR) afr[i % PF] = aread(i + PF);
+      if constexpr (decltype(dofill)::value) {
+        if (i < FK + FV) fill_item(i);
+      }
+#pragma unroll
+      for (int k = i * NSL / S::NR; k < (i + 1) * NSL / S::NR; ++k) {
+        if (k < 16) weights_e(k);
+        if (k > 0) weights_f(k - 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase B ----
+    // Operand j: key step j / NDB, column block j % NDB; two MFMAs (halves).
+    auto bread = [&](int j, i16x4& lo, i16x4& hi) {
+      const int ks = j / S::NDB, blk = j % S::NDB;
+      lo = lds_read_tr(kb + 16 * ks * S::KS, 64 * blk);
+      hi = lds_read_tr(kb + (16 * ks + 2) * S::KS, 64 * blk);
+    };
+    constexpr int PB = kDqPrefetchB;  // transposed operands in flight
+    i16x4 tlo[PB], thi[PB];
+#pragma unroll
+    for (int j = 0; j < PB; ++j) bread(j, tlo[j], thi[j]);
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+      const int ks = j / S::NDB, blk = j % S::NDB;
+      const bf16x8 a = join_tr(tlo[j % PB], thi[j % PB]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dq[u][blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, sk[u][ks]), dq[u][blk]);
+      if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
+    }
+    // Two MFMAs, the reads PB operands ahead, per group.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PB, 0);
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      if (j + PB < S::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- main loop -------------------------------------------------------------
+  int t0 = 0;
+  if (MASK == kMaskBitmask) {
+    __syncthreads();  // tile classes staged
+    if (t0 < kt_end && tile_class(t0) == kTileEmpty) t0 = next_tile(t0);
+  }
+  if (t0 >= kt_end) t0 = -1;
+  int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
+  if (t0 >= 0) {  // workgroup-uniform
+    int issued = 0;
+    fill(t0, 0);
+    ++issued;
+    if (t1 >= 0) { fill(t1, 1); ++issued; }
+    if (t2 >= 0) { fill(t2, 2); ++issued; }
+    wait_fills(issued - 1);
+    __syncthreads();
+    f32x16 sa[2], pa[2], sb[2], pb[2];
+    score_products(sa, pa, 0, 0);
+    int j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
+    while (true) {
+      const int st = j % S::NSTAGE, nst = (j + 1) % S::NSTAGE;
+      const int k0 = t0 * S::BK;
+      const bool partial = tile_class(t0) == kTilePartial;
+      // chunk 0 of t0
+      if (partial) mask_chunk(sa, st, 0, k0);
+      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1);
+      // The next tile's stage must be complete and visible before chunk 1's
+      // phase A reads it; after this barrier every wave is past tile j-1, so
+      // its stage takes the fill of position j+3 (empty past the last tile),
+      // spread over chunk 1's first phase.
+      wait_fills(issued - (j + 2 < issued ? j + 2 : issued));
+      __syncthreads();
+      fill_begin(t3, (j + 3) % S::NSTAGE);
+      ++issued;
+      // chunk 1 of t0
+      if (partial) mask_chunk(sb, st, 1, k0);
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0);
+      if (t1 < 0) break;
+      t0 = t1;
+      t1 = t2;
+      t2 = t3;
+      t3 = next_tile(t2);
+      ++j;
+    }
+    wait_vm_n<0>();  // copies of empty positions
+  }
+
+  // Epilogue: dQ = c dQ^T (lane = query; 4 consecutive columns per store).
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = qa + 32 * u;
+    if (q < n) {
+      char* dQp = (char*)p.dQ + ((int64_t)b * p.sq[0] + (int64_t)h * p.sq[1] + (int64_t)q * p.sq[2]) * 2;
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = db * 32 + 8 * g + 4 * hh;
+          const float x0 = dq[u][db][4 * g] * p.scale, x1 = dq[u][db][4 * g + 1] * p.scale;
+          const float x2 = dq[u][db][4 * g + 2] * p.scale, x3 = dq[u][db][4 * g + 3] * p.scale;
+          *reinterpret_cast<u32x2*>(dQp + c0 * 2) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+    }
+  }
+}
+
+template <int D, int DV, int MASK>
+static int launch_dq_pipe(const BwdParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, DV, MASK>), dim3((unsigned)p.grid_pad_dq), dim3(256), 0, st, p);
+  return (int)hipGetLastError();
+}
+
+template <int D, int DV>
+static int launch_dq_pipe_mask(const BwdParams& p, int mask_mode, hipStream_t st) {
+  switch (mask_mode) {
+    case kMaskNone: return launch_dq_pipe<D, DV, kMaskNone>(p, st);
+    case kMaskCausal: return launch_dq_pipe<D, DV, kMaskCausal>(p, st);
+    default: return launch_dq_pipe<D, DV, kMaskBitmask>(p, st);
+  }
+}
+
+int launch_bwd_dq_pipe(const BwdParams& p, int d, int v, int mask_mode, void* stream) {
+  static_assert(DqPipeShape<128, 128>::MAXTK == kDqPipeMaxTk, "staged tile classes");
+  hipStream_t st = (hipStream_t)stream;
+  if (d == 128 && v == 128) return launch_dq_pipe_mask<128, 128>(p, mask_mode, st);
+  if (d == 64 && v == 128) return launch_dq_pipe_mask<64, 128>(p, mask_mode, st);
+  if (d == 64 && v == 64) return launch_dq_pipe_mask<64, 64>(p, mask_mode, st);
+  if (d == 128 && v == 64) return launch_dq_pipe_mask<128, 64>(p, mask_mode, st);
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace eta

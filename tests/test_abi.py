@@ -91,9 +91,12 @@ def test_workspace_formula():
     assert st == 0 and fw == (8 * 64 * 128 + 255) // 256 * 256
     st, bw = wsize(p, 1)
     assert bw == 2 * 4 * 16 * 8192 + 4 * 16 * 8192 * 64 + 8 * 128 * 64
-    p.deterministic = 1  # D, L2 + key-tile-outer map (64 x 128 tiles) + dQ map (128 x 32 tiles)
+    p.deterministic = 1  # D, L2 + key-tile-outer map (64 x 128 tiles) + dQ map (256 x 64 tiles)
     st, bw = wsize(p, 1)
-    assert bw == 2 * 4 * 16 * 8192 + 8 * 128 * 64 + 8 * 64 * 256
+    assert bw == 2 * 4 * 16 * 8192 + 8 * 128 * 64 + 8 * 32 * 128
+    p.dtype = 0  # fp32: key-tile-outer map at 32 x 128 tiles, dQ map at 128 x 32 tiles
+    st, bw = wsize(p, 1)
+    assert bw == 2 * 4 * 16 * 8192 + 8 * 256 * 64 + 8 * 64 * 256
 
 
 @pytest.mark.parametrize("mut,status", [
