@@ -1,4 +1,4 @@
-// Backward, query-tile-outer dQ kernel for bf16 with d, v in {64, 128}: the
+// Backward, query-tile-outer dQ kernel for bf16 with (d, v) = (128, 128), (64, 128) or (64, 64): the
 // second kernel of the deterministic backward (dK and dV come from the
 // key-tile-outer kernel).
 //
@@ -14,8 +14,10 @@
 //
 // gfx950 design.  One workgroup per CU; each of its 4 waves owns 64 queries
 // as two halves of 32 (lane column = query) and keeps their Q and dO rows in
-// registers as MFMA B operands and their dQ^T accumulators in AGPRs, so L_i
-// and D_i are per-lane constants.  Key tiles of 64 rows are processed as two
+// AGPRs as MFMA B operands and their dQ^T accumulators in AGPRs, so L_i and
+// D_i are per-lane constants; the score accumulators live in VGPRs, where
+// the vector ALUs read them without copies (MFMAs written as inline
+// assembly with explicit register classes).  Key tiles of 64 rows are processed as two
 // chunks of 32 keys.  Per chunk, S^T = K Q^T and dP^T = V dO^T: every K or V
 // row operand read from LDS feeds the MFMAs of both halves, and the dP^T
 // accumulators start from -D_i, so that they come out as dP - D.  The vector
@@ -48,6 +50,29 @@ namespace eta {
 // LDS operand prefetch depth, in operands (each feeds two MFMAs), of the two phases.
 constexpr int kDqPrefetchA = ETA_DQ_PREFETCH_A, kDqPrefetchB = ETA_DQ_PREFETCH_B;
 
+// MFMAs with explicit operand register classes: the score products keep
+// their accumulators in VGPRs (read directly by the vector ALUs) and take
+// the Q / dO fragments from AGPRs; the dQ^T products accumulate in AGPRs.
+// The compiler does not see inside these statements, so the wait states
+// around them are kept by construction: every score result is read at
+// least one 16-MFMA phase after it is written (explicit s_nop after the
+// prologue's products), the packed dS operands are written two or more
+// instructions before their first use, and accumulation chains use the
+// same registers for the accumulator and the result.
+__device__ __forceinline__ void mfma_vz(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vc(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
+__device__ __forceinline__ void mfma_vacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_aacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void nops_after_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+
 template <int D, int DV>
 struct DqPipeShape {
   static constexpr int NW = 4;
@@ -63,10 +88,9 @@ struct DqPipeShape {
   static constexpr int KS = KT::kStride, VS = VT::kStride;
   static constexpr int KTILE = BK * KS, VTILE = BK * VS;
   static constexpr int KWINS = KTILE / 1024, VWINS = VTILE / 1024;  // 1 KB fill windows per tile
-  // Windows of wave w: w, w + NW, ... (the counts differ by wave).
+  // Windows of wave w: w, w + NW, ... (KWIN per wave; a wave past the last
+  // window copies an empty range into a spare window instead).
   static constexpr int KWIN = (KWINS + NW - 1) / NW, VWIN = (VWINS + NW - 1) / NW;
-  static constexpr int kwins(int w) { return (KWINS - w + NW - 1) / NW; }
-  static constexpr int vwins(int w) { return (VWINS - w + NW - 1) / NW; }
   static constexpr int MWORDS = BK / 32;         // bitmask words per query row and tile
   static constexpr int MTILE = BQ * MWORDS * 4;  // bitmask bytes per stage
   static constexpr int MAXTK = 4096;             // bitmask: key tiles whose classes are staged in LDS
@@ -82,6 +106,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char vts[S::NSTAGE * S::VTILE];
   __shared__ __attribute__((aligned(16))) char mws[MASK == kMaskBitmask ? S::NSTAGE * S::MTILE : 16];
   __shared__ uint8_t cls_s[MASK == kMaskBitmask ? S::MAXTK : 1];
+  __shared__ __attribute__((aligned(1024))) char spare[1024];  // target of the padding copies
 
   const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad_dq, p.total_dq);
   if (logical < 0) return;
@@ -179,11 +204,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // groups of 16 rows taken in transposed order, 4 u + v -> u + 4 v.
   auto perm = [](int l) { return (l & ~15) + ((l & 15) >> 2) + 4 * (l & 3); };
   const uint32_t ks_l = lds_address(kts), vs_l = lds_address(vts), ms_l = lds_address(mws);
-  // Per tile, wave w issues kwins(w) + vwins(w) tile copies and, with a
-  // bitmask, two more (mask words of 32 query rows each).
+  const uint32_t sp_l = lds_address(spare);
+  // Per tile every wave issues KWIN + VWIN copies (a wave without a last
+  // window copies an empty range into the spare window) and, with a bitmask,
+  // two more (mask words of 32 query rows each).
   constexpr int kBm = MASK == kMaskBitmask;
-  constexpr int kF0 = S::kwins(0) + S::vwins(0) + 2 * kBm, kF1 = S::kwins(1) + S::vwins(1) + 2 * kBm;
-  constexpr int kF2 = S::kwins(2) + S::vwins(2) + 2 * kBm, kF3 = S::kwins(3) + S::vwins(3) + 2 * kBm;
+  constexpr int kF = S::KWIN + S::VWIN + 2 * kBm;
+  const i32x4 r_none = rsrc_words(Kb, 0);
   // Mask words: copy i of wave w covers query rows 64 w + 32 i + lane / 2 of
   // the tile, word lane % 2 of the key tile; row r lands at bytes 8 r.
   auto fill_mask = [&](const i32x4& rm, int st, int k0) {
@@ -195,26 +222,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     }
   };
   auto mask_rsrc = [&](int64_t rows) { return rsrc_words(mbase + (int64_t)q0 * p.mask_si, rows * p.mask_si * 4); };
-  auto fill = [&](int kt, int st) {
-    const int k0 = kt * S::BK;
-    const i32x4 rk = rsrc_words(Kb + (int64_t)k0 * krow, (int64_t)(n - k0) * krow);
-    const i32x4 rv = rsrc_words(Vb + (int64_t)k0 * vrow, (int64_t)(n - k0) * vrow);
+  // Window i of K (V) for wave w, or the spare window with an empty range.
+  auto kwin = [&](const i32x4& rk, int st, int i) {
+    const bool real = S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS;
+    fill16(real ? rk : r_none, real ? ks_l + st * S::KTILE + (w + S::NW * i) * 1024 : sp_l, ksrc[i]);
+  };
+  auto vwin = [&](const i32x4& rv, int st, int i) {
+    const bool real = S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS;
+    fill16(real ? rv : r_none, real ? vs_l + st * S::VTILE + (w + S::NW * i) * 1024 : sp_l, vsrc[i]);
+  };
+  auto fill = [&](int kt, int st) {  // kt < 0: empty ranges, same instructions
+    const int k0 = kt < 0 ? 0 : kt * S::BK;
+    const int64_t rows = kt < 0 ? 0 : n - k0;
+    const i32x4 rk = rsrc_words(Kb + (int64_t)k0 * krow, rows * krow);
+    const i32x4 rv = rsrc_words(Vb + (int64_t)k0 * vrow, rows * vrow);
 #pragma unroll
-    for (int i = 0; i < S::KWIN; ++i)
-      if (S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS)
-        fill16(rk, ks_l + st * S::KTILE + (w + S::NW * i) * 1024, ksrc[i]);
+    for (int i = 0; i < S::KWIN; ++i) kwin(rk, st, i);
 #pragma unroll
-    for (int i = 0; i < S::VWIN; ++i)
-      if (S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS)
-        fill16(rv, vs_l + st * S::VTILE + (w + S::NW * i) * 1024, vsrc[i]);
-    if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(n - q0), st, k0);
+    for (int i = 0; i < S::VWIN; ++i) vwin(rv, st, i);
+    if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(kt < 0 ? 0 : n - q0), st, k0);
   };
   // The same copies split in two, for the fill issued inside a pipeline step:
   // FK + FV windows that every wave copies (issued one per operand of the
   // step's first phase) and the rest.  kt < 0 copies nothing (empty buffer
   // ranges) but issues the same instructions, so that the per-wave counts hold.
   constexpr int FK = S::KWINS / S::NW, FV = S::VWINS / S::NW;
-  static_assert(FK + FV <= S::NR, "one spread copy per first-phase operand at most");
+  static_assert(4 * (FK + FV) <= 2 * S::NR, "one spread copy per four first-phase MFMAs at most");
   i32x4 frk, frv;
   int fst = 0;
   auto fill_begin = [&](int kt, int st) {  // descriptors and the uneven rest
@@ -224,34 +257,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     frv = rsrc_words(Vb + (int64_t)k0 * vrow, rows * vrow);
     fst = st;
 #pragma unroll
-    for (int i = FK; i < S::KWIN; ++i)
-      if (w + S::NW * i < S::KWINS) fill16(frk, ks_l + st * S::KTILE + (w + S::NW * i) * 1024, ksrc[i]);
+    for (int i = FK; i < S::KWIN; ++i) kwin(frk, st, i);
 #pragma unroll
-    for (int i = FV; i < S::VWIN; ++i)
-      if (w + S::NW * i < S::VWINS) fill16(frv, vs_l + st * S::VTILE + (w + S::NW * i) * 1024, vsrc[i]);
+    for (int i = FV; i < S::VWIN; ++i) vwin(frv, st, i);
     if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(kt < 0 ? 0 : n - q0), st, k0);
   };
   auto fill_item = [&](int i) {  // i < FK + FV
     if (i < FK) fill16(frk, ks_l + fst * S::KTILE + (w + S::NW * i) * 1024, ksrc[i]);
     else fill16(frv, vs_l + fst * S::VTILE + (w + S::NW * (i - FK)) * 1024, vsrc[i - FK]);
   };
-  // Wait until at most k of this wave's tile fills are still in flight.
-  auto wait_fills = [&](int k) {
-    if (k <= 0) {
-      wait_vm_n<0>();
-    } else if (k == 1) {
-      if (w == 0) wait_vm_n<kF0>();
-      else if (w == 1) wait_vm_n<kF1>();
-      else if (w == 2) wait_vm_n<kF2>();
-      else wait_vm_n<kF3>();
-    } else {
-      if (w == 0) wait_vm_n<2 * kF0>();
-      else if (w == 1) wait_vm_n<2 * kF1>();
-      else if (w == 2) wait_vm_n<2 * kF2>();
-      else wait_vm_n<2 * kF3>();
-    }
-  };
-
   // ---- per-lane LDS read bases (everything else is a constant offset) -----
   // Row operands (S^T, dP^T): A-operand lane m = lane % 32 of a 32-key chunk
   // reads key row perm(m), 16-byte chunk 2 s + hh.
@@ -296,22 +310,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     const char* kb = kts + st * S::KTILE + 32 * c * S::KS + krb;
     const char* vb = vts + st * S::VTILE + 32 * c * S::VS + vrb;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      sc[u] = f32x16{};
-      dp[u] = dinit[u];
-    }
-#pragma unroll
     for (int s = 0; s < S::NQF; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 32 * s);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) sc[u] = mfma_bf16(a, qf[u][s], sc[u]);
+      for (int u = 0; u < 2; ++u) {
+        if (s == 0) mfma_vz(sc[u], a, qf[u][s]);
+        else mfma_vacc(sc[u], a, qf[u][s]);
+      }
     }
 #pragma unroll
     for (int s = 0; s < S::NVF; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + 32 * s);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) dp[u] = mfma_bf16(a, of[u][s], dp[u]);
+      for (int u = 0; u < 2; ++u) {
+        if (s == 0) mfma_vc(dp[u], a, of[u][s], dinit[u]);
+        else mfma_vacc(dp[u], a, of[u][s]);
+      }
     }
+    nops_after_mfma();
   };
 
   // One pipeline step for chunk (st, c): sc, dp hold its S^T and dP^T - D
@@ -338,42 +354,54 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     for (int i = 0; i < PF; ++i) afr[i] = aread(i);
     u32x4 sk[2][2];
     // Weights of row pair pr (half pr / 8, registers 2 (pr % 8) and +1) in
-    // two halves, issued one slice apart so that the exponentials' latency
-    // is covered: e(pr) = exponentials, f(pr) = dS and the bf16 packing.
-    float pe[16][2];
-    auto weights_e = [&](int pr) {
+    // three stages, so that each exponential's latency is covered by later
+    // work: w1 = both exponents and the first exponential, w2 = the second
+    // exponential, w3 = dS and the bf16 packing.
+    float pt[16], pe[16][2];
+    auto w1 = [&](int pr) {
       const int u = pr >> 3, r = 2 * (pr & 7);
       pe[pr][0] = fast_exp2(__builtin_fmaf(sc[u][r], scale2, -l2[u]));
-      pe[pr][1] = fast_exp2(__builtin_fmaf(sc[u][r + 1], scale2, -l2[u]));
+      pt[pr] = __builtin_fmaf(sc[u][r + 1], scale2, -l2[u]);
     };
-    auto weights_f = [&](int pr) {
+    auto w2 = [&](int pr) { pe[pr][1] = fast_exp2(pt[pr]); };
+    auto w3 = [&](int pr) {
       const int u = pr >> 3, r = 2 * (pr & 7);
       sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0] * dp[u][r], pe[pr][1] * dp[u][r + 1]);
     };
-    // Slices 0..16 over the NR operands: slice k issues e(k) and f(k - 1).
-    constexpr int NSL = 17;
+    // Work items in issue order: w1(k), w2(k), w3(k - 1) for k = 0..15, then
+    // w3(15); item t goes to sub-slice t * NSUB / NITEM.
+    constexpr int NSUB = 2 * S::NR, NITEM = 3 * 16;
+    auto item = [&](int t) {
+      const int k = t / 3, st3 = t % 3;
+      if (st3 == 0) w1(k);
+      else if (st3 == 1) w2(k);
+      else if (k > 0) w3(k - 1);
+    };
+    // Sub-slice m: one MFMA (operand m / 2, half m % 2) and its share of the
+    // vector work; the second sub-slice of an operand issues the prefetch
+    // read, every fourth sub-slice one tile copy.
 #pragma unroll
-    for (int i = 0; i < S::NR; ++i) {
+    for (int m = 0; m < NSUB; ++m) {
       __builtin_amdgcn_sched_barrier(0);
+      const int i = m / 2, u = m % 2;
       const int si = (i * S::NQF) / S::NR;
       if (is_k(i)) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) nsc[u] = mfma_bf16(afr[i % PF], qf[u][si], si == 0 ? f32x16{} : nsc[u]);
+        if (si == 0) mfma_vz(nsc[u], afr[i % PF], qf[u][si]);
+        else mfma_vacc(nsc[u], afr[i % PF], qf[u][si]);
       } else {
         const int vi = i - si;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) ndp[u] = mfma_bf16(afr[i % PF], of[u][vi], vi == 0 ? dinit[u] : ndp[u]);
+        if (vi == 0) mfma_vc(ndp[u], afr[i % PF], of[u][vi], dinit[u]);
+        else mfma_vacc(ndp[u], afr[i % PF], of[u][vi]);
       }
-      if (i + PF < S::NR) afr[i % PF] = aread(i + PF);
+      if (u == 1 && i + PF < S::NR) afr[i % PF] = aread(i + PF);
       if constexpr (decltype(dofill)::value) {
-        if (i < FK + FV) fill_item(i);
+        if (m % 4 == 1 && m / 4 < FK + FV) fill_item(m / 4);
       }
 #pragma unroll
-      for (int k = i * NSL / S::NR; k < (i + 1) * NSL / S::NR; ++k) {
-        if (k < 16) weights_e(k);
-        if (k > 0) weights_f(k - 1);
-      }
+      for (int t = (m * NITEM + NSUB - 1) / NSUB; t < ((m + 1) * NITEM + NSUB - 1) / NSUB; ++t) item(t);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    w3(15);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- phase B ----
@@ -387,20 +415,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     i16x4 tlo[PB], thi[PB];
 #pragma unroll
     for (int j = 0; j < PB; ++j) bread(j, tlo[j], thi[j]);
+    asm volatile("s_nop 1");  // the last packed dS operands were just written
+    // Slice j: two MFMAs (halves) and the reads PB operands ahead.
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
       const int ks = j / S::NDB, blk = j % S::NDB;
       const bf16x8 a = join_tr(tlo[j % PB], thi[j % PB]);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) dq[u][blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, sk[u][ks]), dq[u][blk]);
+      for (int u = 0; u < 2; ++u) mfma_aacc(dq[u][blk], a, __builtin_bit_cast(bf16x8, sk[u][ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
-    }
-    // Two MFMAs, the reads PB operands ahead, per group.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PB, 0);
-#pragma unroll
-    for (int j = 0; j < S::NB; ++j) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-      if (j + PB < S::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -414,12 +438,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   if (t0 >= kt_end) t0 = -1;
   int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
   if (t0 >= 0) {  // workgroup-uniform
-    int issued = 0;
     fill(t0, 0);
-    ++issued;
-    if (t1 >= 0) { fill(t1, 1); ++issued; }
-    if (t2 >= 0) { fill(t2, 2); ++issued; }
-    wait_fills(issued - 1);
+    fill(t1, 1);
+    fill(t2, 2);
+    wait_vm_n<2 * kF>();
     __syncthreads();
     f32x16 sa[2], pa[2], sb[2], pb[2];
     score_products(sa, pa, 0, 0);
@@ -435,10 +457,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3 (empty past the last tile),
       // spread over chunk 1's first phase.
-      wait_fills(issued - (j + 2 < issued ? j + 2 : issued));
+      wait_vm_n<kF>();
       __syncthreads();
       fill_begin(t3, (j + 3) % S::NSTAGE);
-      ++issued;
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, k0);
       step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0);
@@ -451,6 +472,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     }
     wait_vm_n<0>();  // copies of empty positions
   }
+  nops_after_mfma();  // the last dQ^T products were just issued
 
   // Epilogue: dQ = c dQ^T (lane = query; 4 consecutive columns per store).
 #pragma unroll
@@ -492,7 +514,6 @@ int launch_bwd_dq_pipe(const BwdParams& p, int d, int v, int mask_mode, void* st
   if (d == 128 && v == 128) return launch_dq_pipe_mask<128, 128>(p, mask_mode, st);
   if (d == 64 && v == 128) return launch_dq_pipe_mask<64, 128>(p, mask_mode, st);
   if (d == 64 && v == 64) return launch_dq_pipe_mask<64, 64>(p, mask_mode, st);
-  if (d == 128 && v == 64) return launch_dq_pipe_mask<128, 64>(p, mask_mode, st);
   return (int)hipErrorInvalidValue;
 }
 

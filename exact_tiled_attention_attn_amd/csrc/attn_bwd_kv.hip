@@ -494,7 +494,7 @@ static int launch_kv_mask(const BwdParams& p, int mask_mode, hipStream_t st) {
 }
 
 bool bwd_kv_supported(int bf16, int d, int v, int mask_mode, int64_t tq) {
-  if (!bf16 || !((d == 64 || d == 128) && (v == 64 || v == 128))) return false;
+  if (!bf16 || !((d == 128 && v == 128) || (d == 64 && v == 128) || (d == 64 && v == 64))) return false;
   return mask_mode != kMaskBitmask || tq <= KvShape<128, 128>::MAXTQ;
 }
 
@@ -503,7 +503,6 @@ int launch_bwd_kv(const BwdParams& p, int d, int v, int mask_mode, void* stream)
   if (d == 128 && v == 128) return launch_kv_mask<128, 128>(p, mask_mode, st);
   if (d == 64 && v == 128) return launch_kv_mask<64, 128>(p, mask_mode, st);
   if (d == 64 && v == 64) return launch_kv_mask<64, 64>(p, mask_mode, st);
-  if (d == 128 && v == 64) return launch_kv_mask<128, 64>(p, mask_mode, st);
   return (int)hipErrorInvalidValue;
 }
 

@@ -16,7 +16,7 @@ constexpr int kBwdBk = 128;
 // Backward dQ (query-tile outer): the forward's tiling.
 constexpr int kDqBq = 128;
 constexpr int kDqBk = 32;
-// Pipelined dQ kernel (bf16, d and v in {64, 128}): 256-query tiles, 64-key
+// Pipelined dQ kernel (bf16, (d, v) = (128, 128), (64, 128) or (64, 64)): 256-query tiles, 64-key
 // tiles; with a bitmask at most kDqPipeMaxTk key tiles per row.
 constexpr int kDqPipeBq = 256;
 constexpr int kDqPipeBk = 64;
@@ -96,7 +96,7 @@ int launch_bwd_kv(const BwdParams& p, int d, int v, int mask_mode, void* stream)
 // Pipelined dQ kernel of the deterministic path; the tiling of the dQ pass
 // (and of its bitmask tile map) follows this choice.
 inline bool bwd_dq_pipe_supported(int bf16, int64_t d, int64_t v, int mask_mode, int64_t n) {
-  if (!bf16 || !((d == 64 || d == 128) && (v == 64 || v == 128))) return false;
+  if (!bf16 || !((d == 128 && v == 128) || (d == 64 && v == 128) || (d == 64 && v == 64))) return false;
   return mask_mode != 2 || (n + kDqPipeBk - 1) / kDqPipeBk <= kDqPipeMaxTk;
 }
 int launch_bwd_dq_pipe(const BwdParams& p, int d, int v, int mask_mode, void* stream);
