@@ -50,28 +50,15 @@ namespace eta {
 // LDS operand prefetch depth, in operands (each feeds two MFMAs), of the two phases.
 constexpr int kDqPrefetchA = ETA_DQ_PREFETCH_A, kDqPrefetchB = ETA_DQ_PREFETCH_B;
 
-// MFMAs with explicit operand register classes: the score products keep
-// their accumulators in VGPRs (read directly by the vector ALUs) and take
-// the Q / dO fragments from AGPRs; the dQ^T products accumulate in AGPRs.
-// The compiler does not see inside these statements, so the wait states
-// around them are kept by construction: every score result is read at
-// least one 16-MFMA phase after it is written (explicit s_nop after the
+// The score products use the explicit-register MFMAs of kern_common.h: their
+// accumulators live in VGPRs (read directly by the vector ALUs) and their Q /
+// dO operands in AGPRs; the dQ^T products accumulate in AGPRs.  Wait states
+// the compiler cannot see are kept by construction: every score result is
+// read at least one 16-MFMA phase after it is written (s_nop after the
 // prologue's products), the packed dS operands are written two or more
-// instructions before their first use, and accumulation chains use the
-// same registers for the accumulator and the result.
-__device__ __forceinline__ void mfma_vz(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_vc(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
-}
-__device__ __forceinline__ void mfma_vacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_aacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void nops_after_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+// instructions before their first use (s_nop 1 at the start of the second
+// phase), and accumulation chains use the same registers for the
+// accumulator and the result.
 
 template <int D, int DV>
 struct DqPipeShape {

@@ -1,4 +1,4 @@
-// Backward, key-tile-outer dK / dV kernel for bf16 with d, v in {64, 128}:
+// Backward, key-tile-outer dK / dV kernel for bf16 with (d, v) = (128, 128), (64, 128) or (64, 64):
 // the main kernel of the deterministic backward (dQ comes from the
 // query-tile-outer kernel).
 //
@@ -11,8 +11,13 @@
 // tiles are masked (ob1 page, part 3).
 //
 // gfx950 design.  One workgroup (one per CU) owns 128 keys, 32 per wave; a
-// wave keeps its K and V rows in registers as MFMA B operands and its dK^T,
-// dV^T accumulators for the whole loop over query tiles.  Query tiles of 64
+// wave keeps its K and V rows in AGPRs as MFMA B operands and its dK^T,
+// dV^T accumulators in AGPRs for the whole loop over query tiles, while the
+// S / dP accumulators live in VGPRs, where the vector ALUs read them without
+// copies (explicit-register MFMAs of kern_common.h; their wait states are
+// kept by construction: scores are read one 16-MFMA phase after they are
+// written, s_nop after the prologue's products and before the epilogue, the
+// packed P / dS operands written before the second phase's first read).  Query tiles of 64
 // rows are visited from the last one down and processed as two chunks of 32
 // rows.  Per chunk, S = Q K^T and dP = dO V^T put one key in each lane
 // column, so the registers holding P and dS are directly the B operand of
@@ -59,10 +64,9 @@ struct KvShape {
   static constexpr int QS = QT::kStride, OS = OT::kStride;
   static constexpr int QTILE = BQ * QS, OTILE = BQ * OS;
   static constexpr int QWINS = QTILE / 1024, OWINS = OTILE / 1024;  // 1 KB fill windows per tile
-  // Windows of wave w: w, w + NW, ... (the counts differ by wave).
+  // Windows of wave w: w, w + NW, ... (QWIN / OWIN per wave; a wave past the
+  // last window copies an empty range into a spare window instead).
   static constexpr int QWIN = (QWINS + NW - 1) / NW, OWIN = (OWINS + NW - 1) / NW;
-  static constexpr int qwins(int w) { return (QWINS - w + NW - 1) / NW; }
-  static constexpr int owins(int w) { return (OWINS - w + NW - 1) / NW; }
   static constexpr int MWORDS = BK / 32;
   // Per stage: L log2(e) [BQ], D [BQ], mask words [BQ][MWORDS].
   static constexpr int LD_L = 0, LD_D = BQ * 4, LD_M = 2 * BQ * 4;
@@ -79,6 +83,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char os[S::NSTAGE * S::OTILE];
   __shared__ __attribute__((aligned(16))) char lds_ld[S::NSTAGE * S::LDB];
   __shared__ uint8_t cls_s[MASK == kMaskBitmask ? S::MAXTQ : 1];
+  __shared__ __attribute__((aligned(1024))) char spare[1024];  // target of the padding copies
 
   const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad, p.total);
   if (logical < 0) return;
@@ -164,39 +169,50 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // transposed order, 4 u + v -> u + 4 v.
   auto perm = [](int l) { return (l & ~15) + ((l & 15) >> 2) + 4 * (l & 3); };
   const uint32_t qs_l = lds_address(qs), os_l = lds_address(os), ld_l = lds_address(lds_ld);
-  // Per tile, wave w issues qwins(w) + owins(w) tile fills, waves 0 / 1 one
-  // more (L log2(e) / D rows), and with a bitmask every wave one more (mask
-  // words of 16 query rows).
+  const uint32_t sp_l = lds_address(spare);
+  // Per tile every wave issues QWIN + OWIN tile copies (a wave past the last
+  // window copies an empty range into the spare window), one row copy (L
+  // log2(e) rows by wave 0, D rows by wave 1, empty ranges by the others)
+  // and, with a bitmask, one more (mask words of 16 query rows).
   constexpr int kBm = MASK == kMaskBitmask;
-  constexpr int kF0 = S::qwins(0) + S::owins(0) + 1 + kBm, kF1 = S::qwins(1) + S::owins(1) + 1 + kBm;
-  constexpr int kF2 = S::qwins(2) + S::owins(2) + kBm, kF3 = S::qwins(3) + S::owins(3) + kBm;
-  auto fill = [&](int qt, int st) {
-    const int q0 = qt * S::BQ;
-    const i32x4 rq = rsrc_words(Qb + (int64_t)q0 * qrow, (int64_t)(n - q0) * qrow);
-    const i32x4 ro = rsrc_words(dOb + (int64_t)q0 * orow, (int64_t)(n - q0) * orow);
-#pragma unroll
-    for (int i = 0; i < S::QWIN; ++i)
-      if (S::QWINS % S::NW == 0 || w + S::NW * i < S::QWINS)
-        fill16(rq, qs_l + st * S::QTILE + (w + S::NW * i) * 1024, qsrc[i]);
-#pragma unroll
-    for (int i = 0; i < S::OWIN; ++i)
-      if (S::OWINS % S::NW == 0 || w + S::NW * i < S::OWINS)
-        fill16(ro, os_l + st * S::OTILE + (w + S::NW * i) * 1024, osrc[i]);
-    if (w < 2) {  // padded rows: always in range; slot l holds row perm(l)
-      const float* src = (w == 0 ? L2b : Db) + q0;
-      fill4(rsrc_words(src, S::BQ * 4), ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D), 4 * perm(lane));
-    }
+  constexpr int kF = S::QWIN + S::OWIN + 1 + kBm;
+  const i32x4 r_none = rsrc_words(Qb, 0);
+  auto qwin = [&](const i32x4& rq, int st, int i) {
+    const bool real = S::QWINS % S::NW == 0 || w + S::NW * i < S::QWINS;
+    fill16(real ? rq : r_none, real ? qs_l + st * S::QTILE + (w + S::NW * i) * 1024 : sp_l, qsrc[i]);
+  };
+  auto owin = [&](const i32x4& ro, int st, int i) {
+    const bool real = S::OWINS % S::NW == 0 || w + S::NW * i < S::OWINS;
+    fill16(real ? ro : r_none, real ? os_l + st * S::OTILE + (w + S::NW * i) * 1024 : sp_l, osrc[i]);
+  };
+  // The rest of a tile's copies (row statistics, mask words); qt < 0 copies
+  // nothing (empty buffer ranges) but issues the same instructions.
+  auto fill_rows = [&](int qt, int st) {
+    const int q0 = qt < 0 ? 0 : qt * S::BQ;
+    const bool rows_real = w < 2 && qt >= 0;  // padded rows: always in range; slot l holds row perm(l)
+    const float* src = (w == 0 ? L2b : Db) + q0;
+    fill4(rows_real ? rsrc_words(src, S::BQ * 4) : r_none,
+          w < 2 ? ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D) : sp_l, 4 * perm(lane));
     if constexpr (MASK == kMaskBitmask) {
       // Row 16 w + lane / 4 of the tile, word lane % 4 of this key tile.
       const int r = 16 * w + lane / 4;
-      const i32x4 rm = rsrc_words(mbase + (int64_t)q0 * p.mask_si, (int64_t)(n - q0) * p.mask_si * 4);
+      const i32x4 rm = rsrc_words(mbase + (int64_t)q0 * p.mask_si, qt < 0 ? 0 : (int64_t)(n - q0) * p.mask_si * 4);
       fill4(rm, ld_l + st * S::LDB + S::LD_M + 256 * w, (int)(((int64_t)r * p.mask_si + (k0 >> 5) + (lane & 3)) * 4));
     }
   };
+  auto fill = [&](int qt, int st) {
+    const int q0 = qt < 0 ? 0 : qt * S::BQ;
+    const int64_t rows = qt < 0 ? 0 : n - q0;
+    const i32x4 rq = rsrc_words(Qb + (int64_t)q0 * qrow, rows * qrow);
+    const i32x4 ro = rsrc_words(dOb + (int64_t)q0 * orow, rows * orow);
+#pragma unroll
+    for (int i = 0; i < S::QWIN; ++i) qwin(rq, st, i);
+#pragma unroll
+    for (int i = 0; i < S::OWIN; ++i) owin(ro, st, i);
+    fill_rows(qt, st);
+  };
   // The same copies split in two, for the fill issued inside a pipeline step:
-  // FQ + FO windows that every wave copies (issued one per MFMA of the step's
-  // first phase) and the rest.  qt < 0 copies nothing (empty buffer ranges)
-  // but issues the same instructions, so that the per-wave counts hold.
+  // FQ + FO windows (issued one per MFMA of the step's first phase) and the rest.
   constexpr int FQ = S::QWINS / S::NW, FO = S::OWINS / S::NW;
   i32x4 frq, fro;
   int fst = 0;
@@ -207,42 +223,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     fro = rsrc_words(dOb + (int64_t)q0 * orow, rows * orow);
     fst = st;
 #pragma unroll
-    for (int i = FQ; i < S::QWIN; ++i)
-      if (w + S::NW * i < S::QWINS) fill16(frq, qs_l + st * S::QTILE + (w + S::NW * i) * 1024, qsrc[i]);
+    for (int i = FQ; i < S::QWIN; ++i) qwin(frq, st, i);
 #pragma unroll
-    for (int i = FO; i < S::OWIN; ++i)
-      if (w + S::NW * i < S::OWINS) fill16(fro, os_l + st * S::OTILE + (w + S::NW * i) * 1024, osrc[i]);
-    if (w < 2) {
-      const float* src = (w == 0 ? L2b : Db) + q0;
-      fill4(rsrc_words(src, qt < 0 ? 0 : S::BQ * 4), ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D), 4 * perm(lane));
-    }
-    if constexpr (MASK == kMaskBitmask) {
-      const int r = 16 * w + lane / 4;
-      const i32x4 rm = rsrc_words(mbase + (int64_t)q0 * p.mask_si, rows * p.mask_si * 4);
-      fill4(rm, ld_l + st * S::LDB + S::LD_M + 256 * w, (int)(((int64_t)r * p.mask_si + (k0 >> 5) + (lane & 3)) * 4));
-    }
+    for (int i = FO; i < S::OWIN; ++i) owin(fro, st, i);
+    fill_rows(qt, st);
   };
   auto fill_item = [&](int i) {  // i < FQ + FO
     if (i < FQ) fill16(frq, qs_l + fst * S::QTILE + (w + S::NW * i) * 1024, qsrc[i]);
     else fill16(fro, os_l + fst * S::OTILE + (w + S::NW * (i - FQ)) * 1024, osrc[i - FQ]);
   };
   static_assert(FQ + FO <= S::NQF + S::NVF, "one spread fill per first-phase MFMA at most");
-  // Wait until at most k of this wave's tile fills are still in flight.
-  auto wait_fills = [&](int k) {
-    if (k <= 0) {
-      wait_vm_n<0>();
-    } else if (k == 1) {
-      if (w == 0) wait_vm_n<kF0>();
-      else if (w == 1) wait_vm_n<kF1>();
-      else if (w == 2) wait_vm_n<kF2>();
-      else wait_vm_n<kF3>();
-    } else {
-      if (w == 0) wait_vm_n<2 * kF0>();
-      else if (w == 1) wait_vm_n<2 * kF1>();
-      else if (w == 2) wait_vm_n<2 * kF2>();
-      else wait_vm_n<2 * kF3>();
-    }
-  };
 
   // ---- per-lane LDS read bases (everything else is a constant offset) -----
   // Row operands (S, dP): A-operand lane m = lane % 32 of a 32-row chunk
@@ -261,12 +251,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   auto score_products = [&](f32x16& sc, f32x16& dp, int st, int c) {
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS;
     const char* ob = os + st * S::OTILE + 32 * c * S::OS;
-    sc = f32x16{};
-    dp = f32x16{};
 #pragma unroll
-    for (int s = 0; s < S::NQF; ++s) sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qb + qrb + 32 * s), kf[s], sc);
+    for (int s = 0; s < S::NQF; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qb + qrb + 32 * s);
+      if (s == 0) mfma_vz(sc, a, kf[s]);
+      else mfma_vacc(sc, a, kf[s]);
+    }
 #pragma unroll
-    for (int s = 0; s < S::NVF; ++s) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(ob + orb + 32 * s), vf[s], dp);
+    for (int s = 0; s < S::NVF; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + orb + 32 * s);
+      if (s == 0) mfma_vz(dp, a, vf[s]);
+      else mfma_vacc(dp, a, vf[s]);
+    }
+    nops_after_mfma();
   };
   // Exponent scale: c log2(e), with c = 0 replaced by 1e-30 (every finite
   // score then maps to exactly exp2(-L log2 e), as for c = 0, while the
@@ -314,8 +311,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     bf16x8 afr[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) afr[i] = aread(i);
-    nsc = f32x16{};
-    ndp = f32x16{};
     u32x4 pk[2], sk[2];
     // Weights of row pair pr in two halves, issued one slice apart so that
     // the exponentials' latency is covered: e(pr) = exponentials, f(pr) = dS
@@ -338,8 +333,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     for (int i = 0; i < S::NA; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       const int si = (i * S::NQF) / S::NA, next = ((i + 1) * S::NQF) / S::NA;
-      if (next > si) nsc = mfma_bf16(afr[i % PF], kf[si], nsc);
-      else ndp = mfma_bf16(afr[i % PF], vf[i - si], ndp);
+      if (next > si) {
+        if (si == 0) mfma_vz(nsc, afr[i % PF], kf[si]);
+        else mfma_vacc(nsc, afr[i % PF], kf[si]);
+      } else {
+        if (i - si == 0) mfma_vz(ndp, afr[i % PF], vf[i - si]);
+        else mfma_vacc(ndp, afr[i % PF], vf[i - si]);
+      }
       if (i + PF < S::NA) afr[i % PF] = aread(i + PF);
       if constexpr (decltype(dofill)::value) {
         if (i < FQ + FO) fill_item(i);
@@ -375,27 +375,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     i16x4 tlo[PB], thi[PB];
 #pragma unroll
     for (int j = 0; j < PB; ++j) bread(j, tlo[j], thi[j]);
+    asm volatile("s_nop 1");  // the last packed P / dS operands were just written
+    // Slice j: one MFMA, the reads PB MFMAs ahead and, for j < 8, one of the
+    // next chunk's L log2(e) / D reads.
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
       bool is_v;
       int blk, ks;
       bmfma(j, is_v, blk, ks);
       const bf16x8 a = join_tr(tlo[j % PB], thi[j % PB]);
-      if (is_v) dv[blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, pk[ks]), dv[blk]);
-      else dk[blk] = mfma_bf16(a, __builtin_bit_cast(bf16x8, sk[ks]), dk[blk]);
+      if (is_v) mfma_aacc(dv[blk], a, __builtin_bit_cast(bf16x8, pk[ks]));
+      else mfma_aacc(dk[blk], a, __builtin_bit_cast(bf16x8, sk[ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
-      if (j < 8) {  // next chunk's L log2(e) and D rows, one read per MFMA
+      if (j < 8) {
         if (j % 2 == 0) lv[j / 2] = *reinterpret_cast<const f32x4*>(nls + 8 * (j / 2));
         else dvv[j / 2] = *reinterpret_cast<const f32x4*>(nds + 8 * (j / 2));
       }
-    }
-    // One MFMA, the reads PB MFMAs ahead, per group.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PB, 0);
-#pragma unroll
-    for (int j = 0; j < S::NB; ++j) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (j + PB < S::NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      if (j < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -410,12 +406,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
   __syncthreads();  // ring cleared
   if (t0 >= 0) {  // workgroup-uniform
-    int issued = 0;
     fill(t0, 0);
-    ++issued;
-    if (t1 >= 0) { fill(t1, 1); ++issued; }
-    if (t2 >= 0) { fill(t2, 2); ++issued; }
-    wait_fills(issued - 1);
+    fill(t1, 1);
+    fill(t2, 2);
+    wait_vm_n<2 * kF>();
     __syncthreads();
     f32x16 sa, pa, sb, pb;
     score_products(sa, pa, 0, 0);
@@ -435,12 +429,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3.
-      wait_fills(issued - (j + 2 < issued ? j + 2 : issued));
+      wait_vm_n<kF>();
       __syncthreads();
-      // The fill of position j+3 (empty past the last tile) is spread over
-      // chunk 1's first phase.
       fill_begin(t3, (j + 3) % S::NSTAGE);
-      ++issued;
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, q0);
       step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0);
@@ -454,6 +445,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     wait_vm_n<0>();  // copies of empty positions
   }
 
+  nops_after_mfma();  // the last dK^T / dV^T products were just issued
   // Epilogue: dK = c dK^T, dV = dV^T (lane = key; 4 consecutive columns per store).
   if (kvalid) {
     char* dKp = (char*)p.dK + ((int64_t)b * p.sk[0] + (int64_t)h * p.sk[1] + (int64_t)key * p.sk[2]) * 2;

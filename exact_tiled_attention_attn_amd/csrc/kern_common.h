@@ -230,6 +230,30 @@ __device__ __forceinline__ void wait_vm_n() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// 32x32x16 bf16 MFMAs with explicit operand register classes (inline
+// assembly), for kernels that keep some accumulators in VGPRs and others in
+// AGPRs: mfma_vz / mfma_vc / mfma_vacc accumulate in VGPRs with the B
+// operand in AGPRs (start from zero / from c / in place), mfma_aacc
+// accumulates in AGPRs with both operands in VGPRs.  The compiler's hazard
+// tracking does not see inside these statements: a caller reads a VGPR
+// result with a vector instruction only after at least 19 wait states (for
+// instance nops_after_mfma), writes an A / B operand with a vector
+// instruction at least 2 wait states before the MFMA, and reads AGPR
+// results only after nops_after_mfma.
+__device__ __forceinline__ void mfma_vz(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vc(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
+__device__ __forceinline__ void mfma_vacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_aacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void nops_after_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 enum : int { kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200 };
 
