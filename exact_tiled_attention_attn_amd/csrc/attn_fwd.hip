@@ -360,7 +360,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // HBM straight into padded LDS rows (buffer_load ... lds), so no registers
 // are spent on staging and every LDS read address is a per-lane base plus a
 // constant; K and V have two buffers each: K_{j+2} and V_{j+1} stream in
-// while tile j is consumed.
+// while tile j is consumed.  O is normalised by the fp32 sum of the weights
+// (the one L is taken from); the PV product uses their bf16 roundings.
 // ---------------------------------------------------------------------------
 template <int D, int DV>
 struct FwdPipeShape {
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     reinterpret_cast<u32x4*>(vbuf1)[c] = u32x4{0, 0, 0, 0};
   }
 
-  float m_run = -INFINITY, l_run = 0.f, l_use = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[S::NVB];
 #pragma unroll
   for (int vb = 0; vb < S::NVB; ++vb) o[vb] = f32x16{};
@@ -544,7 +545,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 16; ++r) o[vb][r] *= alpha;
     }
     l_run *= alpha;
-    l_use *= alpha;
     m_run = m_new;
   };
 
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // ---- phase A: S^T(t1) on the MFMA pipe, weights of t0 on the VALU ----
       const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       u32x4 pk[S::NKB][2];
-      float ls[4] = {0.f, 0.f, 0.f, 0.f}, lu[2] = {0.f, 0.f};
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
       auto weights = [&](int pr) {  // pair pr: registers 2 (pr % 8), +1 of block pr / 8
         const int kb = pr / 8, r = 2 * (pr % 8);
         const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], scale2, neg_m));
@@ -602,7 +602,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         ls[pr % 4] += p0 + p1;
         const uint32_t u = pack_bf16x2(p0, p1);
         pk[kb][r / 8][(r / 2) % 4] = u;
-        lu[pr % 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), ones_bf16x2(), lu[pr % 2], false);
       };
       bf16x8 kfr[PF];
 #pragma unroll
@@ -626,7 +625,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       __builtin_amdgcn_sched_barrier(0);
       l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      l_use += lu[0] + lu[1];
 
       // ---- phase B: O^T += V^T P^T(t0) on the MFMA pipe, row max of t1 ----
       // Max over the 32 scores of t1 in three-input steps (v_max3): node
@@ -683,7 +681,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   const float l_tot = sum_halves(l_run);
-  const float l_norm = sum_halves(l_use);
+  const float l_norm = l_tot;
   const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
   if (qvalid) {
     const int64_t obase = (int64_t)b * p.so[0] + (int64_t)h * p.so[1] + (int64_t)q * p.so[2];
