@@ -202,19 +202,26 @@ hipEvent_t take_event() {
 void timing_begin(int kind, void* stream) {
   if (!g_timing) return;
   TimedLaunch t{kind, take_event(), take_event()};
-  if (!t.start || !t.stop) return;
-  hipEventRecord(t.start, (hipStream_t)stream);
+  if (!t.start || !t.stop || hipEventRecord(t.start, (hipStream_t)stream) != hipSuccess) {
+    if (t.start) g_free.push_back(t.start);
+    if (t.stop) g_free.push_back(t.stop);
+    return;  // this launch goes untimed
+  }
   g_pending.push_back(t);
 }
 
 void timing_end(int kind, void* stream) {
   if (!g_timing || g_pending.empty() || g_pending.back().kind != kind) return;
-  hipEventRecord(g_pending.back().stop, (hipStream_t)stream);
+  if (hipEventRecord(g_pending.back().stop, (hipStream_t)stream) != hipSuccess) {
+    g_free.push_back(g_pending.back().start);
+    g_free.push_back(g_pending.back().stop);
+    g_pending.pop_back();  // a start without a stop is not a measurement
+  }
 }
 
 void timing_reset() {
   for (auto& t : g_pending) {
-    hipEventSynchronize(t.stop);
+    (void)hipEventSynchronize(t.stop);
     g_free.push_back(t.start);
     g_free.push_back(t.stop);
   }
