@@ -349,7 +349,7 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.O = O;
   b.dO = dO;
   b.L = L;
-  b.Dv = reinterpret_cast<float*>(wsb + lay.off_D);
+  b.Dn = reinterpret_cast<float*>(wsb + lay.off_D);
   b.L2 = reinterpret_cast<float*>(wsb + lay.off_L2);
   b.n_pad = row_pad(p->n);
   b.dQacc = lay.dq_bytes ? reinterpret_cast<float*>(wsb + lay.off_dQ) : nullptr;

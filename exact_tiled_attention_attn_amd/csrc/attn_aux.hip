@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_
       const float Lv = p.L[unit * p.n + i];
       l2 = Lv == -INFINITY ? INFINITY : Lv * kLog2e;
     }
-    p.Dv[row] = acc;
+    p.Dn[row] = -acc;
     p.L2[row] = l2;
   }
   // Clear the dQ accumulator (grid-stride over float4s).

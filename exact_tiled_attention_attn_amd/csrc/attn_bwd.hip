@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const char* Vb = (const char*)p.V + ((int64_t)b * p.sv[0] + (int64_t)h * p.sv[1]) * S::ES;
   const char* dOb = (const char*)p.dO + ((int64_t)b * p.so[0] + (int64_t)h * p.so[1]) * S::ES;
   const float* Lb = p.L + (int64_t)unit * n;
-  const float* Db = p.Dv + (int64_t)unit * p.n_pad;
+  const float* Dnb = p.Dn + (int64_t)unit * p.n_pad;
 
   if constexpr (FUSED) {
     // Resident K tile in LDS (B operand of dQ), padded columns cleared.
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
       const float Lv = qq < n ? Lb[qq] : -INFINITY;
       // Rows with L = -inf (no allowed key, or past n) get +inf: p = exp2(s - inf) = 0.
       lreg = (Lv == -INFINITY) ? INFINITY : Lv * kLog2e;
-      dreg = qq < n ? Db[qq] : 0.f;
+      dreg = qq < n ? -Dnb[qq] : 0.f;
     }
     if constexpr (MASK == kMaskBitmask) {
       if (tid < S::BQ * S::MWORDS) {

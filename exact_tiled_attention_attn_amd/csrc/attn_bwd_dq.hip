@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
   if (qvalid) {
     const float Lv = p.L[(int64_t)unit * n + q];
     L2 = (Lv == -INFINITY) ? INFINITY : Lv * kLog2e;
-    Dq = p.Dv[(int64_t)unit * p.n_pad + q];
+    Dq = -p.Dn[(int64_t)unit * p.n_pad + q];
   }
 
   // Q and dO rows as B operands.

@@ -120,13 +120,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   if constexpr (MASK == kMaskBitmask) mbase = p.mask + b * p.mask_sb + h * p.mask_sh;
 
   // Per-lane row statistics of the two halves: L log2(e) (+inf for rows past
-  // n or with L = -inf, so that p = 0) and D.
-  float l2[2], dd[2];
+  // n or with L = -inf, so that p = 0) and -D.
+  float l2[2], dn[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int q = qa + 32 * u;
     l2[u] = q < n ? p.L2[(int64_t)unit * p.n_pad + q] : INFINITY;
-    dd[u] = q < n ? p.Dv[(int64_t)unit * p.n_pad + q] : 0.f;
+    dn[u] = q < n ? p.Dn[(int64_t)unit * p.n_pad + q] : 0.f;
   }
 
   // Key-tile sequence: ascending, up to the last tile that can hold an
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < S::NDB; ++i) dq[u][i] = f32x16{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dinit[u][r] = -dd[u];
+    for (int r = 0; r < 16; ++r) dinit[u][r] = dn[u];
   }
 
   // ---- tile fills ----------------------------------------------------------
@@ -315,6 +315,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       }
     }
     nops_after_mfma();
+    after_nops_v(sc[0], sc[1], dp[0], dp[1]);
   };
 
   // One pipeline step for chunk (st, c): sc, dp hold its S^T and dP^T - D
@@ -457,9 +458,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       t3 = next_tile(t2);
       ++j;
     }
+    nops_after_mfma();  // the last dQ^T products were just issued
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < S::NDB; ++i) after_nops_a(dq[u][i]);
     wait_vm_n<0>();  // copies of empty positions
   }
-  nops_after_mfma();  // the last dQ^T products were just issued
 
   // Epilogue: dQ = c dQ^T (lane = query; 4 consecutive columns per store).
 #pragma unroll

@@ -14,7 +14,8 @@
 // wave keeps its K and V rows in AGPRs as MFMA B operands and its dK^T,
 // dV^T accumulators in AGPRs for the whole loop over query tiles, while the
 // S / dP accumulators live in VGPRs, where the vector ALUs read them without
-// copies (explicit-register MFMAs of kern_common.h; their wait states are
+// copies, and each dP accumulator starts from -D, so that dS = P (dP - D) is
+// one multiply (explicit-register MFMAs of kern_common.h; their wait states are
 // kept by construction: scores are read one 16-MFMA phase after they are
 // written, s_nop after the prologue's products and before the epilogue, the
 // packed P / dS operands written before the second phase's first read).  Query tiles of 64
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const char* Vb = (const char*)p.V + ((int64_t)b * p.sv[0] + (int64_t)h * p.sv[1]) * 2;
   const char* dOb = (const char*)p.dO + ((int64_t)b * p.so[0] + (int64_t)h * p.so[1]) * 2;
   const float* L2b = p.L2 + (int64_t)unit * p.n_pad;
-  const float* Db = p.Dv + (int64_t)unit * p.n_pad;
+  const float* Dnb = p.Dn + (int64_t)unit * p.n_pad;
   const uint32_t* mbase = nullptr;
   if constexpr (MASK == kMaskBitmask) mbase = p.mask + b * p.mask_sb + h * p.mask_sh;
 
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   auto fill_rows = [&](int qt, int st) {
     const int q0 = qt < 0 ? 0 : qt * S::BQ;
     const bool rows_real = w < 2 && qt >= 0;  // padded rows: always in range; slot l holds row perm(l)
-    const float* src = (w == 0 ? L2b : Db) + q0;
+    const float* src = (w == 0 ? L2b : Dnb) + q0;
     fill4(rows_real ? rsrc_words(src, S::BQ * 4) : r_none,
           w < 2 ? ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D) : sp_l, 4 * perm(lane));
     if constexpr (MASK == kMaskBitmask) {
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int otb = (hh + 4 * (r16 >> 2)) * S::OS + 2 * (16 * g1 + 4 * (r16 & 3));
 
   // S and dP of one chunk (32 query rows at tile row 32 c) from stage st.
-  auto score_products = [&](f32x16& sc, f32x16& dp, int st, int c) {
+  auto score_products = [&](f32x16& sc, f32x16& dp, int st, int c, const f32x16& dn) {
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS;
     const char* ob = os + st * S::OTILE + 32 * c * S::OS;
 #pragma unroll
@@ -260,10 +261,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < S::NVF; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + orb + 32 * s);
-      if (s == 0) mfma_vz(dp, a, vf[s]);
+      if (s == 0) mfma_vc(dp, a, vf[s], dn);
       else mfma_vacc(dp, a, vf[s]);
     }
     nops_after_mfma();
+    after_nops_v(sc, dp);
+    asm volatile("" ::"v"(dn));  // keep the init registers until its product is done
+  };
+  // -D of a 32-row chunk of stage st, in the C layout of the dP accumulator
+  // (register r holds row 8 (r / 4) + 4 hh + r % 4 of the chunk).
+  auto load_dn = [&](int st, int c) -> f32x16 {
+    const float* ds = reinterpret_cast<const float*>(lds_ld + st * S::LDB + S::LD_D) + 32 * c + 4 * hh;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(ds), a1 = *reinterpret_cast<const f32x4*>(ds + 8);
+    const f32x4 a2 = *reinterpret_cast<const f32x4*>(ds + 16), a3 = *reinterpret_cast<const f32x4*>(ds + 24);
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    const f32x8 lo = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const f32x8 hi = __builtin_shufflevector(a2, a3, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
   };
   // Exponent scale: c log2(e), with c = 0 replaced by 1e-30 (every finite
   // score then maps to exactly exp2(-L log2 e), as for c = 0, while the
@@ -290,16 +304,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // from whatever that stage holds (unused after the last chunk).
   //   phase A: MFMA S, dP (next chunk)   || VALU P, dS (this chunk)
   //   phase B: MFMA dV^T, dK^T (this chunk) with transposed reads
-  // lv / dvv hold this chunk's L log2(e) and D rows (f32x4 per row group);
-  // on return they hold those of the next chunk.
-  f32x4 lv[4], dvv[4];
-  auto step = [&](auto dofill, f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc) {
+  // lv holds this chunk's L log2(e) rows (f32x4 per row group); on return it
+  // holds those of the next chunk.  dp arrives as dP - D (its accumulator
+  // started from -D); dni is -D of the next chunk, the start of ndp.  With
+  // dload, the second phase also reads -D of chunk 1 of stage nst into dnx.
+  f32x4 lv[4];
+  auto step = [&](auto dofill, f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc,
+                  const f32x16& dni, auto dload, f32x16& dnx) {
     const char* nqb = qs + nst * S::QTILE + 32 * nc * S::QS + qrb;
     const char* nob = os + nst * S::OTILE + 32 * nc * S::OS + orb;
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS + qtb;
     const char* ob = os + st * S::OTILE + 32 * c * S::OS + otb;
     const float* nls = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_L) + 32 * nc + 4 * hh;
-    const float* nds = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_D) + 32 * nc + 4 * hh;
+    const float* nds = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_D) + 32 * 1 + 4 * hh;
 
     // ---- phase A ----
     constexpr int PF = kPrefetchA;  // row operands in flight
@@ -322,9 +339,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       pe[pr][1] = fast_exp2(__builtin_fmaf(sc[r + 1], scale2, -lv[g][e + 1]));
     };
     auto weights_f = [&](int pr) {
-      const int r = 2 * pr, g = r >> 2, e = r & 3;
-      const float d0 = pe[pr][0] * (dp[r] - dvv[g][e]);
-      const float d1 = pe[pr][1] * (dp[r + 1] - dvv[g][e + 1]);
+      const int r = 2 * pr;
+      const float d0 = pe[pr][0] * dp[r];
+      const float d1 = pe[pr][1] * dp[r + 1];
       pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0], pe[pr][1]);
       sk[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
     };
@@ -337,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         if (si == 0) mfma_vz(nsc, afr[i % PF], kf[si]);
         else mfma_vacc(nsc, afr[i % PF], kf[si]);
       } else {
-        if (i - si == 0) mfma_vz(ndp, afr[i % PF], vf[i - si]);
+        if (i - si == 0) mfma_vc(ndp, afr[i % PF], vf[i - si], dni);
         else mfma_vacc(ndp, afr[i % PF], vf[i - si]);
       }
       if (i + PF < S::NA) afr[i % PF] = aread(i + PF);
@@ -351,6 +368,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(dni));  // keep the init registers until its product is done
 
     // ---- phase B ----
     // MFMA j: even j -> dV block, odd -> dK block (while both remain).
@@ -388,9 +406,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       if (is_v) mfma_aacc(dv[blk], a, __builtin_bit_cast(bf16x8, pk[ks]));
       else mfma_aacc(dk[blk], a, __builtin_bit_cast(bf16x8, sk[ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
-      if (j < 8) {
-        if (j % 2 == 0) lv[j / 2] = *reinterpret_cast<const f32x4*>(nls + 8 * (j / 2));
-        else dvv[j / 2] = *reinterpret_cast<const f32x4*>(nds + 8 * (j / 2));
+      if (j < 4) lv[j] = *reinterpret_cast<const f32x4*>(nls + 8 * j);
+      if constexpr (decltype(dload)::value) {
+        if (j >= 4 && j < 8) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(nds + 8 * (j - 4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dnx[4 * (j - 4) + e] = x[e];
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -412,12 +434,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     wait_vm_n<2 * kF>();
     __syncthreads();
     f32x16 sa, pa, sb, pb;
-    score_products(sa, pa, 0, 0);
+    score_products(sa, pa, 0, 0, load_dn(0, 0));
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < 4; ++g)
       lv[g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds_ld + S::LD_L) + 8 * g + 4 * hh);
-      dvv[g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds_ld + S::LD_D) + 8 * g + 4 * hh);
-    }
+    // -D starts of chunk 1 of the current tile (dnA) and chunk 0 of the next (dnB).
+    f32x16 dnA = load_dn(0, 1), dnB;
     int j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
     while (true) {
       const int st = j % S::NSTAGE, nst = (j + 1) % S::NSTAGE;
@@ -425,16 +447,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       const bool partial = tile_class(t0) == kTilePartial;
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, q0);
-      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1);
+      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, dnA, std::false_type{}, dnA);
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3.
       wait_vm_n<kF>();
       __syncthreads();
+      dnB = load_dn(nst, 0);  // stage nst is complete after this barrier
       fill_begin(t3, (j + 3) % S::NSTAGE);
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, q0);
-      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0);
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA);
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;
@@ -442,10 +465,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       t3 = next_tile(t2);
       ++j;
     }
+    nops_after_mfma();  // the last dK^T / dV^T products were just issued
+#pragma unroll
+    for (int i = 0; i < S::NDB; ++i) after_nops_a(dk[i]);
+#pragma unroll
+    for (int i = 0; i < S::NVB; ++i) after_nops_a(dv[i]);
     wait_vm_n<0>();  // copies of empty positions
   }
 
-  nops_after_mfma();  // the last dK^T / dV^T products were just issued
   // Epilogue: dK = c dK^T, dV = dV^T (lane = key; 4 consecutive columns per store).
   if (kvalid) {
     char* dKp = (char*)p.dK + ((int64_t)b * p.sk[0] + (int64_t)h * p.sk[1] + (int64_t)key * p.sk[2]) * 2;

@@ -243,8 +243,14 @@ __device__ __forceinline__ void wait_vm_n() {
 __device__ __forceinline__ void mfma_vz(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
+// mfma_vc may receive c in registers the compiler copied (from AGPRs) just
+// before the statement and treats as free right after it: the statement
+// itself waits for such a copy and keeps the wave from overwriting those
+// registers while the MFMA still reads them.
 __device__ __forceinline__ void mfma_vc(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
+               : "=&v"(d)
+               : "v"(a), "a"(b), "v"(c));
 }
 __device__ __forceinline__ void mfma_vacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
@@ -253,6 +259,25 @@ __device__ __forceinline__ void mfma_aacc(f32x16& d, const bf16x8& a, const bf16
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void nops_after_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+// After nops_after_mfma: tie the MFMA results to it, so that no read of them
+// is scheduled above the nops (the nops have no data dependence of their
+// own).  Volatile statements keep their relative order.
+template <typename T>
+__device__ __forceinline__ void tie_v(T& x) {
+  asm volatile("" : "+v"(x));
+}
+template <typename T>
+__device__ __forceinline__ void tie_a(T& x) {
+  asm volatile("" : "+a"(x));
+}
+template <typename... T>
+__device__ __forceinline__ void after_nops_v(T&... x) {
+  (tie_v(x), ...);
+}
+template <typename... T>
+__device__ __forceinline__ void after_nops_a(T&... x) {
+  (tie_a(x), ...);
+}
 
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 enum : int { kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200 };
