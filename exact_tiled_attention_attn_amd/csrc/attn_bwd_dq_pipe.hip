@@ -75,8 +75,8 @@ struct DqPipeShape {
   static constexpr int KS = KT::kStride, VS = VT::kStride;
   static constexpr int KTILE = BK * KS, VTILE = BK * VS;
   static constexpr int KWINS = KTILE / 1024, VWINS = VTILE / 1024;  // 1 KB fill windows per tile
-  // Windows of wave w: w, w + NW, ... (KWIN per wave; a wave past the last
-  // window copies an empty range into a spare window instead).
+  // Copies per wave and tile (KWIN / VWIN): a contiguous run of windows, the
+  // last of which is an empty copy for some waves.
   static constexpr int KWIN = (KWINS + NW - 1) / NW, VWIN = (VWINS + NW - 1) / NW;
   static constexpr int MWORDS = BK / 32;         // bitmask words per query row and tile
   static constexpr int MTILE = BQ * MWORDS * 4;  // bitmask bytes per stage
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char vts[S::NSTAGE * S::VTILE];
   __shared__ __attribute__((aligned(16))) char mws[MASK == kMaskBitmask ? S::NSTAGE * S::MTILE : 16];
   __shared__ uint8_t cls_s[MASK == kMaskBitmask ? S::MAXTK : 1];
-  __shared__ __attribute__((aligned(1024))) char spare[1024];  // target of the padding copies
+  __shared__ __attribute__((aligned(1024))) char spare[4096];  // target of the padding copies (any immediate offset)
 
   const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad_dq, p.total_dq);
   if (logical < 0) return;
@@ -182,19 +182,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   }
 
   // ---- tile fills ----------------------------------------------------------
+  // Wave w copies a contiguous run of 1 KB windows of each tile: KB = KWINS /
+  // NW of them, plus one more for the first KX = KWINS % NW waves (the others
+  // issue that item as an empty copy into the spare window, so that every
+  // wave issues the same instructions).  Consecutive windows share one M0
+  // value in groups of four: the copy's immediate offset selects the window
+  // and is taken off the per-lane source offsets.
+  constexpr int KB = S::KWINS / S::NW, KX = S::KWINS % S::NW;
+  constexpr int VB = S::VWINS / S::NW, VX = S::VWINS % S::NW;
+  static_assert(S::KWIN == KB + (KX > 0) && S::VWIN == VB + (VX > 0), "window counts");
+  const int kfirst = w * KB + (w < KX ? w : KX), vfirst = w * VB + (w < VX ? w : VX);
   int ksrc[S::KWIN], vsrc[S::VWIN];
 #pragma unroll
-  for (int i = 0; i < S::KWIN; ++i) ksrc[i] = S::KT::fill_src((w + S::NW * i) * 1024 + 16 * lane, krow);
+  for (int i = 0; i < S::KWIN; ++i)
+    ksrc[i] = (int)((uint32_t)S::KT::fill_src((kfirst + i) * 1024 + 16 * lane, krow) - (uint32_t)((i % 4) * 1024));
 #pragma unroll
-  for (int i = 0; i < S::VWIN; ++i) vsrc[i] = S::VT::fill_src((w + S::NW * i) * 1024 + 16 * lane, vrow);
+  for (int i = 0; i < S::VWIN; ++i)
+    vsrc[i] = (int)((uint32_t)S::VT::fill_src((vfirst + i) * 1024 + 16 * lane, vrow) - (uint32_t)((i % 4) * 1024));
   // Key row of the tile behind lane m % 32 of a score product's A operand:
   // groups of 16 rows taken in transposed order, 4 u + v -> u + 4 v.
   auto perm = [](int l) { return (l & ~15) + ((l & 15) >> 2) + 4 * (l & 3); };
   const uint32_t ks_l = lds_address(kts), vs_l = lds_address(vts), ms_l = lds_address(mws);
   const uint32_t sp_l = lds_address(spare);
-  // Per tile every wave issues KWIN + VWIN copies (a wave without a last
-  // window copies an empty range into the spare window) and, with a bitmask,
-  // two more (mask words of 32 query rows each).
+  // Per tile every wave issues KWIN + VWIN copies and, with a bitmask, two
+  // more (mask words of 32 query rows each).
   constexpr int kBm = MASK == kMaskBitmask;
   constexpr int kF = S::KWIN + S::VWIN + 2 * kBm;
   const i32x4 r_none = rsrc_words(Kb, 0);
@@ -209,15 +220,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     }
   };
   auto mask_rsrc = [&](int64_t rows) { return rsrc_words(mbase + (int64_t)q0 * p.mask_si, rows * p.mask_si * 4); };
-  // Window i of K (V) for wave w, or the spare window with an empty range.
-  auto kwin = [&](const i32x4& rk, int st, int i) {
-    const bool real = S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS;
-    fill16(real ? rk : r_none, real ? ks_l + st * S::KTILE + (w + S::NW * i) * 1024 : sp_l, ksrc[i]);
+  // Item i of this wave's run over a tile at LDS byte address `tile`.
+  auto win_item = [&](const i32x4& r, uint32_t tile, int first, int nb, int nx, const auto& src, int i) {
+    const bool extra = i == nb;
+    const bool real = !extra || w < nx;
+    if (i % 4 == 0 || extra)  // group start, or the item that may be an empty copy
+      set_m0(real ? tile + (first + 4 * (i / 4)) * 1024 : sp_l);  // an empty copy lands at sp_l + (i % 4) KB
+    fill16_off(real ? r : r_none, src[i], i % 4);
   };
-  auto vwin = [&](const i32x4& rv, int st, int i) {
-    const bool real = S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS;
-    fill16(real ? rv : r_none, real ? vs_l + st * S::VTILE + (w + S::NW * i) * 1024 : sp_l, vsrc[i]);
-  };
+  auto kwin = [&](const i32x4& rk, int st, int i) { win_item(rk, ks_l + st * S::KTILE, kfirst, KB, KX, ksrc, i); };
+  auto vwin = [&](const i32x4& rv, int st, int i) { win_item(rv, vs_l + st * S::VTILE, vfirst, VB, VX, vsrc, i); };
   auto fill = [&](int kt, int st) {  // kt < 0: empty ranges, same instructions
     const int k0 = kt < 0 ? 0 : kt * S::BK;
     const int64_t rows = kt < 0 ? 0 : n - k0;
@@ -230,10 +242,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(kt < 0 ? 0 : n - q0), st, k0);
   };
   // The same copies split in two, for the fill issued inside a pipeline step:
-  // FK + FV windows that every wave copies (issued one per operand of the
-  // step's first phase) and the rest.  kt < 0 copies nothing (empty buffer
-  // ranges) but issues the same instructions, so that the per-wave counts hold.
-  constexpr int FK = S::KWINS / S::NW, FV = S::VWINS / S::NW;
+  // the first FK + FV items (issued one per four MFMAs of the step's first
+  // phase) and the rest (the extra items, mask words), issued first.  kt < 0
+  // copies nothing (empty buffer ranges) but issues the same instructions.
+  constexpr int FK = KB, FV = VB;
   static_assert(4 * (FK + FV) <= 2 * S::NR, "one spread copy per four first-phase MFMAs at most");
   i32x4 frk, frv;
   int fst = 0;
@@ -250,8 +262,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(kt < 0 ? 0 : n - q0), st, k0);
   };
   auto fill_item = [&](int i) {  // i < FK + FV
-    if (i < FK) fill16(frk, ks_l + fst * S::KTILE + (w + S::NW * i) * 1024, ksrc[i]);
-    else fill16(frv, vs_l + fst * S::VTILE + (w + S::NW * (i - FK)) * 1024, vsrc[i - FK]);
+    if (i < FK) kwin(frk, fst, i);
+    else vwin(frv, fst, i - FK);
   };
   // ---- per-lane LDS read bases (everything else is a constant offset) -----
   // Row operands (S^T, dP^T): A-operand lane m = lane % 32 of a 32-key chunk

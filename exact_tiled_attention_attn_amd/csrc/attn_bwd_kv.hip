@@ -39,8 +39,6 @@
 #include "kern_common.h"
 
 namespace eta {
-
-
 #ifndef ETA_KV_PREFETCH_A
 #define ETA_KV_PREFETCH_A 4
 #endif
@@ -65,8 +63,8 @@ struct KvShape {
   static constexpr int QS = QT::kStride, OS = OT::kStride;
   static constexpr int QTILE = BQ * QS, OTILE = BQ * OS;
   static constexpr int QWINS = QTILE / 1024, OWINS = OTILE / 1024;  // 1 KB fill windows per tile
-  // Windows of wave w: w, w + NW, ... (QWIN / OWIN per wave; a wave past the
-  // last window copies an empty range into a spare window instead).
+  // Copies per wave and tile (QWIN / OWIN): a contiguous run of windows, the
+  // last of which is an empty copy for some waves.
   static constexpr int QWIN = (QWINS + NW - 1) / NW, OWIN = (OWINS + NW - 1) / NW;
   static constexpr int MWORDS = BK / 32;
   // Per stage: L log2(e) [BQ], D [BQ], mask words [BQ][MWORDS].
@@ -84,7 +82,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char os[S::NSTAGE * S::OTILE];
   __shared__ __attribute__((aligned(16))) char lds_ld[S::NSTAGE * S::LDB];
   __shared__ uint8_t cls_s[MASK == kMaskBitmask ? S::MAXTQ : 1];
-  __shared__ __attribute__((aligned(1024))) char spare[1024];  // target of the padding copies
+  __shared__ __attribute__((aligned(1024))) char spare[4096];  // target of the padding copies (any immediate offset)
 
   const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad, p.total);
   if (logical < 0) return;
@@ -160,32 +158,45 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   for (int i = 0; i < S::NVB; ++i) dv[i] = f32x16{};
 
   // ---- tile fills ----------------------------------------------------------
+  // Wave w copies a contiguous run of 1 KB windows of each tile: QB = QWINS /
+  // NW of them, plus one more for the first QX = QWINS % NW waves (the others
+  // issue that item as an empty copy into the spare window, so that every
+  // wave issues the same instructions).  Consecutive windows share one M0
+  // value in groups of four: the copy's immediate offset selects the window
+  // and is taken off the per-lane source offsets.
+  constexpr int QB = S::QWINS / S::NW, QX = S::QWINS % S::NW;
+  constexpr int OB = S::OWINS / S::NW, OX = S::OWINS % S::NW;
+  static_assert(S::QWIN == QB + (QX > 0) && S::OWIN == OB + (OX > 0), "window counts");
+  const int qfirst = w * QB + (w < QX ? w : QX), ofirst = w * OB + (w < OX ? w : OX);
   int qsrc[S::QWIN], osrc[S::OWIN];
 #pragma unroll
-  for (int i = 0; i < S::QWIN; ++i) qsrc[i] = S::QT::fill_src((w + S::NW * i) * 1024 + 16 * lane, qrow);
+  for (int i = 0; i < S::QWIN; ++i)
+    qsrc[i] = (int)((uint32_t)S::QT::fill_src((qfirst + i) * 1024 + 16 * lane, qrow) - (uint32_t)((i % 4) * 1024));
 #pragma unroll
-  for (int i = 0; i < S::OWIN; ++i) osrc[i] = S::OT::fill_src((w + S::NW * i) * 1024 + 16 * lane, orow);
+  for (int i = 0; i < S::OWIN; ++i)
+    osrc[i] = (int)((uint32_t)S::OT::fill_src((ofirst + i) * 1024 + 16 * lane, orow) - (uint32_t)((i % 4) * 1024));
   // Query row of the tile behind LDS slot l of the L / D copies (and behind
   // lane l % 32 of a score product's A operand): groups of 16 rows taken in
   // transposed order, 4 u + v -> u + 4 v.
   auto perm = [](int l) { return (l & ~15) + ((l & 15) >> 2) + 4 * (l & 3); };
   const uint32_t qs_l = lds_address(qs), os_l = lds_address(os), ld_l = lds_address(lds_ld);
   const uint32_t sp_l = lds_address(spare);
-  // Per tile every wave issues QWIN + OWIN tile copies (a wave past the last
-  // window copies an empty range into the spare window), one row copy (L
-  // log2(e) rows by wave 0, D rows by wave 1, empty ranges by the others)
+  // Per tile every wave issues QWIN + OWIN tile copies, one row copy (L
+  // log2(e) rows by wave 0, -D rows by wave 1, empty ranges by the others)
   // and, with a bitmask, one more (mask words of 16 query rows).
   constexpr int kBm = MASK == kMaskBitmask;
   constexpr int kF = S::QWIN + S::OWIN + 1 + kBm;
   const i32x4 r_none = rsrc_words(Qb, 0);
-  auto qwin = [&](const i32x4& rq, int st, int i) {
-    const bool real = S::QWINS % S::NW == 0 || w + S::NW * i < S::QWINS;
-    fill16(real ? rq : r_none, real ? qs_l + st * S::QTILE + (w + S::NW * i) * 1024 : sp_l, qsrc[i]);
+  // Item i of this wave's run over a tile at LDS byte address `tile`.
+  auto win_item = [&](const i32x4& r, uint32_t tile, int first, int nb, int nx, const auto& src, int i) {
+    const bool extra = i == nb;
+    const bool real = !extra || w < nx;
+    if (i % 4 == 0 || extra)  // group start, or the item that may be an empty copy
+      set_m0(real ? tile + (first + 4 * (i / 4)) * 1024 : sp_l);  // an empty copy lands at sp_l + (i % 4) KB
+    fill16_off(real ? r : r_none, src[i], i % 4);
   };
-  auto owin = [&](const i32x4& ro, int st, int i) {
-    const bool real = S::OWINS % S::NW == 0 || w + S::NW * i < S::OWINS;
-    fill16(real ? ro : r_none, real ? os_l + st * S::OTILE + (w + S::NW * i) * 1024 : sp_l, osrc[i]);
-  };
+  auto qwin = [&](const i32x4& rq, int st, int i) { win_item(rq, qs_l + st * S::QTILE, qfirst, QB, QX, qsrc, i); };
+  auto owin = [&](const i32x4& ro, int st, int i) { win_item(ro, os_l + st * S::OTILE, ofirst, OB, OX, osrc, i); };
   // The rest of a tile's copies (row statistics, mask words); qt < 0 copies
   // nothing (empty buffer ranges) but issues the same instructions.
   auto fill_rows = [&](int qt, int st) {
@@ -213,11 +224,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     fill_rows(qt, st);
   };
   // The same copies split in two, for the fill issued inside a pipeline step:
-  // FQ + FO windows (issued one per MFMA of the step's first phase) and the rest.
-  constexpr int FQ = S::QWINS / S::NW, FO = S::OWINS / S::NW;
+  // the first FQ + FO items (issued one per MFMA of the step's first phase)
+  // and the rest (the extra items, rows, mask words), issued first.
+  constexpr int FQ = QB, FO = OB;
   i32x4 frq, fro;
   int fst = 0;
-  auto fill_begin = [&](int qt, int st) {  // descriptors and the uneven rest
+  auto fill_begin = [&](int qt, int st) {
     const int q0 = qt < 0 ? 0 : qt * S::BQ;
     const int64_t rows = qt < 0 ? 0 : n - q0;
     frq = rsrc_words(Qb + (int64_t)q0 * qrow, rows * qrow);
@@ -230,8 +242,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     fill_rows(qt, st);
   };
   auto fill_item = [&](int i) {  // i < FQ + FO
-    if (i < FQ) fill16(frq, qs_l + fst * S::QTILE + (w + S::NW * i) * 1024, qsrc[i]);
-    else fill16(fro, os_l + fst * S::OTILE + (w + S::NW * (i - FQ)) * 1024, osrc[i - FQ]);
+    if (i < FQ) qwin(frq, fst, i);
+    else owin(fro, fst, i - FQ);
   };
   static_assert(FQ + FO <= S::NQF + S::NVF, "one spread fill per first-phase MFMA at most");
 

@@ -225,6 +225,22 @@ __device__ __forceinline__ void fill4(i32x4 r, uint32_t lds, int voff) {
                : "s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+// Copies that share one M0 value: set_m0 writes the LDS base, fill16_off
+// copies with an immediate offset of k KB (k = 0..3), which the hardware adds
+// to both the source offset and the LDS address (M0 + k KB + 16 lane), so
+// four consecutive 1 KB windows need one M0 write.  Nothing else in the
+// kernels that use them writes M0 (checked in the assembly by the tests).
+__device__ __forceinline__ void set_m0(uint32_t v) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(v) : "memory", "m0");
+}
+__device__ __forceinline__ void fill16_off(i32x4 r, int voff, int k) {
+  switch (k) {
+    case 0: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r) : "memory"); break;
+    case 1: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:1024 lds" : : "v"(voff), "s"(r) : "memory"); break;
+    case 2: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:2048 lds" : : "v"(voff), "s"(r) : "memory"); break;
+    default: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:3072 lds" : : "v"(voff), "s"(r) : "memory"); break;
+  }
+}
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");

@@ -94,6 +94,16 @@ def functions(asm: str):
     return out
 
 
+def m0_writers(ins):
+    """Instructions writing M0 that are not an s_mov_b32 followed by s_nop 0 (set_m0)."""
+    out = []
+    for i, t in enumerate(ins):
+        op, args = _split(t)
+        if args and args[0] == "m0" and not (op == "s_mov_b32" and i + 1 < len(ins) and ins[i + 1] == "s_nop 0"):
+            out.append(t)
+    return out
+
+
 def check(ins):
     """List of hazard descriptions for one function's instructions."""
     problems = []

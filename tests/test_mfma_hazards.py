@@ -3,8 +3,9 @@
 The dK/dV and dQ kernels issue their MFMAs from inline assembly (explicit
 register classes), which the compiler's hazard recognizer does not see.
 These tests compile both sources for gfx950 and check every instance with
-tests/mfma_hazards.py; two planted listings show that the checker catches
-each kind of hazard.
+tests/mfma_hazards.py, and that no instruction other than the copies'
+set_m0 writes M0; planted listings show that the checker catches each kind
+of hazard.
 """
 
 import os
@@ -12,7 +13,7 @@ import tempfile
 
 import pytest
 
-from tests.mfma_hazards import check, compile_to_asm, functions
+from tests.mfma_hazards import check, compile_to_asm, functions, m0_writers
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc")
@@ -54,3 +55,7 @@ def test_kernel_wait_states(src):
     found = {k: check(v) for k, v in kernels.items()}
     bad = {k: v[:3] for k, v in found.items() if v}
     assert not bad, bad
+    # The grouped direct copies keep M0 between set_m0 statements: nothing
+    # else may write it.
+    other = {k: m0_writers(v)[:3] for k, v in kernels.items() if m0_writers(v)}
+    assert not other, other
