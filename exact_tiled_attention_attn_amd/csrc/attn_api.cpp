@@ -101,8 +101,9 @@ attn_status check_view(const char* name, const int64_t s[3], int64_t B, int64_t 
       return fail(ATTN_ERR_STRIDE, "%s: stride %lld elements is not a multiple of 16 bytes", name,
                   (long long)s[i]);
   }
-  // The kernels address one (batch, head) slice with 32-bit byte offsets.
-  if ((n - 1) * s[2] * es + w * es > int64_t(0x7FFFFFFF))
+  // The kernels address one (batch, head) slice with 32-bit byte offsets,
+  // row strides included.
+  if ((n - 1) * s[2] * es + w * es > int64_t(0x7FFFFFFF) || s[2] * es > int64_t(0x7FFFFFFF))
     return fail(ATTN_ERR_UNSUPPORTED, "%s: one head spans more than 2 GiB (n * row stride)", name);
   struct Dim {
     int64_t size, stride;

@@ -54,6 +54,7 @@ struct KvShape {
   static constexpr int BK = kBwdBk;  // keys per workgroup, 32 per wave
   static constexpr int BQ = kBwdBq;  // queries per tile: two chunks of 32
   static constexpr int NSTAGE = 4;   // LDS ring: tiles j .. j+2 resident or in flight
+  static_assert((NSTAGE & (NSTAGE - 1)) == 0, "power-of-two ring");
   static constexpr int NQF = D / 16, NVF = DV / 16;  // K / V fragments per lane
   static constexpr int NDB = D / 32, NVB = DV / 32;  // 32-column blocks of dK^T / dV^T
   static constexpr int NA = NQF + NVF;               // S and dP MFMAs per chunk
@@ -199,18 +200,22 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   auto owin = [&](const i32x4& ro, int st, int i) { win_item(ro, os_l + st * S::OTILE, ofirst, OB, OX, osrc, i); };
   // The rest of a tile's copies (row statistics, mask words); qt < 0 copies
   // nothing (empty buffer ranges) but issues the same instructions.
+  auto fill_mask = [&](int qt, int st) {
+    if constexpr (MASK == kMaskBitmask) {
+      // Row 16 w + lane / 4 of the tile, word lane % 4 of this key tile.
+      const int q0 = qt < 0 ? 0 : qt * S::BQ;
+      const int r = 16 * w + lane / 4;
+      const i32x4 rm = rsrc_words(mbase + (int64_t)q0 * p.mask_si, qt < 0 ? 0 : (int64_t)(n - q0) * p.mask_si * 4);
+      fill4(rm, ld_l + st * S::LDB + S::LD_M + 256 * w, (int)(((int64_t)r * p.mask_si + (k0 >> 5) + (lane & 3)) * 4));
+    }
+  };
   auto fill_rows = [&](int qt, int st) {
     const int q0 = qt < 0 ? 0 : qt * S::BQ;
     const bool rows_real = w < 2 && qt >= 0;  // padded rows: always in range; slot l holds row perm(l)
     const float* src = (w == 0 ? L2b : Dnb) + q0;
     fill4(rows_real ? rsrc_words(src, S::BQ * 4) : r_none,
           w < 2 ? ld_l + st * S::LDB + (w == 0 ? S::LD_L : S::LD_D) : sp_l, 4 * perm(lane));
-    if constexpr (MASK == kMaskBitmask) {
-      // Row 16 w + lane / 4 of the tile, word lane % 4 of this key tile.
-      const int r = 16 * w + lane / 4;
-      const i32x4 rm = rsrc_words(mbase + (int64_t)q0 * p.mask_si, qt < 0 ? 0 : (int64_t)(n - q0) * p.mask_si * 4);
-      fill4(rm, ld_l + st * S::LDB + S::LD_M + 256 * w, (int)(((int64_t)r * p.mask_si + (k0 >> 5) + (lane & 3)) * 4));
-    }
+    fill_mask(qt, st);
   };
   auto fill = [&](int qt, int st) {
     const int q0 = qt < 0 ? 0 : qt * S::BQ;
@@ -224,22 +229,39 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     fill_rows(qt, st);
   };
   // The same copies split in two, for the fill issued inside a pipeline step:
-  // the first FQ + FO items (issued one per MFMA of the step's first phase)
-  // and the rest (the extra items, rows, mask words), issued first.
+  // the first FQ + FO items (issued one per MFMA of chunk 1's first phase)
+  // and the rest (the extra items, rows, mask words), issued right after the
+  // mid-tile barrier.  Their buffer resources are computed by plan_fill in
+  // chunk 0's second phase, where the scalar work issues under the MFMAs.
   constexpr int FQ = QB, FO = OB;
-  i32x4 frq, fro;
-  int fst = 0;
-  auto fill_begin = [&](int qt, int st) {
-    const int q0 = qt < 0 ? 0 : qt * S::BQ;
-    const int64_t rows = qt < 0 ? 0 : n - q0;
-    frq = rsrc_words(Qb + (int64_t)q0 * qrow, rows * qrow);
-    fro = rsrc_words(dOb + (int64_t)q0 * orow, rows * orow);
+  // Buffer resource of the rows of query tile q0.. of a [n, row] slice with
+  // rb bytes per row; the host bounds (n - 1) rb + the row width by 2^31 - 1,
+  // so the products below fit in 32 bits.  qt < 0: an empty range.
+  auto tile_words = [&](const void* base, int qt, int rb) -> i32x4 {
+    const uint32_t q0 = qt < 0 ? 0u : (uint32_t)(qt * S::BQ);
+    const uint32_t nb = qt < 0 ? 0u : (uint32_t)(n - (int)q0) * (uint32_t)rb;
+    const uint64_t a = reinterpret_cast<uint64_t>(base) + q0 * (uint32_t)rb;
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)(nb < 0x7FFFFFFFu ? nb : 0x7FFFFFFFu), 0x00020000};
+  };
+  // The next in-step fill: resources of the Q, dO and row-statistic copies,
+  // the query tile and the target stage.
+  i32x4 frq, fro, frr;
+  int fst = 0, fqt = -1;
+  auto plan_fill = [&](int qt, int st) {
+    frq = tile_words(Qb, qt, qrow);
+    fro = tile_words(dOb, qt, orow);
+    const float* src = (w == 0 ? L2b : Dnb) + (qt < 0 ? 0 : qt * S::BQ);
+    frr = (w < 2 && qt >= 0) ? rsrc_words(src, S::BQ * 4) : r_none;
     fst = st;
+    fqt = qt;
+  };
+  auto fill_begin = [&]() {
 #pragma unroll
-    for (int i = FQ; i < S::QWIN; ++i) qwin(frq, st, i);
+    for (int i = FQ; i < S::QWIN; ++i) qwin(frq, fst, i);
 #pragma unroll
-    for (int i = FO; i < S::OWIN; ++i) owin(fro, st, i);
-    fill_rows(qt, st);
+    for (int i = FO; i < S::OWIN; ++i) owin(fro, fst, i);
+    fill4(frr, w < 2 ? ld_l + fst * S::LDB + (w == 0 ? S::LD_L : S::LD_D) : sp_l, 4 * perm(lane));
+    fill_mask(fqt, fst);
   };
   auto fill_item = [&](int i) {  // i < FQ + FO
     if (i < FQ) qwin(frq, fst, i);
@@ -316,13 +338,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // from whatever that stage holds (unused after the last chunk).
   //   phase A: MFMA S, dP (next chunk)   || VALU P, dS (this chunk)
   //   phase B: MFMA dV^T, dK^T (this chunk) with transposed reads
+  // hook() runs in the third slice of the second phase (scalar set-up work).
   // lv holds this chunk's L log2(e) rows (f32x4 per row group); on return it
   // holds those of the next chunk.  dp arrives as dP - D (its accumulator
   // started from -D); dni is -D of the next chunk, the start of ndp.  With
   // dload, the second phase also reads -D of chunk 1 of stage nst into dnx.
   f32x4 lv[4];
   auto step = [&](auto dofill, f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc,
-                  const f32x16& dni, auto dload, f32x16& dnx) {
+                  const f32x16& dni, auto dload, f32x16& dnx, auto hook) {
     const char* nqb = qs + nst * S::QTILE + 32 * nc * S::QS + qrb;
     const char* nob = os + nst * S::OTILE + 32 * nc * S::OS + orb;
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS + qtb;
@@ -419,6 +442,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       else mfma_aacc(dk[blk], a, __builtin_bit_cast(bf16x8, sk[ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
       if (j < 4) lv[j] = *reinterpret_cast<const f32x4*>(nls + 8 * j);
+      if (j == 2) hook();
       if constexpr (decltype(dload)::value) {
         if (j >= 4 && j < 8) {
           const f32x4 x = *reinterpret_cast<const f32x4*>(nds + 8 * (j - 4));
@@ -452,24 +476,25 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       lv[g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds_ld + S::LD_L) + 8 * g + 4 * hh);
     // -D starts of chunk 1 of the current tile (dnA) and chunk 0 of the next (dnB).
     f32x16 dnA = load_dn(0, 1), dnB;
-    int j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
+    unsigned j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
     while (true) {
-      const int st = j % S::NSTAGE, nst = (j + 1) % S::NSTAGE;
+      const int st = (int)(j & (S::NSTAGE - 1)), nst = (int)((j + 1) & (S::NSTAGE - 1));
       const int q0 = t0 * S::BQ;
       const bool partial = tile_class(t0) == kTilePartial;
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, q0);
-      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, dnA, std::false_type{}, dnA);
+      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, dnA, std::false_type{}, dnA,
+           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); });
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3.
       wait_vm_n<kF>();
       __syncthreads();
       dnB = load_dn(nst, 0);  // stage nst is complete after this barrier
-      fill_begin(t3, (j + 3) % S::NSTAGE);
+      fill_begin();
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, q0);
-      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA);
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA, [] {});
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;

@@ -115,6 +115,7 @@ def test_workspace_formula():
     (lambda p: p.sq.__setitem__(2, 32), 3),   # rows overlap
     (lambda p: p.sk.__setitem__(1, -6400), 3),
     (lambda p: p.so.__setitem__(1, 64 * 99), 3),  # heads overlap
+    (lambda p: (setattr(p, "n", 1), p.sq.__setitem__(2, 1 << 31)), 6),  # row stride past 32-bit offsets
 ])
 def test_invalid_problem_rejected(mut, status):
     p = problem()
