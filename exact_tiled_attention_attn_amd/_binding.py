@@ -46,6 +46,7 @@ class AttnProblem(ctypes.Structure):
         ("sq", ctypes.c_int64 * 3), ("sk", ctypes.c_int64 * 3),
         ("sv", ctypes.c_int64 * 3), ("so", ctypes.c_int64 * 3),
         ("deterministic", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("nk", ctypes.c_int64), ("causal_offset", ctypes.c_int64),
     ]
 
 
@@ -96,13 +97,24 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, deterministic=False) -> AttnProblem:
-    """Fill the ABI problem struct from [B, H, n, .] tensors (strides in elements)."""
-    if q.dim() != 4:
-        raise ValueError("tensors must be [B, H, n, dim]")
+def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, deterministic=False,
+                 causal_offset=0) -> AttnProblem:
+    """Fill the ABI problem struct (strides in elements).
+
+    q [B, H, n, d]; k [B, H, nk, d]; v [B, H, nk, v]; o_like [B, H, n, v].
+    causal_offset (causal mask only): key j is allowed for query i iff
+    j <= i + causal_offset.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("tensors must be [B, H, rows, dim]")
     B, H, n, d = q.shape
+    nk = k.shape[2]
+    if tuple(k.shape) != (B, H, nk, d) or tuple(v.shape[:3]) != (B, H, nk):
+        raise ValueError(f"shapes do not match: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     p = AttnProblem()
     p.B, p.H, p.n, p.d, p.v = B, H, n, d, v.shape[-1]
+    p.nk = nk
+    p.causal_offset = int(causal_offset)
     p.dtype = _dtype_code(q)
     p.mask_mode = MASK_MODES[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
     p.scale = float(scale)
@@ -148,13 +160,18 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, workspace=None):
-    """O [B,H,n,v] (dtype of q) and L [B,H,n] (fp32 natural-log logsumexp)."""
+def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, workspace=None,
+        causal_offset=0):
+    """O [B,H,n,v] (dtype of q) and L [B,H,n] (fp32 natural-log logsumexp).
+
+    q has n rows, k and v nk rows (any nk >= 1); causal_offset shifts the
+    causal mask (key j allowed for query i iff j <= i + causal_offset).
+    """
     lib = load_library()
     B, H, n, _ = q.shape
     o = out if out is not None else torch.empty((B, H, n, v.shape[-1]), dtype=q.dtype, device=q.device)
     L = lse if lse is not None else torch.empty((B, H, n), dtype=torch.float32, device=q.device)
-    p = make_problem(q, k, v, o, scale, mask_mode, mask)
+    p = make_problem(q, k, v, o, scale, mask_mode, mask, causal_offset=causal_offset)
     need = workspace_size(p, False)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
@@ -163,7 +180,7 @@ def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, work
 
 
 def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=None, dv=None,
-        workspace=None, deterministic=False):
+        workspace=None, deterministic=False, causal_offset=0):
     """dQ, dK, dV (dtype of q) from the forward's O and L and the upstream dO.
 
     ``deterministic`` selects the query-tile-outer dQ kernel (bitwise
@@ -181,7 +198,7 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
         raise ValueError("dQ, dK, dV must have the strides of Q, K, V")
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, H, n]")
-    p = make_problem(q, k, v, o, scale, mask_mode, mask, deterministic)
+    p = make_problem(q, k, v, o, scale, mask_mode, mask, deterministic, causal_offset)
     need = workspace_size(p, True)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
@@ -190,13 +207,14 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
     return dq, dk, dv
 
 
-def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=0):
+def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=0, causal_offset=0):
     """The kernels' (query tile x key tile) classification as uint8 [units, tq, tk].
 
     is_bwd: 0 forward, 1 key-tile-outer backward, 2 query-tile-outer dQ.
     """
     lib = load_library()
-    p = make_problem(q, k, v, v, scale, mask_mode, mask)
+    o_like = torch.empty((*q.shape[:3], v.shape[-1]), device="meta")  # strides of a contiguous O
+    p = make_problem(q, k, v, o_like, scale, mask_mode, mask, causal_offset=causal_offset)
     bq, bk, tq, tk = (ctypes.c_int32() for _ in range(4))
     _check(lib.attn_debug_tile_map(ctypes.byref(p), int(is_bwd), None, 0, ctypes.byref(bq),
                                    ctypes.byref(bk), ctypes.byref(tq), ctypes.byref(tk), None, 0,

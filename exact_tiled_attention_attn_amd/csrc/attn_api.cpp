@@ -37,12 +37,15 @@ struct Tiles {
   int64_t tq, tk;
 };
 
+// Key rows (nk = 0 stands for nk = n).
+int64_t nkeys(const attn_problem& p) { return p.nk == 0 ? p.n : p.nk; }
+
 Tiles fwd_tiles(const attn_problem& p) {
-  return Tiles{eta::kFwdBq, eta::kFwdBk, cdiv(p.n, eta::kFwdBq), cdiv(p.n, eta::kFwdBk)};
+  return Tiles{eta::kFwdBq, eta::kFwdBk, cdiv(p.n, eta::kFwdBq), cdiv(nkeys(p), eta::kFwdBk)};
 }
 Tiles bwd_tiles(const attn_problem& p) {
   const int bq = p.dtype == ATTN_BF16 ? eta::kBwdBq : 32;
-  return Tiles{bq, eta::kBwdBk, cdiv(p.n, bq), cdiv(p.n, eta::kBwdBk)};
+  return Tiles{bq, eta::kBwdBk, cdiv(p.n, bq), cdiv(nkeys(p), eta::kBwdBk)};
 }
 
 int64_t row_pad(int64_t n) { return cdiv(n, eta::kRowPad) * eta::kRowPad; }
@@ -50,9 +53,10 @@ int64_t row_pad(int64_t n) { return cdiv(n, eta::kRowPad) * eta::kRowPad; }
 int64_t mask_units(const attn_problem& p) { return p.mask_sb == 0 ? p.H : p.B * p.H; }
 
 Tiles dq_tiles(const attn_problem& p) {
-  if (eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, p.n))
-    return Tiles{eta::kDqPipeBq, eta::kDqPipeBk, cdiv(p.n, eta::kDqPipeBq), cdiv(p.n, eta::kDqPipeBk)};
-  return Tiles{eta::kDqBq, eta::kDqBk, cdiv(p.n, eta::kDqBq), cdiv(p.n, eta::kDqBk)};
+  const int64_t nk = nkeys(p);
+  if (eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nk))
+    return Tiles{eta::kDqPipeBq, eta::kDqPipeBk, cdiv(p.n, eta::kDqPipeBq), cdiv(nk, eta::kDqPipeBk)};
+  return Tiles{eta::kDqBq, eta::kDqBk, cdiv(p.n, eta::kDqBq), cdiv(nk, eta::kDqBk)};
 }
 
 struct Layout {
@@ -140,8 +144,10 @@ attn_status validate_problem(const attn_problem* p) {
   if (p->B < 1 || p->H < 1 || p->n < 1 || p->d < 1 || p->v < 1)
     return fail(ATTN_ERR_SHAPE, "B, H, n, d, v must be >= 1 (got %lld %lld %lld %lld %lld)",
                 (long long)p->B, (long long)p->H, (long long)p->n, (long long)p->d, (long long)p->v);
-  if (p->n > (int64_t(1) << 30) || p->B * p->H > (int64_t(1) << 24) ||
-      p->B * p->H * p->n > kMaxElems / std::max(p->d, p->v))
+  if (p->nk < 0) return fail(ATTN_ERR_SHAPE, "nk must be >= 1 (or 0 for nk = n)");
+  const int64_t nk = nkeys(*p);
+  if (p->n > (int64_t(1) << 30) || nk > (int64_t(1) << 30) || p->B * p->H > (int64_t(1) << 24) ||
+      p->B * p->H * std::max(p->n, nk) > kMaxElems / std::max(p->d, p->v))
     return fail(ATTN_ERR_SHAPE, "problem too large");
   if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16)
     return fail(ATTN_ERR_DTYPE, "unknown dtype %d", p->dtype);
@@ -154,11 +160,15 @@ attn_status validate_problem(const attn_problem* p) {
     return fail(ATTN_ERR_UNSUPPORTED, "deterministic must be 0 or 1");
   if (p->reserved != 0) return fail(ATTN_ERR_UNSUPPORTED, "reserved field must be 0");
   if (!std::isfinite(p->scale)) return fail(ATTN_ERR_SHAPE, "scale must be finite");
+  if (p->causal_offset != 0 && p->mask_mode != ATTN_MASK_CAUSAL)
+    return fail(ATTN_ERR_MASK, "causal_offset applies to the causal mask only");
+  if (p->causal_offset > (int64_t(1) << 30) || p->causal_offset < -(int64_t(1) << 30))
+    return fail(ATTN_ERR_SHAPE, "|causal_offset| must be <= 2^30");
   if (p->mask_mode == ATTN_MASK_BITMASK) {
     if (!p->mask) return fail(ATTN_ERR_MASK, "bitmask mode needs a mask");
     if (reinterpret_cast<uintptr_t>(p->mask) % 4)
       return fail(ATTN_ERR_STRIDE, "mask pointer must be 4-byte aligned");
-    const int64_t words = (p->n + 31) / 32;
+    const int64_t words = (nk + 31) / 32;
     if (p->mask_si < words || p->mask_sh < 0 || p->mask_sb < 0)
       return fail(ATTN_ERR_MASK, "mask strides invalid (row stride %lld < %lld words?)",
                   (long long)p->mask_si, (long long)words);
@@ -166,8 +176,8 @@ attn_status validate_problem(const attn_problem* p) {
   const int es = p->dtype == ATTN_BF16 ? 2 : 4;
   attn_status st;
   if ((st = check_view("Q", p->sq, p->B, p->H, p->n, p->d, es)) != ATTN_OK) return st;
-  if ((st = check_view("K", p->sk, p->B, p->H, p->n, p->d, es)) != ATTN_OK) return st;
-  if ((st = check_view("V", p->sv, p->B, p->H, p->n, p->v, es)) != ATTN_OK) return st;
+  if ((st = check_view("K", p->sk, p->B, p->H, nk, p->d, es)) != ATTN_OK) return st;
+  if ((st = check_view("V", p->sv, p->B, p->H, nk, p->v, es)) != ATTN_OK) return st;
   if ((st = check_view("O", p->so, p->B, p->H, p->n, p->v, es)) != ATTN_OK) return st;
   return ATTN_OK;
 }
@@ -209,6 +219,8 @@ eta::MapParams map_params(const attn_problem& p, const Tiles& t, uint8_t* map, i
   m.mask_si = p.mask_si;
   m.map = map;
   m.n = p.n;
+  m.nk = nkeys(p);
+  m.coff = p.causal_offset;
   m.B = (int32_t)p.B;
   m.H = (int32_t)p.H;
   m.units = units;
@@ -253,8 +265,8 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
   const int es = p->dtype == ATTN_BF16 ? 2 : 4;
   const int64_t Lst[3] = {p->H * p->n, p->n, 1};
   const Range rq = view_range(Q, p->sq, p->B, p->H, p->n, p->d, es);
-  const Range rk = view_range(K, p->sk, p->B, p->H, p->n, p->d, es);
-  const Range rv = view_range(V, p->sv, p->B, p->H, p->n, p->v, es);
+  const Range rk = view_range(K, p->sk, p->B, p->H, nkeys(*p), p->d, es);
+  const Range rv = view_range(V, p->sv, p->B, p->H, nkeys(*p), p->v, es);
   const Range ro = view_range(O, p->so, p->B, p->H, p->n, p->v, es);
   const Range rl = view_range(L, Lst, p->B, p->H, p->n, 1, 4);
   for (const Range& in : {rq, rk, rv}) {
@@ -292,6 +304,8 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
   f.mask_si = p->mask_si;
   fill_common(*p, f.sq, f.sk, f.sv, f.so);
   f.n = p->n;
+  f.nk = nkeys(*p);
+  f.coff = p->causal_offset;
   f.B = (int32_t)p->B;
   f.H = (int32_t)p->H;
   f.tq = (int32_t)t.tq;
@@ -317,14 +331,14 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   const int es = p->dtype == ATTN_BF16 ? 2 : 4;
   const int64_t Lst[3] = {p->H * p->n, p->n, 1};
   const Range ins[6] = {view_range(Q, p->sq, p->B, p->H, p->n, p->d, es),
-                        view_range(K, p->sk, p->B, p->H, p->n, p->d, es),
-                        view_range(V, p->sv, p->B, p->H, p->n, p->v, es),
+                        view_range(K, p->sk, p->B, p->H, nkeys(*p), p->d, es),
+                        view_range(V, p->sv, p->B, p->H, nkeys(*p), p->v, es),
                         view_range(O, p->so, p->B, p->H, p->n, p->v, es),
                         view_range(dO, p->so, p->B, p->H, p->n, p->v, es),
                         view_range(L, Lst, p->B, p->H, p->n, 1, 4)};
   const Range outs[3] = {view_range(dQ, p->sq, p->B, p->H, p->n, p->d, es),
-                         view_range(dK, p->sk, p->B, p->H, p->n, p->d, es),
-                         view_range(dV, p->sv, p->B, p->H, p->n, p->v, es)};
+                         view_range(dK, p->sk, p->B, p->H, nkeys(*p), p->d, es),
+                         view_range(dV, p->sv, p->B, p->H, nkeys(*p), p->v, es)};
   const char* onames[3] = {"dQ", "dK", "dV"};
   for (int i = 0; i < 3; ++i) {
     for (const Range& in : ins)
@@ -364,6 +378,8 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.mask_si = p->mask_si;
   fill_common(*p, b.sq, b.sk, b.sv, b.so);
   b.n = p->n;
+  b.nk = nkeys(*p);
+  b.coff = p->causal_offset;
   b.B = (int32_t)p->B;
   b.H = (int32_t)p->H;
   b.tq = (int32_t)t.tq;
@@ -466,6 +482,6 @@ attn_status attn_timing_reset(void) {
   return ATTN_OK;
 }
 
-int32_t attn_version(void) { return 100; }
+int32_t attn_version(void) { return 200; }
 
 }  // extern "C"

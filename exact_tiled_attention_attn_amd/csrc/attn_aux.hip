@@ -19,13 +19,13 @@ namespace eta {
 __global__ __launch_bounds__(256) void tile_map_kernel(MapParams p) {
   const int mu = blockIdx.x / p.tq;
   const int a = blockIdx.x % p.tq;
-  const int64_t n = p.n;
+  const int64_t n = p.n, nk = p.nk;  // query rows, key rows
   const int64_t q0 = (int64_t)a * p.bq;
   const int64_t q1 = (q0 + p.bq < n) ? q0 + p.bq : n;
   uint8_t* out = p.map + ((int64_t)mu * p.tq + a) * p.tk;
   if (p.mask_mode != kMaskBitmask) {
     for (int kt = threadIdx.x; kt < p.tk; kt += blockDim.x)
-      out[kt] = classify_analytic(p.mask_mode, q0, p.bq, (int64_t)kt * p.bk, p.bk, n);
+      out[kt] = classify_analytic(p.mask_mode, q0, p.bq, (int64_t)kt * p.bk, p.bk, n, nk, p.coff);
     return;
   }
   int64_t base;
@@ -34,12 +34,12 @@ __global__ __launch_bounds__(256) void tile_map_kernel(MapParams p) {
   } else {
     base = (int64_t)(mu / p.H) * p.mask_sb + (int64_t)(mu % p.H) * p.mask_sh;
   }
-  const int64_t W = (n + 31) / 32;
-  const uint32_t tail_bits = (n % 32) ? ((1u << (n % 32)) - 1u) : 0xFFFFFFFFu;
+  const int64_t W = (nk + 31) / 32;
+  const uint32_t tail_bits = (nk % 32) ? ((1u << (nk % 32)) - 1u) : 0xFFFFFFFFu;
   const int wpt = p.bk / 32;  // words per key tile
   for (int kt = threadIdx.x; kt < p.tk; kt += blockDim.x) {
     uint32_t any = 0;
-    bool all = (int64_t)(kt + 1) * p.bk <= n;
+    bool all = (int64_t)(kt + 1) * p.bk <= nk;
     for (int64_t r = q0; r < q1; ++r) {
       const uint32_t* row = p.mask + base + r * p.mask_si;
       for (int wi = 0; wi < wpt; ++wi) {

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const int unit = (int)(logical / p.tk);
   const int kt = (int)(logical % p.tk);  // low key tiles (most causal work) first
   const int b = unit / p.H, h = unit % p.H;
-  const int n = (int)p.n;
+  const int n = (int)p.n, nk = (int)p.nk, coff = (int)p.coff;  // query rows, key rows, causal offset
   const int k0 = kt * S::BK;
 
   const int tid = threadIdx.x;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const int g1 = (lane >> 4) & 1;
   const int klocal = 32 * w + (lane & 31);
   const int key = k0 + klocal;
-  const bool kvalid = key < n;
+  const bool kvalid = key < nk;
 
   const int qrow = (int)p.sq[2] * S::ES, krow = (int)p.sk[2] * S::ES;
   const int vrow = (int)p.sv[2] * S::ES, orow = (int)p.so[2] * S::ES;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   if constexpr (FUSED) {
     // Resident K tile in LDS (B operand of dQ), padded columns cleared.
     constexpr int KCH = S::DP * S::ES / 16;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (n - k0) * krow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
     for (int c = tid; c < S::BK * KCH; c += 256) {
       const int r = c / KCH, cc = c % KCH;
       u32x4 x = u32x4{0, 0, 0, 0};
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   constexpr int NKF = D / S::KSTEP, NVF = DV / S::KSTEP;
   Frag kf[NKF], vf[NVF];
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, n * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, n * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, nk * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, nk * vrow);
 #pragma unroll
     for (int s = 0; s < NKF; ++s) {
       if constexpr (BF16)
@@ -161,9 +161,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   for (int i = 0; i < S::NVB; ++i) dv[i] = f32x16{};
 
   // Query tiles are visited from the last down to the first one that can
-  // hold an allowed pair (causal: the tile containing row k0).
+  // hold an allowed pair (causal: the tile containing row k0 - coff).
   int qt_first = 0;
-  if constexpr (MASK == kMaskCausal) qt_first = k0 / S::BQ;
+  if constexpr (MASK == kMaskCausal) qt_first = k0 - coff > 0 ? (k0 - coff) / S::BQ : 0;
   const uint8_t* map_col = nullptr;
   const uint32_t* mbase = nullptr;
   if constexpr (MASK == kMaskBitmask) {
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   }
   auto tile_class = [&](int qt) -> uint8_t {
     if constexpr (MASK == kMaskBitmask) return map_col[(int64_t)qt * p.tk];
-    return classify_analytic(MASK, (int64_t)qt * S::BQ, S::BQ, k0, S::BK, n);
+    return classify_analytic(MASK, (int64_t)qt * S::BQ, S::BQ, k0, S::BK, n, nk, coff);
   };
   auto next_tile = [&](int qt) -> int {  // next (lower) tile with an allowed pair, or -1
     if constexpr (MASK != kMaskBitmask) return qt - 1 >= qt_first ? qt - 1 : -1;
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
         const int r = tid / S::MWORDS, wi = tid % S::MWORDS;
         const int qq = q0 + r;
         const int wd = (k0 >> 5) + wi;
-        mreg = (qq < n && wd * 32 < n) ? mbase[(int64_t)qq * p.mask_si + wd] : 0u;
+        mreg = (qq < n && wd * 32 < nk) ? mbase[(int64_t)qq * p.mask_si + wd] : 0u;
       }
     }
   };
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     const uint32_t* Ms = reinterpret_cast<const uint32_t*>(Dsv + S::BQ);
 
     bool active = true;
-    if constexpr (MASK == kMaskCausal) active = (k0 + 32 * w) <= (q0 + S::BQ - 1);  // wave-uniform
+    if constexpr (MASK == kMaskCausal) active = (k0 + 32 * w) <= (q0 + S::BQ - 1 + coff);  // wave-uniform
     if (active) {
 #pragma unroll
       for (int qb = 0; qb < S::NQB; ++qb) {
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
             if (cls == kTilePartial) {
               const int qq = q0 + ql + e;
               bool ok = kvalid;
-              if constexpr (MASK == kMaskCausal) ok = ok && key <= qq;
+              if constexpr (MASK == kMaskCausal) ok = ok && key <= qq + coff;
               if constexpr (MASK == kMaskBitmask)
                 ok = ok && ((Ms[(ql + e) * S::MWORDS + (klocal >> 5)] >> (klocal & 31)) & 1u);
               pv = ok ? pv : 0.f;

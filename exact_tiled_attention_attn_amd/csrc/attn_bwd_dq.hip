@@ -54,9 +54,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
   const int unit = (int)(logical / p.tq_dq);
   const int qt = p.tq_dq - 1 - (int)(logical % p.tq_dq);  // heaviest causal tiles first
   const int b = unit / p.H, h = unit % p.H;
-  const int n = (int)p.n;
+  const int n = (int)p.n, nk = (int)p.nk, coff = (int)p.coff;  // query rows, key rows, causal offset
   const int q0 = qt * S::BQ;
-  const int tk = (n + S::BK - 1) / S::BK;
+  const int tk = (nk + S::BK - 1) / S::BK;
 
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid % kWave;
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
 
   int kt_end = tk;
   if constexpr (MASK == kMaskCausal) {
-    const int q_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1;
-    kt_end = q_hi / S::BK + 1;
+    const int k_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1 + coff;  // last key any row allows
+    kt_end = k_hi < 0 ? 0 : (k_hi / S::BK + 1 < tk ? k_hi / S::BK + 1 : tk);
   }
   const uint8_t* map_row = nullptr;
   const uint32_t* mrow = nullptr;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
   }
   auto tile_class = [&](int kt) -> uint8_t {
     if constexpr (MASK == kMaskBitmask) return map_row[kt];
-    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n);
+    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n, nk, coff);
   };
   auto next_tile = [&](int kt) -> int {
     if constexpr (MASK != kMaskBitmask) return kt + 1;
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
   u32x4 kreg[S::KLD], vreg[S::VLD];
   auto gload = [&](int kt) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (n - k0) * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (n - k0) * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (nk - k0) * vrow);
 #pragma unroll
     for (int i = 0; i < S::KLD; ++i) {
       const int c = tid + i * 256;
@@ -182,19 +182,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
   }
   __syncthreads();
   int buf = 0;
-  const int wave_q_hi = q0 + 32 * w + 31;
+  const int wave_k_hi = q0 + 32 * w + 31 + coff;  // last key this wave's rows can allow
   const float scale2 = p.scale2;
 
   while (kt < kt_end) {
-    const int nk = next_tile(kt);
+    const int kn = next_tile(kt);
     const uint8_t cls = tile_class(kt);
-    if (nk < kt_end) gload(nk);
+    if (kn < kt_end) gload(kn);
     const int k0 = kt * S::BK;
     const char* Ks = smem + buf * (S::KTILE + S::VTILE);
     const char* Vs = Ks + S::KTILE;
 
     bool active = true;
-    if constexpr (MASK == kMaskCausal) active = k0 <= wave_q_hi;
+    if constexpr (MASK == kMaskCausal) active = k0 <= wave_k_hi;
     if (active) {
       f32x16 s[S::NKB], dp[S::NKB];
 #pragma unroll
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
       for (int kb = 0; kb < S::NKB; ++kb) {
         uint32_t word = 0xFFFFFFFFu;
         if constexpr (MASK == kMaskBitmask) {
-          if (cls == kTilePartial && qvalid && k0 + 32 * kb < n) word = mrow[(k0 + 32 * kb) >> 5];
+          if (cls == kTilePartial && qvalid && k0 + 32 * kb < nk) word = mrow[(k0 + 32 * kb) >> 5];
         }
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
@@ -240,8 +240,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
             if (cls == kTilePartial) {
               const int kk = 32 * kb + 8 * ((r + e) >> 2) + 4 * hh + ((r + e) & 3);
               const int key = k0 + kk;
-              bool ok = key < n;
-              if constexpr (MASK == kMaskCausal) ok = ok && key <= q;
+              bool ok = key < nk;
+              if constexpr (MASK == kMaskCausal) ok = ok && key <= q + coff;
               if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> (kk & 31)) & 1u);
               pv = ok ? pv : 0.f;
             }
@@ -282,10 +282,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
           }
       }
     }
-    if (nk < kt_end) lstore(buf ^ 1);
+    if (kn < kt_end) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
-    kt = nk;
+    kt = kn;
   }
 
   // dQ = c dQ^T (lane = query row; 4 consecutive columns per store).
@@ -333,7 +333,7 @@ static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, hipStrea
 }
 
 int launch_bwd_dq(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream) {
-  if (bwd_dq_pipe_supported(bf16, d, v, mask_mode, p.n)) return launch_bwd_dq_pipe(p, d, v, mask_mode, stream);
+  if (bwd_dq_pipe_supported(bf16, d, v, mask_mode, p.nk)) return launch_bwd_dq_pipe(p, d, v, mask_mode, stream);
   hipStream_t st = (hipStream_t)stream;
   return bf16 ? launch_dims<true>(p, d, v, mask_mode, st) : launch_dims<false>(p, d, v, mask_mode, st);
 }

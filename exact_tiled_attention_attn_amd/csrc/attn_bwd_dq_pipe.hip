@@ -100,9 +100,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   const int unit = (int)(logical / p.tq_dq);
   const int qt = p.tq_dq - 1 - (int)(logical % p.tq_dq);  // heaviest causal tiles first
   const int b = unit / p.H, h = unit % p.H;
-  const int n = (int)p.n;
+  const int n = (int)p.n, nk = (int)p.nk, coff = (int)p.coff;  // query rows, key rows, causal offset
   const int q0 = qt * S::BQ;
-  const int tk = (n + S::BK - 1) / S::BK;
+  const int tk = (nk + S::BK - 1) / S::BK;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -130,13 +130,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   }
 
   // Key-tile sequence: ascending, up to the last tile that can hold an
-  // allowed pair (causal: the tile containing the last query row); bitmask
+  // allowed pair (causal: the tile holding the last key the last row allows); bitmask
   // tiles come from the tile map, staged in LDS so that the loop issues no
   // loads of its own.
   int kt_end = tk;
   if constexpr (MASK == kMaskCausal) {
-    const int q_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1;
-    kt_end = q_hi / S::BK + 1;
+    const int k_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1 + coff;  // last key any row allows
+    kt_end = k_hi < 0 ? 0 : (k_hi / S::BK + 1 < tk ? k_hi / S::BK + 1 : tk);
   }
   if constexpr (MASK == kMaskBitmask) {
     const int64_t mu = p.mask_sb == 0 ? h : unit;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   }
   auto tile_class = [&](int kt) -> uint8_t {
     if constexpr (MASK == kMaskBitmask) return cls_s[kt];
-    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n);
+    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n, nk, coff);
   };
   auto next_tile = [&](int kt) -> int {  // next (higher) tile with an allowed pair, or -1
     if (kt < 0) return -1;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   auto vwin = [&](const i32x4& rv, int st, int i) { win_item(rv, vs_l + st * S::VTILE, vfirst, VB, VX, vsrc, i); };
   auto fill = [&](int kt, int st) {  // kt < 0: empty ranges, same instructions
     const int k0 = kt < 0 ? 0 : kt * S::BK;
-    const int64_t rows = kt < 0 ? 0 : n - k0;
+    const int64_t rows = kt < 0 ? 0 : nk - k0;
     const i32x4 rk = rsrc_words(Kb + (int64_t)k0 * krow, rows * krow);
     const i32x4 rv = rsrc_words(Vb + (int64_t)k0 * vrow, rows * vrow);
 #pragma unroll
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   int fst = 0;
   auto fill_begin = [&](int kt, int st) {  // descriptors and the uneven rest
     const int k0 = kt < 0 ? 0 : kt * S::BK;
-    const int64_t rows = kt < 0 ? 0 : n - k0;
+    const int64_t rows = kt < 0 ? 0 : nk - k0;
     frk = rsrc_words(Kb + (int64_t)k0 * krow, rows * krow);
     frv = rsrc_words(Vb + (int64_t)k0 * vrow, rows * vrow);
     fst = st;
@@ -296,8 +296,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r) {
         const int kk = perm(8 * (r >> 2) + 4 * hh + (r & 3));
         const int key = k0 + 32 * c + kk;
-        bool ok = key < n;
-        if constexpr (MASK == kMaskCausal) ok = ok && key <= q;
+        bool ok = key < nk;
+        if constexpr (MASK == kMaskCausal) ok = ok && key <= q + coff;
         if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> kk) & 1u);
         sc[u][r] = ok ? sc[u][r] : masked_score;
       }

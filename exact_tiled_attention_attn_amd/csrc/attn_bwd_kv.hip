@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int unit = (int)(logical / p.tk);
   const int kt = (int)(logical % p.tk);  // low key tiles (most causal work) first
   const int b = unit / p.H, h = unit % p.H;
-  const int n = (int)p.n;
+  const int n = (int)p.n, nk = (int)p.nk, coff = (int)p.coff;  // query rows, key rows, causal offset
   const int k0 = kt * S::BK;
 
   const int tid = threadIdx.x;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int g1 = (lane >> 4) & 1;
   const int klocal = 32 * w + (lane & 31);
   const int key = k0 + klocal;
-  const bool kvalid = key < n;
+  const bool kvalid = key < nk;
 
   const int qrow = (int)p.sq[2] * 2, krow = (int)p.sk[2] * 2;
   const int vrow = (int)p.sv[2] * 2, orow = (int)p.so[2] * 2;
@@ -119,10 +119,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   for (int c = tid; c < S::NSTAGE * S::LDB / 16; c += 256) reinterpret_cast<u32x4*>(lds_ld)[c] = u32x4{0, 0, 0, 0};
 
   // Query-tile sequence: from the last tile down to the first that can hold
-  // an allowed pair (causal: the tile containing row k0); bitmask tiles come
+  // an allowed pair (causal: the tile containing row k0 - coff); bitmask tiles come
   // from the tile map, staged in LDS so that the loop issues no loads of its own.
   int qt_first = 0;
-  if constexpr (MASK == kMaskCausal) qt_first = k0 / S::BQ;
+  if constexpr (MASK == kMaskCausal) qt_first = k0 - coff > 0 ? (k0 - coff) / S::BQ : 0;
   if constexpr (MASK == kMaskBitmask) {
     const int64_t mu = p.mask_sb == 0 ? h : unit;
     const uint8_t* map_col = p.map + mu * (int64_t)p.tq * p.tk + kt;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   }
   auto tile_class = [&](int qt) -> uint8_t {
     if constexpr (MASK == kMaskBitmask) return cls_s[qt];
-    return classify_analytic(MASK, (int64_t)qt * S::BQ, S::BQ, k0, S::BK, n);
+    return classify_analytic(MASK, (int64_t)qt * S::BQ, S::BQ, k0, S::BK, n, nk, coff);
   };
   auto next_tile = [&](int qt) -> int {  // next (lower) tile with an allowed pair, or -1
     if (qt < 0) return -1;
@@ -143,8 +143,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // K and V rows of this wave's keys (B operands; lane column = key).
   bf16x8 kf[S::NQF], vf[S::NVF];
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, n * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, n * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, nk * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, nk * vrow);
 #pragma unroll
     for (int s = 0; s < S::NQF; ++s)
       kf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * krow + (16 * s + 8 * hh) * 2, 0, 0));
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     for (int r = 0; r < 16; ++r) {
       const int ql = 32 * c + perm(8 * (r >> 2) + 4 * hh + (r & 3));
       bool ok = kvalid;
-      if constexpr (MASK == kMaskCausal) ok = ok && key <= q0 + ql;
+      if constexpr (MASK == kMaskCausal) ok = ok && key <= q0 + ql + coff;
       if constexpr (MASK == kMaskBitmask) ok = ok && ((ms[ql * S::MWORDS + w] >> (lane & 31)) & 1u);
       sc[r] = ok ? sc[r] : masked_score;
     }

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int unit = (int)(logical / p.tq);
   const int qt = p.tq - 1 - (int)(logical % p.tq);  // heaviest causal tiles first
   const int b = unit / p.H, h = unit % p.H;
-  const int n = (int)p.n;
+  const int n = (int)p.n, nk = (int)p.nk, coff = (int)p.coff;  // query rows, key rows, causal offset
   const int q0 = qt * S::BQ;
 
   const int tid = threadIdx.x;
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Key-tile range and classification.
   int kt_end = p.tk;
   if constexpr (MASK == kMaskCausal) {
-    const int q_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1;
-    kt_end = q_hi / S::BK + 1;
+    const int k_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1 + coff;  // last key any row allows
+    kt_end = k_hi < 0 ? 0 : (k_hi / S::BK + 1 < p.tk ? k_hi / S::BK + 1 : p.tk);
   }
   const uint8_t* map_row = nullptr;
   const uint32_t* mrow = nullptr;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   auto tile_class = [&](int kt) -> uint8_t {
     if constexpr (MASK == kMaskBitmask) return map_row[kt];
-    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n);
+    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n, nk, coff);
   };
   // Next tile with an allowed pair (none/causal: every tile in [0, kt_end) has one).
   auto next_tile = [&](int kt) -> int {
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   u32x4 kreg[S::KLD], vreg[S::VLD];
   auto gload = [&](int kt) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (n - k0) * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (n - k0) * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (nk - k0) * vrow);
 #pragma unroll
     for (int i = 0; i < S::KLD; ++i) {
       const int c = tid + i * 256;
@@ -197,18 +197,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
   int buf = 0;
-  const int wave_q_hi = q0 + 32 * w + 31;
+  const int wave_k_hi = q0 + 32 * w + 31 + coff;  // last key this wave's rows can allow
 
   while (kt < kt_end) {
-    const int nk = next_tile(kt);
+    const int kn = next_tile(kt);
     const uint8_t cls = tile_class(kt);
-    if (nk < kt_end) gload(nk);
+    if (kn < kt_end) gload(kn);
     const int k0 = kt * S::BK;
     const char* Ks = smem + buf * (S::KTILE + S::VTILE);
     const char* Vs = Ks + S::KTILE;
 
     bool active = true;
-    if constexpr (MASK == kMaskCausal) active = k0 <= wave_q_hi;  // wave-uniform
+    if constexpr (MASK == kMaskCausal) active = k0 <= wave_k_hi;  // wave-uniform
     if (active) {
       // S^T = K Q^T for NKB blocks of 32 keys.
       f32x16 s[S::NKB];
@@ -235,14 +235,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (cls == kTilePartial) {
           uint32_t word = 0xFFFFFFFFu;
           if constexpr (MASK == kMaskBitmask) {
-            if (qvalid && k0 + 32 * kb < n) word = mrow[(k0 + 32 * kb) >> 5];
+            if (qvalid && k0 + 32 * kb < nk) word = mrow[(k0 + 32 * kb) >> 5];
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
             const int key = k0 + kk;
-            bool ok = key < n;
-            if constexpr (MASK == kMaskCausal) ok = ok && key <= q;
+            bool ok = key < nk;
+            if constexpr (MASK == kMaskCausal) ok = ok && key <= q + coff;
             if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> (kk & 31)) & 1u);
             s[kb][r] = ok ? s[kb][r] : -INFINITY;
           }
@@ -314,10 +314,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
       }
     }
-    if (nk < kt_end) lstore(buf ^ 1);
+    if (kn < kt_end) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
-    kt = nk;
+    kt = kn;
   }
 
   // Epilogue: O = acc / l, L = (m + log2 l) ln 2.
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int unit = (int)(logical / p.tq);
   const int qt = p.tq - 1 - (int)(logical % p.tq);  // heaviest causal tiles first
   const int b = unit / p.H, h = unit % p.H;
-  const int n = (int)p.n;
+  const int n = (int)p.n, nk = (int)p.nk, coff = (int)p.coff;  // query rows, key rows, causal offset
   const int q0 = qt * S::BQ;
 
   const int tid = threadIdx.x;
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int kt_end = p.tk;
   if constexpr (MASK == kMaskCausal) {
-    const int q_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1;
-    kt_end = q_hi / S::BK + 1;
+    const int k_hi = (q0 + S::BQ < n ? q0 + S::BQ : n) - 1 + coff;  // last key any row allows
+    kt_end = k_hi < 0 ? 0 : (k_hi / S::BK + 1 < p.tk ? k_hi / S::BK + 1 : p.tk);
   }
   const uint8_t* map_row = nullptr;
   const uint32_t* mrow = nullptr;
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   auto tile_class = [&](int kt) -> uint8_t {
     if constexpr (MASK == kMaskBitmask) return map_row[kt];
-    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n);
+    return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n, nk, coff);
   };
   auto next_tile = [&](int kt) -> int {
     if constexpr (MASK != kMaskBitmask) return kt + 1;
@@ -456,14 +456,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < S::VWIN; ++i) voff[i] = S::VT::fill_src((w + S::NW * i) * 1024 + 16 * lane, vrow);
   auto fill_k = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (n - k0) * krow);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
 #pragma unroll
     for (int i = 0; i < S::KWIN; ++i)
       if (S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS) dma16(r, buf + (w + S::NW * i) * 1024, koff[i]);
   };
   auto fill_v = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + (int64_t)k0 * vrow, (n - k0) * vrow);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + (int64_t)k0 * vrow, (nk - k0) * vrow);
 #pragma unroll
     for (int i = 0; i < S::VWIN; ++i)
       if (S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS) dma16(r, buf + (w + S::NW * i) * 1024, voff[i]);
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kbase = (lane & 31) * S::KS + 16 * hh;
   const int vbase = (4 * hh + ((lane & 15) >> 2)) * S::VS + (16 * g1 + 4 * (lane & 3)) * 2;
 
-  // V rows past n are multiplied by zero weights: clear both V buffers once
+  // V rows past nk are multiplied by zero weights: clear both V buffers once
   // so that they never hold non-finite bit patterns.
   for (int c = tid; c < S::VTILE / 16; c += 256) {
     reinterpret_cast<u32x4*>(vbuf0)[c] = u32x4{0, 0, 0, 0};
@@ -496,21 +496,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         sc[kb] = mfma_bf16(lds_read_b128(ks_s, kbase + 32 * kb * S::KS + 32 * ks), qf[ks], sc[kb]);
   };
 
-  // Masking of a partially allowed tile's scores (rows past n, causal, bitmask).
+  // Masking of a partially allowed tile's scores (keys past nk, causal, bitmask).
   auto mask_tile = [&](f32x16 (&sc)[S::NKB], int kt) {
     const int k0 = kt * S::BK;
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) {
       uint32_t word = 0xFFFFFFFFu;
       if constexpr (MASK == kMaskBitmask) {
-        if (qvalid && k0 + 32 * kb < n) word = mrow[(k0 + 32 * kb) >> 5];
+        if (qvalid && k0 + 32 * kb < nk) word = mrow[(k0 + 32 * kb) >> 5];
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
         const int key = k0 + kk;
-        bool ok = key < n;
-        if constexpr (MASK == kMaskCausal) ok = ok && key <= q;
+        bool ok = key < nk;
+        if constexpr (MASK == kMaskCausal) ok = ok && key <= q + coff;
         if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> (kk & 31)) & 1u);
         sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
       }

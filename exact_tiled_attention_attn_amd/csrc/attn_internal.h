@@ -35,7 +35,9 @@ struct FwdParams {
   const uint32_t* mask;
   int64_t mask_sb, mask_sh, mask_si;
   int64_t sq[3], sk[3], sv[3], so[3];
-  int64_t n;
+  int64_t n;         // query rows
+  int64_t nk;        // key rows
+  int64_t coff;      // causal: key j allowed for query i iff j <= i + coff
   int32_t B, H;
   int32_t tq, tk;
   int64_t total;     // B * H * tq work items
@@ -61,7 +63,9 @@ struct BwdParams {
   const uint32_t* mask;
   int64_t mask_sb, mask_sh, mask_si;
   int64_t sq[3], sk[3], sv[3], so[3];
-  int64_t n;
+  int64_t n;     // query rows
+  int64_t nk;    // key rows
+  int64_t coff;  // causal offset, as in FwdParams
   int32_t B, H;
   int32_t tq, tk;  // key-tile-outer tiling: tq query tiles, tk key tiles of kBwdBk
   int64_t total;
@@ -79,7 +83,8 @@ struct MapParams {
   const uint32_t* mask;
   int64_t mask_sb, mask_sh, mask_si;
   uint8_t* map;
-  int64_t n;
+  int64_t n, nk;  // query and key rows
+  int64_t coff;   // causal offset
   int32_t B, H;
   int32_t units;  // distinct masks: H (batch-shared) or B * H
   int32_t bq, bk, tq, tk;
@@ -95,9 +100,9 @@ bool bwd_kv_supported(int bf16, int d, int v, int mask_mode, int64_t tq);
 int launch_bwd_kv(const BwdParams& p, int d, int v, int mask_mode, void* stream);
 // Pipelined dQ kernel of the deterministic path; the tiling of the dQ pass
 // (and of its bitmask tile map) follows this choice.
-inline bool bwd_dq_pipe_supported(int bf16, int64_t d, int64_t v, int mask_mode, int64_t n) {
+inline bool bwd_dq_pipe_supported(int bf16, int64_t d, int64_t v, int mask_mode, int64_t nk) {
   if (!bf16 || !((d == 128 && v == 128) || (d == 64 && v == 128) || (d == 64 && v == 64))) return false;
-  return mask_mode != 2 || (n + kDqPipeBk - 1) / kDqPipeBk <= kDqPipeMaxTk;
+  return mask_mode != 2 || (nk + kDqPipeBk - 1) / kDqPipeBk <= kDqPipeMaxTk;
 }
 int launch_bwd_dq_pipe(const BwdParams& p, int d, int v, int mask_mode, void* stream);
 int launch_tile_map(const MapParams& p, void* stream);

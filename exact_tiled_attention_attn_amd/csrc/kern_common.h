@@ -323,17 +323,18 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t bid, int64_t grid_pad, in
 }
 
 // Classification of a tile from its corners for none/causal masks: the same
-// rule the skip logic and the partial-tile masking follow.
+// rule the skip logic and the partial-tile masking follow.  nq query rows,
+// nk key rows; causal: key j allowed for query i iff j <= i + coff.
 __device__ __forceinline__ uint8_t classify_analytic(int mask_mode, int64_t q0, int bq, int64_t k0,
-                                                     int bk, int64_t n) {
-  int64_t q_hi = (q0 + bq < n ? q0 + bq : n) - 1;
-  int64_t k_hi = k0 + bk - 1;
+                                                     int bk, int64_t nq, int64_t nk, int64_t coff) {
+  const int64_t q_hi = (q0 + bq < nq ? q0 + bq : nq) - 1;
+  const int64_t k_hi = k0 + bk - 1;
   if (mask_mode == kMaskCausal) {
-    if (k0 > q_hi) return kTileEmpty;
-    if (k_hi <= q0 && k_hi < n) return kTileFull;
+    if (k0 > q_hi + coff) return kTileEmpty;
+    if (k_hi <= q0 + coff && k_hi < nk) return kTileFull;
     return kTilePartial;
   }
-  return (k_hi < n) ? kTileFull : kTilePartial;
+  return (k_hi < nk) ? kTileFull : kTilePartial;
 }
 
 }  // namespace eta

@@ -5,6 +5,8 @@
  * block-recomputed vector-Jacobian products", Inputs): for every (batch,
  * head) unit, positive n, d, v; Q, K in R^{n x d}; V in R^{n x v}; a real
  * scale c; nonempty allowed-key sets A_1..A_n.  With s_ij = c <Q_i, K_j>:
+ * (Rectangular problems, with n query rows and nk key rows and a causal
+ * offset, are described at attn_problem.nk.)
  *
  *   forward   O_i = sum_{j in A_i} exp(s_ij - L_i) V_j,
  *             L_i = ln sum_{j in A_i} exp(s_ij)            (natural log, fp32)
@@ -24,7 +26,7 @@
  * - All tensor pointers are DEVICE pointers.  The caller owns every buffer
  *   (inputs, outputs, mask, workspace); the library allocates nothing and
  *   keeps no state between calls except its loaded code objects.
- * - Q, K, V, O, dO, dQ, dK, dV are [B, H, n, .] with element strides
+ * - Q, K, V, O, dO, dQ, dK, dV are [B, H, n, .] (K, V, dK, dV: [B, H, nk, .]) with element strides
  *   (batch, head, row) given in attn_problem and a unit stride on the last
  *   dimension.  dQ, dK, dV use the strides of Q, K, V; dO uses those of O.
  *   Pointers must be 16-byte aligned and row/head/batch strides multiples
@@ -73,7 +75,7 @@ typedef enum {
  * demand; a caller-owned mask representation is input storage). */
 typedef enum {
   ATTN_MASK_NONE = 0,    /* A_i = {0..n-1} */
-  ATTN_MASK_CAUSAL = 1,  /* A_i = {j <= i} (ob1 page, part 3: block causal) */
+  ATTN_MASK_CAUSAL = 1,  /* A_i = {j <= i + causal_offset} (ob1 page, part 3: block causal) */
   ATTN_MASK_BITMASK = 2  /* explicit: bit (j & 31) of word j >> 5 of row i */
 } attn_mask_mode;
 
@@ -88,7 +90,7 @@ typedef struct {
   const uint32_t* mask;   /* BITMASK only: device words, LSB first, pad bits ignored */
   int64_t mask_sb;        /* mask strides in uint32 words: batch (0 = shared), */
   int64_t mask_sh;        /*   head, */
-  int64_t mask_si;        /*   row (>= ceil(n/32)) */
+  int64_t mask_si;        /*   row (>= ceil(nk/32)) */
   int64_t sq[3];          /* element strides [batch, head, row] of Q and dQ */
   int64_t sk[3];          /* ... of K and dK */
   int64_t sv[3];          /* ... of V and dV */
@@ -97,6 +99,18 @@ typedef struct {
                              kernel; 1 = dQ by a separate query-tile-outer
                              kernel (bitwise reproducible, no atomics) */
   int32_t reserved;       /* must be 0 */
+  /* Rectangular problems (maitreyasuin page, the tiled forward: Tq query
+   * rows against Tk key rows).  nk: rows of K, V, dK, dV; 0 means nk = n.
+   * causal_offset (CAUSAL only, else it must be 0): key j is allowed for
+   * query i iff j <= i + causal_offset.  0 is the square causal mask;
+   * nk - n aligns the last query with the last key (queries appended after
+   * a cache of keys); a shard of queries starting at absolute position qp
+   * against keys starting at kp uses qp - kp.  |causal_offset| <= 2^30.
+   * Rows left with no allowed key get O_i = 0, L_i = -inf (see above), so
+   * that results over disjoint key ranges merge exactly:
+   * L = ln sum_s exp(L_s), O = sum_s exp(L_s - L) O_s. */
+  int64_t nk;
+  int64_t causal_offset;
 } attn_problem;
 
 /* Bytes of device workspace attn_fwd (is_bwd = 0) or attn_bwd (is_bwd = 1)
@@ -109,7 +123,8 @@ attn_status attn_workspace_size(const attn_problem* p, int is_bwd, size_t* bytes
 
 /* Forward: O [B,H,n,v] (dtype) and L [B,H,n] (fp32, natural-log logsumexp
  * of the scaled allowed scores).  Kernels: bitmask tile classification
- * (bitmask mode only), then one fused tiled kernel per call. */
+ * (bitmask mode only), then one fused tiled kernel per call.  Rectangular
+ * problems: O and L have n rows, K and V nk rows. */
 attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const void* V,
                      void* O, float* L, void* workspace, size_t workspace_bytes,
                      void* stream);

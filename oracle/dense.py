@@ -46,7 +46,8 @@ def _check_rows(allowed):
 def forward(Q, K, V, c, allowed, row_chunk: int = 1024):
     """Y, m, l, L for one (batch, head) unit.
 
-    Q [n,d], K [n,d], V [n,v]; ``allowed`` bool [n,n] (None = all keys).
+    Q [n,d], K [nk,d], V [nk,v]; ``allowed`` bool [n,nk] (None = all keys);
+    nk = n for the square problems of the pages, any nk >= 1 otherwise.
     Returns float64 Y [n,v], m [n], l [n], L [n].
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)

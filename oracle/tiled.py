@@ -52,7 +52,7 @@ def _merge(m, l, z, m2, l2, z2):
 def forward(Q, K, V, c, allowed, b):
     """Forward procedure, steps 1-4.
 
-    Q [n,d], K [n,d], V [n,v]; ``allowed`` bool [n,n] (None = all keys);
+    Q [n,d], K [nk,d], V [nk,v]; ``allowed`` bool [n,nk] (None = all keys);
     ``b`` the key-block size.  Returns float64 Y [n,v], m [n], l [n] and
     L = m + ln l [n] (the logsumexp form of the retained statistics).
     """

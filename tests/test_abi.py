@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(E.EXPORTS)
     for name in names:
         assert getattr(lib, name) is not None
-    assert lib.attn_version() == 100
+    assert lib.attn_version() == 200
 
 
 def problem(B=1, H=2, n=100, d=64, v=64, dtype=1, mask_mode=0, contiguous=True):
@@ -116,6 +116,11 @@ def test_workspace_formula():
     (lambda p: p.sk.__setitem__(1, -6400), 3),
     (lambda p: p.so.__setitem__(1, 64 * 99), 3),  # heads overlap
     (lambda p: (setattr(p, "n", 1), p.sq.__setitem__(2, 1 << 31)), 6),  # row stride past 32-bit offsets
+    (lambda p: setattr(p, "nk", -1), 2),
+    (lambda p: setattr(p, "causal_offset", 3), 5),  # offset without the causal mask
+    (lambda p: (setattr(p, "mask_mode", 1), setattr(p, "causal_offset", (1 << 30) + 1)), 2),
+    (lambda p: (setattr(p, "mask_mode", 1), setattr(p, "causal_offset", -(1 << 30) - 1)), 2),
+    (lambda p: (setattr(p, "nk", 1 << 20), p.sk.__setitem__(1, 64 * 99)), 3),  # K heads overlap at nk rows
 ])
 def test_invalid_problem_rejected(mut, status):
     p = problem()
@@ -124,6 +129,34 @@ def test_invalid_problem_rejected(mut, status):
     assert call_bwd(p) == status, err()
     assert wsize(p, 0)[0] == status
     assert err() != ""
+
+
+def test_rectangular_problems():
+    """nk key rows (0 = n) and a causal offset: validation, tiling, workspace."""
+    p = problem(n=100)
+    p.nk, p.mask_mode, p.causal_offset = 0, 1, -40
+    assert wsize(p, 0) == (0, 0)
+    p.nk = 300  # K and V views [B, H, 300, .] inside their strides
+    for name, w in (("sk", 64), ("sv", 64)):
+        arr = getattr(p, name)
+        arr[0], arr[1], arr[2] = 2 * 300 * w, 300 * w, w
+    assert wsize(p, 0) == (0, 0) and wsize(p, 1)[0] == 0, err()
+    bq, bk, tq, tk = (ctypes.c_int32() for _ in range(4))
+    lib = E.load_library()
+    assert lib.attn_debug_tile_map(ctypes.byref(p), 0, None, 0, ctypes.byref(bq), ctypes.byref(bk),
+                                   ctypes.byref(tq), ctypes.byref(tk), None, 0, None) == 0
+    assert (tq.value, tk.value) == (-(-100 // bq.value), -(-300 // bk.value))
+    # Bitmask: a row holds ceil(nk / 32) words; the maps follow nk.
+    p.mask_mode, p.causal_offset = 2, 0
+    p.mask = FAKE + (6 << 30)
+    p.mask_sb, p.mask_sh, p.mask_si = 0, 100 * 10, 10  # ceil(300 / 32) = 10 words
+    st, bw = wsize(p, 1)
+    assert st == 0
+    rows = 2 * 128  # B H n_pad
+    map_kv = 2 * 2 * 3   # heads x (100 / 64 -> 2 query tiles) x (300 / 128 -> 3 key tiles)
+    assert bw == 4 * rows + 4 * rows + 4 * 1 * 2 * 100 * 64 + 256 * (-(-map_kv // 256))
+    p.mask_si = 9
+    assert wsize(p, 1)[0] == 5, err()
 
 
 def test_null_and_misaligned_pointers():

@@ -23,19 +23,19 @@ from oracle import dense
 from tests.payload import payload, traced_tiled_forward
 
 
-def _allowed(mask_mode, mask, n):
+def _allowed(mask_mode, mask, n, nk, offset=0):
     if mask_mode == "none":
         return lambda b, h: None
     if mask_mode == "causal":
-        A = W.causal_allowed(n)
+        A = W.causal_allowed(n, nk=nk, offset=offset)
         return lambda b, h: A
     words = mask.numpy().view(np.uint32)
-    return lambda b, h: W.unpack_bits(words[h] if words.ndim == 3 else words[b, h], n)
+    return lambda b, h: W.unpack_bits(words[h] if words.ndim == 3 else words[b, h], nk)
 
 
-def _oracle_fwd(q, k, v, scale, mask_mode="none", mask=None):
+def _oracle_fwd(q, k, v, scale, mask_mode="none", mask=None, causal_offset=0):
     B, H, n, _ = q.shape
-    A = _allowed(mask_mode, mask, n)
+    A = _allowed(mask_mode, mask, n, k.shape[2], causal_offset)
     o = torch.empty((B, H, n, v.shape[-1]), dtype=q.dtype)
     L = torch.empty((B, H, n), dtype=torch.float32)
     for b in range(B):
@@ -47,9 +47,10 @@ def _oracle_fwd(q, k, v, scale, mask_mode="none", mask=None):
     return o, L
 
 
-def _oracle_bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, deterministic=False, **_):
+def _oracle_bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, deterministic=False,
+                causal_offset=0, **_):
     B, H, n, _ = q.shape
-    A = _allowed(mask_mode, mask, n)
+    A = _allowed(mask_mode, mask, n, k.shape[2], causal_offset)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     for b in range(B):
         for h in range(H):
@@ -128,9 +129,9 @@ def test_only_requested_gradients(cpu_kernels):
 def test_default_scale_and_flags(cpu_kernels, monkeypatch):
     seen = {}
 
-    def fwd(q, k, v, scale, mask_mode="none", mask=None):
+    def fwd(q, k, v, scale, mask_mode="none", mask=None, causal_offset=0):
         seen["scale"], seen["mask"] = scale, mask_mode
-        return _oracle_fwd(q, k, v, scale, mask_mode, mask)
+        return _oracle_fwd(q, k, v, scale, mask_mode, mask, causal_offset)
 
     def bwd(*a, deterministic=False, **kw):
         seen["det"] = deterministic

@@ -135,10 +135,11 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 # Masks
 # ---------------------------------------------------------------------------
 
-def causal_allowed(n: int, rows=None) -> np.ndarray:
-    """A_i = {j <= i} (0-based) as a boolean [len(rows), n] array."""
+def causal_allowed(n: int, rows=None, nk: int | None = None, offset: int = 0) -> np.ndarray:
+    """A_i = {j <= i + offset} (0-based) over nk keys (default n), as bool [len(rows), nk]."""
+    nk = n if nk is None else nk
     rows = np.arange(n) if rows is None else np.asarray(rows)
-    return np.arange(n)[None, :] <= rows[:, None]
+    return np.arange(nk)[None, :] <= rows[:, None] + offset
 
 
 def window_allowed(n: int, window: int, rows=None) -> np.ndarray:
