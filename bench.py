@@ -73,6 +73,11 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--deterministic", type=int, default=1, choices=(0, 1),
                     help="backward dQ path: 1 = query-tile-outer kernel (default), 0 = fp32 atomics")
+    ap.add_argument("--queries", type=int, default=0,
+                    help="rectangular run: only the last QUERIES query rows against all n keys, causal "
+                         "offset n - QUERIES (the last shard of a query-sharded sequence); 0 = square")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability on the attention weights (seed 1234); 0 = none")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -162,7 +167,18 @@ def main():
     E.load_library()  # fail loudly if the HIP library is missing
     prob = W.generate(args.workload)
     w = prob.w
-    pairs = W.allowed_pairs(w, prob)
+    nq, coff = w.n, 0
+    if args.queries:
+        if w.mask == W.MASK_BITMASK or not 0 < args.queries <= w.n:
+            print("--queries needs a none/causal workload and 0 < QUERIES <= n", file=sys.stderr)
+            sys.exit(2)
+        nq = args.queries
+        coff = w.n - nq if w.mask == W.MASK_CAUSAL else 0
+        # Pairs per unit: row i (of the last nq) allows min(n, i + coff + 1) keys.
+        per_unit = nq * w.n if w.mask == W.MASK_NONE else sum(min(w.n, i + coff + 1) for i in range(nq))
+        pairs = w.B * w.H * per_unit
+    else:
+        pairs = W.allowed_pairs(w, prob)
     f_fwd, f_bwd = W.flops(w, pairs)
     dev = "cuda:0"
 
@@ -172,21 +188,24 @@ def main():
         return torch.from_numpy(getattr(prob, name)).to(dev)
 
     q, k, v, g = (up(x) for x in "QKVG")
+    if nq != w.n:
+        q, g = q[:, :, w.n - nq:].contiguous(), g[:, :, w.n - nq:].contiguous()
     mask = None
     if prob.mask_words is not None:
         mask = torch.from_numpy(prob.mask_words.view(np.int32)).to(dev)
-    o = torch.empty((w.B, w.H, w.n, w.v), dtype=q.dtype, device=dev)
-    lse = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.H, nq, w.v), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.B, w.H, nq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    pf = E.make_problem(q, k, v, o, w.scale, w.mask, mask)
+    drop = dict(dropout_p=args.dropout, dropout_seed=1234)
+    pf = E.make_problem(q, k, v, o, w.scale, w.mask, mask, causal_offset=coff, **drop)
     ws_f = torch.empty(max(E.workspace_size(pf, False), 256), dtype=torch.uint8, device=dev)
-    pf_b = E.make_problem(q, k, v, o, w.scale, w.mask, mask, bool(args.deterministic))
+    pf_b = E.make_problem(q, k, v, o, w.scale, w.mask, mask, bool(args.deterministic), coff, **drop)
     ws_b = torch.empty(max(E.workspace_size(pf_b, True), 256), dtype=torch.uint8, device=dev)
 
     def step():
-        E.fwd(q, k, v, w.scale, w.mask, mask, out=o, lse=lse, workspace=ws_f)
+        E.fwd(q, k, v, w.scale, w.mask, mask, out=o, lse=lse, workspace=ws_f, causal_offset=coff, **drop)
         E.bwd(q, k, v, o, g, lse, w.scale, w.mask, mask, dq=dq, dk=dk, dv=dv, workspace=ws_b,
-              deterministic=bool(args.deterministic))
+              deterministic=bool(args.deterministic), causal_offset=coff, **drop)
 
     for _ in range(args.warmup):
         step()
@@ -247,9 +266,15 @@ def main():
         "roofline": {"kernel": dominant, "flops_per_launch": kflops[dominant], "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(w.name, args.deterministic, dominant)},
+                     "traffic": (recorded_traffic(w.name, args.deterministic, dominant)
+                                 if nq == w.n and not args.dropout else None)},
     }
-    if not args.no_cpu_baseline:
+    if args.dropout:
+        out["config"].update(dropout_p=args.dropout, dropout_seed=1234)
+    if nq != w.n:
+        out["config"].update(queries=nq, keys=w.n, causal_offset=coff,
+                             workload=f"{w.name}, last {nq} query rows against all {w.n} keys")
+    if not args.no_cpu_baseline and nq == w.n and not args.dropout:
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
 

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     AttnProblem,
     bwd,
     debug_tile_map,
+    dropout_mask,
     fwd,
     load_library,
     make_problem,

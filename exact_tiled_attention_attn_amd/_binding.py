@@ -23,7 +23,7 @@ STATUS = {
     4: "ATTN_ERR_DTYPE", 5: "ATTN_ERR_MASK", 6: "ATTN_ERR_UNSUPPORTED",
     7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP",
 }
-EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map",
+EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask",
            "attn_timing_enable", "attn_timing_read", "attn_timing_reset",
            "attn_status_str", "attn_last_error", "attn_version"]
 KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post", "bwd_dq"]
@@ -47,6 +47,7 @@ class AttnProblem(ctypes.Structure):
         ("sv", ctypes.c_int64 * 3), ("so", ctypes.c_int64 * 3),
         ("deterministic", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("nk", ctypes.c_int64), ("causal_offset", ctypes.c_int64),
+        ("dropout_p", ctypes.c_double), ("dropout_seed", ctypes.c_uint64),
     ]
 
 
@@ -69,7 +70,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.attn_debug_tile_map.argtypes = [P, ctypes.c_int, vp, sz, i32p, i32p, i32p, i32p, vp, sz, vp]
-    for f in ("attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map"):
+    lib.attn_debug_dropout_mask.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_int32, vp, sz, vp]
+    for f in ("attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -98,12 +101,13 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, deterministic=False,
-                 causal_offset=0) -> AttnProblem:
+                 causal_offset=0, dropout_p=0.0, dropout_seed=0) -> AttnProblem:
     """Fill the ABI problem struct (strides in elements).
 
     q [B, H, n, d]; k [B, H, nk, d]; v [B, H, nk, v]; o_like [B, H, n, v].
     causal_offset (causal mask only): key j is allowed for query i iff
-    j <= i + causal_offset.
+    j <= i + causal_offset.  dropout_p / dropout_seed: dropout on the
+    weights, replayed by the backward with the same values (include/attn.h).
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("tensors must be [B, H, rows, dim]")
@@ -115,6 +119,8 @@ def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, determinis
     p.B, p.H, p.n, p.d, p.v = B, H, n, d, v.shape[-1]
     p.nk = nk
     p.causal_offset = int(causal_offset)
+    p.dropout_p = float(dropout_p)
+    p.dropout_seed = int(dropout_seed) & 0xFFFFFFFFFFFFFFFF
     p.dtype = _dtype_code(q)
     p.mask_mode = MASK_MODES[mask_mode] if isinstance(mask_mode, str) else int(mask_mode)
     p.scale = float(scale)
@@ -128,12 +134,18 @@ def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, determinis
         m = mask
         if m.dtype not in (torch.int32, torch.uint32):
             raise TypeError("mask must be int32/uint32 words")
+        words = (nk + 31) // 32
         if m.dim() == 3:  # [H, n, words]: shared across the batch
+            lead = (H, n)
             p.mask_sb, p.mask_sh, p.mask_si = 0, m.stride(0), m.stride(1)
         elif m.dim() == 4:  # [B, H, n, words]
+            lead = (B, H, n)
             p.mask_sb, p.mask_sh, p.mask_si = m.stride(0), m.stride(1), m.stride(2)
         else:
             raise ValueError("mask must be [H, n, words] or [B, H, n, words]")
+        # The library reads H (or B H) masks of n rows of ceil(nk / 32) words.
+        if tuple(m.shape[:-1]) != lead or m.shape[-1] < words or m.stride(-1) != 1:
+            raise ValueError(f"mask of shape {tuple(m.shape)} does not cover {lead} rows of {words} words")
         p.mask = m.data_ptr()
     p.deterministic = int(bool(deterministic))
     return p
@@ -161,7 +173,7 @@ def _ptr(t):
 
 
 def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, workspace=None,
-        causal_offset=0):
+        causal_offset=0, dropout_p=0.0, dropout_seed=0):
     """O [B,H,n,v] (dtype of q) and L [B,H,n] (fp32 natural-log logsumexp).
 
     q has n rows, k and v nk rows (any nk >= 1); causal_offset shifts the
@@ -171,7 +183,8 @@ def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, work
     B, H, n, _ = q.shape
     o = out if out is not None else torch.empty((B, H, n, v.shape[-1]), dtype=q.dtype, device=q.device)
     L = lse if lse is not None else torch.empty((B, H, n), dtype=torch.float32, device=q.device)
-    p = make_problem(q, k, v, o, scale, mask_mode, mask, causal_offset=causal_offset)
+    p = make_problem(q, k, v, o, scale, mask_mode, mask, causal_offset=causal_offset, dropout_p=dropout_p,
+                     dropout_seed=dropout_seed)
     need = workspace_size(p, False)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
@@ -180,7 +193,7 @@ def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, work
 
 
 def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=None, dv=None,
-        workspace=None, deterministic=False, causal_offset=0):
+        workspace=None, deterministic=False, causal_offset=0, dropout_p=0.0, dropout_seed=0):
     """dQ, dK, dV (dtype of q) from the forward's O and L and the upstream dO.
 
     ``deterministic`` selects the query-tile-outer dQ kernel (bitwise
@@ -198,7 +211,7 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
         raise ValueError("dQ, dK, dV must have the strides of Q, K, V")
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, H, n]")
-    p = make_problem(q, k, v, o, scale, mask_mode, mask, deterministic, causal_offset)
+    p = make_problem(q, k, v, o, scale, mask_mode, mask, deterministic, causal_offset, dropout_p, dropout_seed)
     need = workspace_size(p, True)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
@@ -225,6 +238,18 @@ def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=0, causal
                                    ctypes.byref(bq), ctypes.byref(bk), ctypes.byref(tq),
                                    ctypes.byref(tk), None, 0, _stream()))
     return out, bq.value, bk.value
+
+
+def dropout_mask(q, k, v, dropout_p, dropout_seed, b, h, i0, j0, rows, cols):
+    """The kernels' dropout keep decisions (uint8 [rows, cols], 1 = kept) of
+    unit (b, h), query rows i0.. and keys j0.. (multiples of 4)."""
+    lib = load_library()
+    o_like = torch.empty((*q.shape[:3], v.shape[-1]), device="meta")
+    p = make_problem(q, k, v, o_like, 1.0, dropout_p=dropout_p, dropout_seed=dropout_seed)
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_debug_dropout_mask(ctypes.byref(p), b, h, i0, j0, rows, cols, _ptr(out), out.numel(),
+                                       _stream()))
+    return out
 
 
 def timing_enable(on: bool = True):

@@ -31,13 +31,14 @@ class _Attention(torch.autograd.Function):
     """O, L = attention(Q, K, V); backward from (Q, K, V, O, L) alone."""
 
     @staticmethod
-    def forward(ctx, q, k, v, scale, mask_mode, mask, deterministic, causal_offset):
-        o, lse = _binding.fwd(q, k, v, scale, mask_mode, mask, causal_offset=causal_offset)
+    def forward(ctx, q, k, v, scale, mask_mode, mask, deterministic, causal_offset, dropout_p, dropout_seed):
+        o, lse = _binding.fwd(q, k, v, scale, mask_mode, mask, causal_offset=causal_offset, dropout_p=dropout_p,
+                              dropout_seed=dropout_seed)
         # The mask words are caller-owned input storage, like Q, K and V; they
         # are kept as a reference, not as saved state.
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.scale, ctx.mask_mode, ctx.mask, ctx.deterministic = scale, mask_mode, mask, deterministic
-        ctx.causal_offset = causal_offset
+        ctx.causal_offset, ctx.dropout = causal_offset, (dropout_p, dropout_seed)
         ctx.mark_non_differentiable(lse)
         ctx.set_materialize_grads(False)
         return o, lse
@@ -46,16 +47,17 @@ class _Attention(torch.autograd.Function):
     def backward(ctx, do, _dlse):
         q, k, v, o, lse = ctx.saved_tensors
         if do is None:
-            return (None,) * 8
+            return (None,) * 10
         dq, dk, dv = _binding.bwd(q, k, v, o, do, lse, ctx.scale, ctx.mask_mode, ctx.mask,
-                                  deterministic=ctx.deterministic, causal_offset=ctx.causal_offset)
+                                  deterministic=ctx.deterministic, causal_offset=ctx.causal_offset,
+                                  dropout_p=ctx.dropout[0], dropout_seed=ctx.dropout[1])
         needs = ctx.needs_input_grad
         return (dq if needs[0] else None, dk if needs[1] else None, dv if needs[2] else None,
-                None, None, None, None, None)
+                None, None, None, None, None, None, None)
 
 
 def attention(q, k, v, scale=None, mask_mode="none", mask=None, *, deterministic=True,
-              return_lse=False, causal_offset=0):
+              return_lse=False, causal_offset=0, dropout_p=0.0, dropout_seed=0):
     """Exact softmax attention, differentiable in Q, K, V.
 
     q [B, H, n, d]; k [B, H, nk, d]; v [B, H, nk, v] (nk may differ from n).
@@ -64,14 +66,16 @@ def attention(q, k, v, scale=None, mask_mode="none", mask=None, *, deterministic
     "none", "causal" or "bitmask" (then ``mask`` holds the LSB-first uint32
     words, [H, n, ceil(nk / 32)] or [B, H, n, ceil(nk / 32)]); with "causal",
     key j is allowed for query i iff j <= i + causal_offset.  deterministic
-    selects the bitwise-reproducible dQ pass.  L (fp32 natural-log
+    selects the bitwise-reproducible dQ pass.  dropout_p / dropout_seed:
+    dropout on the weights, the backward replaying the same keep decisions
+    (counter-based, nothing stored).  L (fp32 natural-log
     logsumexp per row) is returned with ``return_lse`` and carries no
     gradient.
     """
     if scale is None:
         scale = q.shape[-1] ** -0.5
     o, lse = _Attention.apply(q, k, v, float(scale), mask_mode, mask, bool(deterministic),
-                              int(causal_offset))
+                              int(causal_offset), float(dropout_p), int(dropout_seed))
     return (o, lse) if return_lse else o
 
 

@@ -40,6 +40,20 @@ struct Tiles {
 // Key rows (nk = 0 stands for nk = n).
 int64_t nkeys(const attn_problem& p) { return p.nk == 0 ? p.n : p.nk; }
 
+// Dropout in units of 1/256 (0 = off), and its kernel parameters.
+uint32_t drop_p8(const attn_problem& p) {
+  const double x = std::floor(p.dropout_p * 256.0 + 0.5);
+  return x >= 255.0 ? 255u : (uint32_t)x;
+}
+eta::DropParams drop_params(const attn_problem& p) {
+  eta::DropParams d{};
+  d.seed_lo = (uint32_t)(p.dropout_seed & 0xFFFFFFFFu);
+  d.seed_hi = (uint32_t)(p.dropout_seed >> 32);
+  d.p8 = drop_p8(p);
+  d.keep_inv = d.p8 ? (float)(256.0 / (256.0 - d.p8)) : 1.f;
+  return d;
+}
+
 Tiles fwd_tiles(const attn_problem& p) {
   return Tiles{eta::kFwdBq, eta::kFwdBk, cdiv(p.n, eta::kFwdBq), cdiv(nkeys(p), eta::kFwdBk)};
 }
@@ -54,7 +68,7 @@ int64_t mask_units(const attn_problem& p) { return p.mask_sb == 0 ? p.H : p.B * 
 
 Tiles dq_tiles(const attn_problem& p) {
   const int64_t nk = nkeys(p);
-  if (eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nk))
+  if (drop_p8(p) == 0 && eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nk))
     return Tiles{eta::kDqPipeBq, eta::kDqPipeBk, cdiv(p.n, eta::kDqPipeBq), cdiv(nk, eta::kDqPipeBk)};
   return Tiles{eta::kDqBq, eta::kDqBk, cdiv(p.n, eta::kDqBq), cdiv(nk, eta::kDqBk)};
 }
@@ -164,6 +178,8 @@ attn_status validate_problem(const attn_problem* p) {
     return fail(ATTN_ERR_MASK, "causal_offset applies to the causal mask only");
   if (p->causal_offset > (int64_t(1) << 30) || p->causal_offset < -(int64_t(1) << 30))
     return fail(ATTN_ERR_SHAPE, "|causal_offset| must be <= 2^30");
+  if (!(p->dropout_p >= 0.0 && p->dropout_p < 1.0))
+    return fail(ATTN_ERR_SHAPE, "dropout_p must be in [0, 1)");
   if (p->mask_mode == ATTN_MASK_BITMASK) {
     if (!p->mask) return fail(ATTN_ERR_MASK, "bitmask mode needs a mask");
     if (reinterpret_cast<uintptr_t>(p->mask) % 4)
@@ -313,6 +329,7 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
   f.total = p->B * p->H * t.tq;
   f.grid_pad = pad8(f.total);
   f.scale2 = (float)(p->scale * 1.4426950408889634);
+  f.drop = drop_params(*p);
   if (f.grid_pad > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
   return timed(ATTN_KERNEL_FWD, stream, "forward launch", [&] {
     return eta::launch_fwd(f, p->dtype == ATTN_BF16, (int)p->d, (int)p->v, p->mask_mode, stream);
@@ -388,6 +405,7 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.grid_pad = pad8(b.total);
   b.scale = (float)p->scale;
   b.scale2 = (float)(p->scale * 1.4426950408889634);
+  b.drop = drop_params(*p);
   const bool det = p->deterministic != 0;
   const Tiles tdq = dq_tiles(*p);
   b.map_dq = lay.map_dq_bytes ? reinterpret_cast<uint8_t*>(wsb + lay.off_map_dq) : nullptr;
@@ -445,6 +463,25 @@ attn_status attn_debug_tile_map(const attn_problem* p, int is_bwd, uint8_t* map_
   return hip_status(eta::launch_tile_map(mp, stream), "tile map launch");
 }
 
+attn_status attn_debug_dropout_mask(const attn_problem* p, int64_t b, int64_t h, int64_t i0, int64_t j0,
+                                    int32_t rows, int32_t cols, uint8_t* out_dev, size_t out_bytes,
+                                    void* stream) {
+  attn_status st = validate_problem(p);
+  if (st != ATTN_OK) return st;
+  if (drop_p8(*p) == 0) return fail(ATTN_ERR_UNSUPPORTED, "dropout is not enabled in this problem");
+  if (!out_dev) return fail(ATTN_ERR_NULL, "out_dev is NULL");
+  if (b < 0 || b >= p->B || h < 0 || h >= p->H) return fail(ATTN_ERR_SHAPE, "unit (b, h) out of range");
+  if (rows < 1 || cols < 1 || i0 < 0 || j0 < 0 || i0 % 4 || j0 % 4 || i0 + rows > (int64_t(1) << 31) ||
+      j0 + cols > (int64_t(1) << 31))
+    return fail(ATTN_ERR_SHAPE, "rows, cols >= 1 and i0, j0 non-negative multiples of 4 are required");
+  if (out_bytes < size_t(rows) * size_t(cols))
+    return fail(ATTN_ERR_WORKSPACE, "out buffer too small: %zu < %zu", out_bytes, size_t(rows) * size_t(cols));
+  eta::hip_last_launch_error();
+  return hip_status(eta::launch_dropout_mask(drop_params(*p), (uint32_t)(b * p->H + h), i0, j0, rows, cols,
+                                             out_dev, stream),
+                    "dropout mask launch");
+}
+
 const char* attn_status_str(int s) {
   switch (s) {
     case ATTN_OK: return "ok";
@@ -482,6 +519,6 @@ attn_status attn_timing_reset(void) {
   return ATTN_OK;
 }
 
-int32_t attn_version(void) { return 200; }
+int32_t attn_version(void) { return 300; }
 
 }  // extern "C"

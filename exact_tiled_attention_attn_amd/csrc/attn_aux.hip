@@ -166,6 +166,32 @@ int launch_bwd_post(const BwdParams& p, int bf16, int d, void* stream) {
   return (int)hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+
+// Dropout keep decisions of rows [i0, i0 + rows) x keys [j0, j0 + cols) of
+// one unit, one byte each: the same keep4_row draws the forward and dQ
+// kernels use (the key-tile-outer kernel draws the same blocks by column).
+__global__ __launch_bounds__(256) void dropout_mask_kernel(DropParams d, uint32_t unit, int64_t i0, int64_t j0,
+                                                           int rows, int cols, uint8_t* out) {
+  const int64_t groups = (int64_t)rows * ((cols + 3) / 4);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < groups; t += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(t / ((cols + 3) / 4)), c4 = (int)(t % ((cols + 3) / 4));
+    const uint32_t bits = keep4_row(d.seed_lo, d.seed_hi, d.p8, unit, (uint32_t)(i0 + r), (uint32_t)(j0 + 4 * c4));
+    for (int e = 0; e < 4 && 4 * c4 + e < cols; ++e) out[(int64_t)r * cols + 4 * c4 + e] = (bits >> e) & 1u;
+  }
+}
+
+int launch_dropout_mask(const DropParams& d, uint32_t unit, int64_t i0, int64_t j0, int rows, int cols,
+                        uint8_t* out, void* stream) {
+  const int64_t groups = (int64_t)rows * ((cols + 3) / 4);
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) return 0;
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, d, unit, i0,
+                     j0, rows, cols, out);
+  return (int)hipGetLastError();
+}
+
 const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
 int hip_last_launch_error() { return (int)hipGetLastError(); }
 

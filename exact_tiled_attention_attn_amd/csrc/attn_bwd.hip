@@ -68,7 +68,9 @@ struct BwdShape {
   static constexpr int smem(bool fused) { return 2 * BUF + (fused ? KTILE + STILE : 0); }
 };
 
-template <bool BF16, int D, int DV, int MASK, bool FUSED>
+// DROP: dropout replayed from the counter-based keep decisions of
+// kern_common.h: dV^T += (P o Z)^T dO / keep, dS = P ((dO V^T) o Z / keep - D).
+template <bool BF16, int D, int DV, int MASK, bool FUSED, bool DROP = false>
 __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   using S = BwdShape<BF16, D, DV>;
   __shared__ __attribute__((aligned(16))) char smem[S::smem(FUSED)];
@@ -317,6 +319,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
           const int ql = 32 * qb + 8 * g + 4 * hh;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dsv + ql);
+          // Dropout: query rows ql..ql+3 of this lane's key share one draw.
+          const uint32_t keep = DROP ? keep4_col(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8, (uint32_t)unit,
+                                                 (uint32_t)(q0 + ql), (uint32_t)key)
+                                     : 0xFu;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
@@ -329,8 +335,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
                 ok = ok && ((Ms[(ql + e) * S::MWORDS + (klocal >> 5)] >> (klocal & 31)) & 1u);
               pv = ok ? pv : 0.f;
             }
-            sc[r] = pv;
-            dp[r] = pv * (dp[r] - d4[e]);
+            if constexpr (DROP) {
+              const bool z = (keep >> e) & 1u;
+              sc[r] = z ? pv : 0.f;
+              dp[r] = pv * ((z ? dp[r] * p.drop.keep_inv : 0.f) - d4[e]);
+            } else {
+              sc[r] = pv;
+              dp[r] = pv * (dp[r] - d4[e]);
+            }
           }
         }
         // dV^T += dO^T P and dK^T += Q^T dS.
@@ -469,8 +481,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
       for (int g = 0; g < 4; ++g) {
         const int c0 = vb * 32 + 8 * g + 4 * hh;
         if (c0 < DV) {
-          const float x0 = dv[vb][4 * g], x1 = dv[vb][4 * g + 1];
-          const float x2 = dv[vb][4 * g + 2], x3 = dv[vb][4 * g + 3];
+          const float ks = DROP ? p.drop.keep_inv : 1.f;
+          const float x0 = dv[vb][4 * g] * ks, x1 = dv[vb][4 * g + 1] * ks;
+          const float x2 = dv[vb][4 * g + 2] * ks, x3 = dv[vb][4 * g + 3] * ks;
           if constexpr (BF16)
             *reinterpret_cast<u32x2*>(dVp + c0 * 2) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
           else
@@ -482,10 +495,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 
 template <bool BF16, int D, int DV, int MASK>
 static int launch_one(const BwdParams& p, bool fused, hipStream_t st) {
-  if (fused)
-    hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, true>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, false>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
+  const dim3 grid((unsigned)p.grid_pad), block(256);
+  if (p.drop.p8 != 0) {
+    if (fused) hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, false, true>), grid, block, 0, st, p);
+  } else if (fused) {
+    hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, true>), grid, block, 0, st, p);
+  } else {
+    hipLaunchKernelGGL((bwd_kernel<BF16, D, DV, MASK, false>), grid, block, 0, st, p);
+  }
   return (int)hipGetLastError();
 }
 
@@ -508,7 +526,8 @@ static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, bool fus
 }
 
 int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, bool fused, void* stream) {
-  if (!fused && bwd_kv_supported(bf16, d, v, mask_mode, p.tq)) return launch_bwd_kv(p, d, v, mask_mode, stream);
+  if (!fused && p.drop.p8 == 0 && bwd_kv_supported(bf16, d, v, mask_mode, p.tq))
+    return launch_bwd_kv(p, d, v, mask_mode, stream);
   hipStream_t st = (hipStream_t)stream;
   return bf16 ? launch_dims<true>(p, d, v, mask_mode, fused, st)
               : launch_dims<false>(p, d, v, mask_mode, fused, st);

@@ -44,7 +44,8 @@ struct DqShape {
   static constexpr int SMEM = 2 * (KTILE + VTILE);
 };
 
-template <bool BF16, int D, int DV, int MASK>
+// DROP: dS = P ((dO V^T) o Z / keep - D) with the replayed keep decisions.
+template <bool BF16, int D, int DV, int MASK, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1, 2))) void bwd_dq_kernel(BwdParams p) {
   using S = DqShape<BF16, D, DV>;
   __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
@@ -233,6 +234,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
         }
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
+          // Dropout: registers 4g..4g+3 hold 4 consecutive keys of this lane's query.
+          const uint32_t keep = DROP ? keep4_row(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8, (uint32_t)unit,
+                                                 (uint32_t)q, (uint32_t)(k0 + 32 * kb + 8 * (r >> 2) + 4 * hh))
+                                     : 0xFu;
           float ds[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
@@ -245,7 +250,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
               if constexpr (MASK == kMaskBitmask) ok = ok && ((word >> (kk & 31)) & 1u);
               pv = ok ? pv : 0.f;
             }
-            ds[e] = pv * (dp[kb][r + e] - Dq);
+            if constexpr (DROP) {
+              const bool z = (keep >> ((r + e) & 3)) & 1u;
+              ds[e] = pv * ((z ? dp[kb][r + e] * p.drop.keep_inv : 0.f) - Dq);
+            } else {
+              ds[e] = pv * (dp[kb][r + e] - Dq);
+            }
           }
           if constexpr (BF16)
             pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(ds[0], ds[1]);
@@ -310,7 +320,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
 
 template <bool BF16, int D, int DV, int MASK>
 static int launch_one(const BwdParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, DV, MASK>), dim3((unsigned)p.grid_pad_dq), dim3(256), 0, st, p);
+  if (p.drop.p8 != 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, DV, MASK, true>), dim3((unsigned)p.grid_pad_dq), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, DV, MASK>), dim3((unsigned)p.grid_pad_dq), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 
@@ -333,7 +346,8 @@ static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, hipStrea
 }
 
 int launch_bwd_dq(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream) {
-  if (bwd_dq_pipe_supported(bf16, d, v, mask_mode, p.nk)) return launch_bwd_dq_pipe(p, d, v, mask_mode, stream);
+  if (p.drop.p8 == 0 && bwd_dq_pipe_supported(bf16, d, v, mask_mode, p.nk))
+    return launch_bwd_dq_pipe(p, d, v, mask_mode, stream);
   hipStream_t st = (hipStream_t)stream;
   return bf16 ? launch_dims<true>(p, d, v, mask_mode, st) : launch_dims<false>(p, d, v, mask_mode, st);
 }

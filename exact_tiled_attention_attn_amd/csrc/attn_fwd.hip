@@ -57,7 +57,10 @@ struct FwdShape {
 // unnormalised weights <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
-template <bool BF16, int D, int DV, int MASK>
+// DROP: dropout on the weights (kern_common.h keep decisions): the PV
+// product takes the kept weights only, the normaliser and L stay those of
+// the undropped softmax, and O is scaled by 1 / P(keep).
+template <bool BF16, int D, int DV, int MASK, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdParams p) {
   using S = FwdShape<BF16, D, DV>;
   __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
@@ -269,20 +272,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       u32x4 pk[S::NKB][2];  // bf16 path: weights packed in pairs, one PV operand per 16 keys
+      // Dropout: registers 4g..4g+3 of block kb hold 4 consecutive keys, one draw.
+      uint32_t keep4[S::NKB][4];
+#pragma unroll
+      for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          keep4[kb][g] = DROP ? keep4_row(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8, (uint32_t)unit, (uint32_t)q,
+                                          (uint32_t)(k0 + 32 * kb + 8 * g + 4 * hh))
+                              : 0xFu;
 #pragma unroll
       for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
+          const uint32_t keep = keep4[kb][r >> 2];
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale2, neg_m));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale2, neg_m));
           l_run += p0 + p1;
+          const bool z0 = (keep >> (r & 3)) & 1u, z1 = (keep >> ((r + 1) & 3)) & 1u;
           if constexpr (BF16) {
             const uint32_t u = pack_bf16x2(p0, p1);
-            pk[kb][r / 8][(r / 2) % 4] = u;
+            pk[kb][r / 8][(r / 2) % 4] = DROP ? (u & ((z0 ? 0xFFFFu : 0u) | (z1 ? 0xFFFF0000u : 0u))) : u;
             l_use = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), ones_bf16x2(), l_use, false);
           } else {
-            s[kb][r] = p0;
-            s[kb][r + 1] = p1;
+            s[kb][r] = (!DROP || z0) ? p0 : 0.f;
+            s[kb][r + 1] = (!DROP || z1) ? p1 : 0.f;
           }
         }
       if constexpr (!BF16) l_use = l_run;
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Epilogue: O = acc / l, L = (m + log2 l) ln 2.
   const float l_tot = sum_halves(l_run);
   const float l_norm = sum_halves(l_use);
-  const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
+  const float inv = l_norm > 0.f ? (DROP ? p.drop.keep_inv : 1.f) / l_norm : 0.f;
   if (qvalid) {
     const int64_t obase = (int64_t)b * p.so[0] + (int64_t)h * p.so[1] + (int64_t)q * p.so[2];
 #pragma unroll
@@ -704,7 +718,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <bool BF16, int D, int DV, int MASK>
 static int launch_one(const FwdParams& p, hipStream_t st) {
   dim3 grid((unsigned)p.grid_pad), block(256);
-  if constexpr (BF16 && (D == 64 || D == 128) && (DV == 64 || DV == 128))
+  if (p.drop.p8 != 0)
+    hipLaunchKernelGGL((fwd_kernel<BF16, D, DV, MASK, true>), grid, block, 0, st, p);
+  else if constexpr (BF16 && (D == 64 || D == 128) && (DV == 64 || DV == 128))
     hipLaunchKernelGGL((fwd_pipe_kernel<D, DV, MASK>), grid, block, 0, st, p);
   else
     hipLaunchKernelGGL((fwd_kernel<BF16, D, DV, MASK>), grid, block, 0, st, p);

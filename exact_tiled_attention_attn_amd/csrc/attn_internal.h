@@ -25,6 +25,15 @@ constexpr int kDqPipeMaxTk = 4096;
 // multiple of every query tile), so that whole tiles can be copied.
 constexpr int kRowPad = 128;
 
+// Dropout on the attention weights (p8 / 256 = drop probability; p8 = 0:
+// none): counter-based keep decisions of kern_common.h, kept weights scaled
+// by keep_inv = 256 / (256 - p8).
+struct DropParams {
+  uint32_t seed_lo, seed_hi;
+  uint32_t p8;
+  float keep_inv;
+};
+
 struct FwdParams {
   const void* Q;
   const void* K;
@@ -43,6 +52,7 @@ struct FwdParams {
   int64_t total;     // B * H * tq work items
   int64_t grid_pad;  // total rounded up to a multiple of 8
   float scale2;      // c * log2(e): scores kept in the base-2 domain
+  DropParams drop;
 };
 
 struct BwdParams {
@@ -77,6 +87,7 @@ struct BwdParams {
   int32_t tq_dq;
   int64_t total_dq;
   int64_t grid_pad_dq;
+  DropParams drop;
 };
 
 struct MapParams {
@@ -105,6 +116,10 @@ inline bool bwd_dq_pipe_supported(int bf16, int64_t d, int64_t v, int mask_mode,
   return mask_mode != 2 || (nk + kDqPipeBk - 1) / kDqPipeBk <= kDqPipeMaxTk;
 }
 int launch_bwd_dq_pipe(const BwdParams& p, int d, int v, int mask_mode, void* stream);
+// Keep decisions of dropout for rows [i0, i0 + rows) x keys [j0, j0 + cols)
+// of one unit, as bytes 0 / 1 (row-major, `cols` per row); i0, j0 multiples of 4.
+int launch_dropout_mask(const DropParams& d, uint32_t unit, int64_t i0, int64_t j0, int rows, int cols,
+                        uint8_t* out, void* stream);
 int launch_tile_map(const MapParams& p, void* stream);
 int launch_bwd_pre(const BwdParams& p, int bf16, int d, int v, bool clear_dq, void* stream);
 int launch_bwd_post(const BwdParams& p, int bf16, int d, void* stream);

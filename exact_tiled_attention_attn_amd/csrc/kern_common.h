@@ -322,6 +322,52 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t bid, int64_t grid_pad, in
   return l < total ? l : -1;
 }
 
+// Dropout keep decisions, regenerated wherever they are needed (the reverse
+// pass replays the forward's mask without storing it).  Generator:
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011), counter (j / 4, i / 4, unit, 0), key
+// (seed_lo, seed_hi).  Its four words cover the 4 x 4 block of pairs with
+// i / 4, j / 4: pair (i, j) takes byte j % 4 (least significant first) of
+// word i % 4 as its 8-bit draw and is kept iff draw >= p8.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                              uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// Keep bits of the pairs (i, j0 + e), e = 0..3, for j0 % 4 == 0: bit e set
+// iff the pair is kept.
+__device__ __forceinline__ uint32_t keep4_row(uint32_t seed_lo, uint32_t seed_hi, uint32_t p8, uint32_t unit,
+                                              uint32_t i, uint32_t j0) {
+  uint32_t c0 = j0 >> 2, c1 = i >> 2, c2 = unit, c3 = 0;
+  philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
+  const uint32_t w = (i & 2) ? ((i & 1) ? c3 : c2) : ((i & 1) ? c1 : c0);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bits |= (((w >> (8 * e)) & 0xFFu) >= p8 ? 1u : 0u) << e;
+  return bits;
+}
+
+// Keep bits of the pairs (i0 + e, j), e = 0..3, for i0 % 4 == 0.
+__device__ __forceinline__ uint32_t keep4_col(uint32_t seed_lo, uint32_t seed_hi, uint32_t p8, uint32_t unit,
+                                              uint32_t i0, uint32_t j) {
+  uint32_t c0 = j >> 2, c1 = i0 >> 2, c2 = unit, c3 = 0;
+  philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
+  const uint32_t sh = 8 * (j & 3);
+  return (((c0 >> sh) & 0xFFu) >= p8 ? 1u : 0u) | (((c1 >> sh) & 0xFFu) >= p8 ? 2u : 0u) |
+         (((c2 >> sh) & 0xFFu) >= p8 ? 4u : 0u) | (((c3 >> sh) & 0xFFu) >= p8 ? 8u : 0u);
+}
+
 // Classification of a tile from its corners for none/causal masks: the same
 // rule the skip logic and the partial-tile masking follow.  nq query rows,
 // nk key rows; causal: key j allowed for query i iff j <= i + coff.

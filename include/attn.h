@@ -111,6 +111,18 @@ typedef struct {
    * L = ln sum_s exp(L_s), O = sum_s exp(L_s - L) O_s. */
   int64_t nk;
   int64_t causal_offset;
+  /* Dropout on the attention weights (the alphabetamath page names dropout
+   * only as an extension whose reverse pass must replay the forward's
+   * realised mask).  dropout_p in [0, 1) is used in units of 1/256:
+   * p8 = round(256 dropout_p); p8 = 0 disables dropout.  Pair (i, j) of
+   * unit u = b H + h is kept iff its 8-bit draw is >= p8: byte j % 4 of word
+   * i % 4 of Philox4x32-10 (Salmon et al., SC 2011) at counter
+   * (j / 4, i / 4, u, 0) and key (dropout_seed mod 2^32, dropout_seed div
+   * 2^32).  O_i = sum_j P_ij Z_ij V_j * 256 / (256 - p8), with P the
+   * undropped softmax, whose L is returned; attn_bwd with the same seed and
+   * dropout_p regenerates Z.  Runs on the register-staged kernels. */
+  double dropout_p;
+  uint64_t dropout_seed;
 } attn_problem;
 
 /* Bytes of device workspace attn_fwd (is_bwd = 0) or attn_bwd (is_bwd = 1)
@@ -154,6 +166,15 @@ attn_status attn_debug_tile_map(const attn_problem* p, int is_bwd, uint8_t* map_
                                 size_t map_bytes, int32_t* bq, int32_t* bk, int32_t* tq,
                                 int32_t* tk, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* Debug: the dropout keep decisions (1 = kept, 0 = dropped) the kernels use
+ * for unit (b, h), query rows [i0, i0 + rows) and keys [j0, j0 + cols), as
+ * rows * cols bytes, row-major, written to out_dev (out_bytes must hold
+ * them).  i0 and j0 must be multiples of 4, rows and cols >= 1; the problem
+ * must have dropout enabled (ATTN_ERR_UNSUPPORTED otherwise). */
+attn_status attn_debug_dropout_mask(const attn_problem* p, int64_t b, int64_t h, int64_t i0, int64_t j0,
+                                    int32_t rows, int32_t cols, uint8_t* out_dev, size_t out_bytes,
+                                    void* stream);
 
 /* Kernel classes reported by the timing facility below. */
 typedef enum {

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(E.EXPORTS)
     for name in names:
         assert getattr(lib, name) is not None
-    assert lib.attn_version() == 200
+    assert lib.attn_version() == 300
 
 
 def problem(B=1, H=2, n=100, d=64, v=64, dtype=1, mask_mode=0, contiguous=True):
@@ -121,6 +121,9 @@ def test_workspace_formula():
     (lambda p: (setattr(p, "mask_mode", 1), setattr(p, "causal_offset", (1 << 30) + 1)), 2),
     (lambda p: (setattr(p, "mask_mode", 1), setattr(p, "causal_offset", -(1 << 30) - 1)), 2),
     (lambda p: (setattr(p, "nk", 1 << 20), p.sk.__setitem__(1, 64 * 99)), 3),  # K heads overlap at nk rows
+    (lambda p: setattr(p, "dropout_p", 1.0), 2),
+    (lambda p: setattr(p, "dropout_p", -0.25), 2),
+    (lambda p: setattr(p, "dropout_p", float("nan")), 2),
 ])
 def test_invalid_problem_rejected(mut, status):
     p = problem()
@@ -157,6 +160,22 @@ def test_rectangular_problems():
     assert bw == 4 * rows + 4 * rows + 4 * 1 * 2 * 100 * 64 + 256 * (-(-map_kv // 256))
     p.mask_si = 9
     assert wsize(p, 1)[0] == 5, err()
+
+
+def test_dropout_mask_entry_validation():
+    lib = E.load_library()
+    p = problem()
+    out = FAKE
+    call = lambda pp, b=0, h=0, i0=0, j0=0, rows=4, cols=4, nbytes=16: lib.attn_debug_dropout_mask(  # noqa: E731
+        ctypes.byref(pp), b, h, i0, j0, rows, cols, ctypes.c_void_p(out), nbytes, None)
+    assert call(p) == 6, err()  # dropout not enabled
+    p.dropout_p = 0.001  # rounds to p8 = 0: still disabled
+    assert call(p) == 6, err()
+    p.dropout_p = 0.1
+    assert call(p, i0=2) == 2 and call(p, j0=6) == 2 and call(p, rows=0) == 2, err()
+    assert call(p, b=1) == 2 and call(p, h=2) == 2, err()
+    assert call(p, nbytes=15) == 7, err()
+    assert lib.attn_debug_dropout_mask(ctypes.byref(p), 0, 0, 0, 0, 4, 4, None, 16, None) == 1
 
 
 def test_null_and_misaligned_pointers():

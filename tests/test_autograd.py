@@ -33,7 +33,8 @@ def _allowed(mask_mode, mask, n, nk, offset=0):
     return lambda b, h: W.unpack_bits(words[h] if words.ndim == 3 else words[b, h], nk)
 
 
-def _oracle_fwd(q, k, v, scale, mask_mode="none", mask=None, causal_offset=0):
+def _oracle_fwd(q, k, v, scale, mask_mode="none", mask=None, causal_offset=0, dropout_p=0.0, dropout_seed=0):
+    assert dropout_p == 0.0
     B, H, n, _ = q.shape
     A = _allowed(mask_mode, mask, n, k.shape[2], causal_offset)
     o = torch.empty((B, H, n, v.shape[-1]), dtype=q.dtype)
@@ -48,7 +49,8 @@ def _oracle_fwd(q, k, v, scale, mask_mode="none", mask=None, causal_offset=0):
 
 
 def _oracle_bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, deterministic=False,
-                causal_offset=0, **_):
+                causal_offset=0, dropout_p=0.0, **_):
+    assert dropout_p == 0.0
     B, H, n, _ = q.shape
     A = _allowed(mask_mode, mask, n, k.shape[2], causal_offset)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -129,9 +131,9 @@ def test_only_requested_gradients(cpu_kernels):
 def test_default_scale_and_flags(cpu_kernels, monkeypatch):
     seen = {}
 
-    def fwd(q, k, v, scale, mask_mode="none", mask=None, causal_offset=0):
+    def fwd(q, k, v, scale, mask_mode="none", mask=None, causal_offset=0, **kw):
         seen["scale"], seen["mask"] = scale, mask_mode
-        return _oracle_fwd(q, k, v, scale, mask_mode, mask, causal_offset)
+        return _oracle_fwd(q, k, v, scale, mask_mode, mask, causal_offset, **kw)
 
     def bwd(*a, deterministic=False, **kw):
         seen["det"] = deterministic

@@ -1,0 +1,111 @@
+"""Dropout on the device against the float64 oracle (oracle/dropout.py).
+
+The reverse pass must replay the forward's realised mask (alphabetamath
+page, reverse procedure): the kernels regenerate each keep decision from
+(seed, unit, i, j) with Philox4x32-10, so the checks are
+
+* the kernels' keep decisions equal the oracle's, bit for bit;
+* O, L and dQ, dK, dV (both dQ paths) equal the oracle's dropout forward
+  and VJP taken with the oracle's own mask, within the dtype tolerance;
+* the same seed gives bitwise the same results, another seed other ones;
+* the autograd wrapper passes the dropout through to the backward.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import dropout
+from tests.gpu_common import DEV, compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(DEV)
+
+
+@pytest.mark.parametrize("seed,p,unit_bh,i0,j0,rows,cols", [
+    (0, 0.1, (0, 0), 0, 0, 64, 96), (12345678901234, 0.5, (1, 2), 120, 44, 37, 53),
+    ((1 << 64) - 1, 0.9, (0, 1), 4, 1000, 8, 5)])
+def test_keep_decisions_match_the_oracle(seed, p, unit_bh, i0, j0, rows, cols):
+    import exact_tiled_attention_attn_amd as E
+
+    B, H = 2, 3
+    q = torch.empty((B, H, 2048, 64), dtype=torch.bfloat16, device=DEV)
+    got = E.dropout_mask(q, q, q, p, seed, unit_bh[0], unit_bh[1], i0, j0, rows, cols)
+    torch.cuda.synchronize()
+    p8 = dropout.p8_of(p)
+    full = dropout.keep_mask(seed, unit_bh[0] * H + unit_bh[1], i0 + rows, j0 + cols, p8)
+    assert np.array_equal(got.cpu().numpy().astype(bool), full[i0:, j0:])
+
+
+DIMS = [("f32", 64, 64), ("f32", 80, 80), ("bf16", 128, 128), ("bf16", 64, 128)]
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "bitmask"])
+@pytest.mark.parametrize("dtype,d,v", DIMS)
+def test_dropout_parity(dtype, d, v, mask):
+    import exact_tiled_attention_attn_amd as E
+
+    B, H, n, nk, p, seed = 1, 2, 333, 333, 0.2, 2024
+    rng = np.random.default_rng(d + v + len(mask))
+    Q = rng.standard_normal((B, H, n, d), dtype=np.float32)
+    K = rng.standard_normal((B, H, nk, d), dtype=np.float32)
+    V = rng.standard_normal((B, H, nk, v), dtype=np.float32)
+    G = rng.standard_normal((B, H, n, v), dtype=np.float32)
+    if dtype == "bf16":
+        Q, K, V, G = (W.round_bf16(x) for x in (Q, K, V, G))
+    A, mdev = None, None
+    if mask == "causal":
+        A = W.causal_allowed(n)
+    elif mask == "bitmask":
+        A = (rng.random((n, nk)) < 0.3) | W.causal_allowed(n)
+        mdev = torch.from_numpy(W.pack_bits(np.stack([A] * H)).view(np.int32)).to(DEV)  # [H, n, words]
+    q, k, val, g = (_dev(x, dtype) for x in (Q, K, V, G))
+    c = 1 / np.sqrt(d)
+    kw = dict(dropout_p=p, dropout_seed=seed)
+    o, L = E.fwd(q, k, val, c, mask, mdev, **kw)
+    grads = {"atomic": E.bwd(q, k, val, o, g, L, c, mask, mdev, **kw),
+             "det": E.bwd(q, k, val, o, g, L, c, mask, mdev, deterministic=True, **kw)}
+    o2, L2 = E.fwd(q, k, val, c, mask, mdev, **kw)
+    o3, _ = E.fwd(q, k, val, c, mask, mdev, dropout_p=p, dropout_seed=seed + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(L, L2)  # the same seed replays the same mask
+    assert not torch.equal(o, o3)
+    p8 = dropout.p8_of(p)
+    got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    for h in range(H):
+        Z = dropout.keep_mask(seed, h, n, nk, p8)
+        Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
+        Y, Lr = dropout.forward(Qh, Kh, Vh, c, A, Z, p8)
+        rdQ, rdK, rdV = dropout.vjp(Qh, Kh, Vh, c, A, Z, p8, Gh)
+        tag = (dtype, d, v, mask, h)
+        compare("O", got(o[0, h]), Y, dtype, tag)
+        compare("L", got(L[0, h]), Lr, dtype, tag)
+        for path, (dq, dk, dv) in grads.items():
+            compare("dQ", got(dq[0, h]), rdQ, dtype, (tag, path))
+            compare("dK", got(dk[0, h]), rdK, dtype, (tag, path))
+            compare("dV", got(dv[0, h]), rdV, dtype, (tag, path))
+
+
+def test_autograd_passes_dropout_through():
+    import exact_tiled_attention_attn_amd as E
+
+    g0 = torch.Generator().manual_seed(0)
+    q, k, val, G = (torch.randn((1, 2, 200, 64), generator=g0).to(torch.bfloat16).to(DEV) for _ in range(4))
+    for t in (q, k, val):
+        t.requires_grad_(True)
+    o = E.attention(q, k, val, 0.125, "causal", dropout_p=0.3, dropout_seed=77)
+    o.backward(G)
+    ro, rl = E.fwd(q.detach(), k.detach(), val.detach(), 0.125, "causal", dropout_p=0.3, dropout_seed=77)
+    dq, dk, dv = E.bwd(q.detach(), k.detach(), val.detach(), ro, G, rl, 0.125, "causal", deterministic=True,
+                       dropout_p=0.3, dropout_seed=77)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), ro)
+    assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(val.grad, dv)
