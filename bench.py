@@ -229,7 +229,7 @@ def main():
     ms_step = total_ms / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     avg = {kname: (ms / cnt if cnt else 0.0) for kname, (ms, cnt) in kern.items()}
-    fwd_ms = avg["fwd"] + (avg["tile_map"] if w.mask == W.MASK_BITMASK else 0.0)
+    fwd_ms = avg["fwd"] + avg["fwd_merge"] + (avg["tile_map"] if w.mask == W.MASK_BITMASK else 0.0)
     n_maps_bwd = (2 if args.deterministic else 1) if w.mask == W.MASK_BITMASK else 0
     bwd_ms = avg["bwd_pre"] + avg["bwd"] + avg["bwd_post"] + avg["bwd_dq"] + n_maps_bwd * avg["tile_map"]
     peak = PEAK_TFLOPS[w.dtype]

@@ -77,7 +77,14 @@ struct Layout {
   size_t total = 0;
   size_t off_D = 0, off_L2 = 0, off_dQ = 0, off_map = 0, off_map_dq = 0;
   size_t map_bytes = 0, map_dq_bytes = 0, dq_bytes = 0;
+  int splits = 1;  // forward key-range splits
+  size_t off_Op = 0, off_Lp = 0, op_bytes = 0, lp_bytes = 0;
 };
+
+int fwd_split_count(const attn_problem& p) {
+  const Tiles t = fwd_tiles(p);
+  return eta::fwd_splits(p.dtype == ATTN_BF16, p.d, p.v, p.B * p.H, t.tq, t.tk, drop_p8(p));
+}
 
 // Backward workspace: D and L log2(e) (fp32 [B,H,n_pad] each, n_pad = n
 // rounded up to kRowPad); the atomic path adds the fp32 dQ accumulator, the
@@ -103,7 +110,13 @@ Layout plan(const attn_problem& p, int is_bwd) {
     const Tiles t = fwd_tiles(p);
     l.off_map = 0;
     l.map_bytes = p.mask_mode == ATTN_MASK_BITMASK ? size_t(mask_units(p) * t.tq * t.tk) : 0;
-    l.total = align_up(l.map_bytes);
+    l.splits = fwd_split_count(p);
+    const size_t rows = size_t(l.splits) * size_t(units) * size_t(p.n);
+    l.op_bytes = l.splits > 1 ? rows * size_t(p.v) * 4 : 0;
+    l.lp_bytes = l.splits > 1 ? rows * 4 : 0;
+    l.off_Op = align_up(l.map_bytes);
+    l.off_Lp = l.off_Op + align_up(l.op_bytes);
+    l.total = l.off_Lp + align_up(l.lp_bytes);
   }
   return l;
 }
@@ -326,14 +339,20 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
   f.H = (int32_t)p->H;
   f.tq = (int32_t)t.tq;
   f.tk = (int32_t)t.tk;
-  f.total = p->B * p->H * t.tq;
+  f.splits = lay.splits;
+  f.Opart = lay.op_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + lay.off_Op) : nullptr;
+  f.Lpart = lay.lp_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + lay.off_Lp) : nullptr;
+  f.total = p->B * p->H * t.tq * f.splits;
   f.grid_pad = pad8(f.total);
   f.scale2 = (float)(p->scale * 1.4426950408889634);
   f.drop = drop_params(*p);
   if (f.grid_pad > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
-  return timed(ATTN_KERNEL_FWD, stream, "forward launch", [&] {
-    return eta::launch_fwd(f, p->dtype == ATTN_BF16, (int)p->d, (int)p->v, p->mask_mode, stream);
-  });
+  if ((st = timed(ATTN_KERNEL_FWD, stream, "forward launch", [&] {
+         return eta::launch_fwd(f, p->dtype == ATTN_BF16, (int)p->d, (int)p->v, p->mask_mode, stream);
+       })) != ATTN_OK || f.splits == 1)
+    return st;
+  return timed(ATTN_KERNEL_FWD_MERGE, stream, "forward merge launch",
+               [&] { return eta::launch_fwd_merge(f, p->dtype == ATTN_BF16, (int)p->v, stream); });
 }
 
 attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const void* V, const void* O,

@@ -402,8 +402,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char vbuf0[S::VTILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[S::VTILE];
 
-  const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad, p.total);
-  if (logical < 0) return;
+  const int64_t logical0 = xcd_logical(blockIdx.x, p.grid_pad, p.total);
+  if (logical0 < 0) return;
+  const int split = (int)(logical0 % p.splits);  // key-range split (0 when not splitting)
+  const int64_t logical = logical0 / p.splits;
   const int unit = (int)(logical / p.tq);
   const int qt = p.tq - 1 - (int)(logical % p.tq);  // heaviest causal tiles first
   const int b = unit / p.H, h = unit % p.H;
@@ -562,7 +564,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     m_run = m_new;
   };
 
+  // This split's share of the key tiles [0, kt_end): [t0, kt_end).
   int t0 = 0;
+  if (p.splits > 1) {
+    const int per = (kt_end + p.splits - 1) / p.splits;
+    t0 = split * per < kt_end ? split * per : kt_end;
+    kt_end = t0 + per < kt_end ? t0 + per : kt_end;
+  }
   if (MASK == kMaskBitmask && t0 < kt_end && tile_class(t0) == kTileEmpty) t0 = next_tile(t0);
   __syncthreads();  // V buffers cleared
   if (t0 < kt_end) {  // workgroup-uniform
@@ -697,6 +705,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float l_tot = sum_halves(l_run);
   const float l_norm = l_tot;
   const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
+  if (p.splits > 1) {  // this split's normalised output and L, for fwd_merge_kernel
+    if (qvalid) {
+      const int64_t row = ((int64_t)split * p.B * p.H + unit) * n + q;
+      float* Op = p.Opart + row * DV;
+#pragma unroll
+      for (int vb = 0; vb < S::NVB; ++vb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int vd = vb * 32 + 8 * g + 4 * hh;
+          *reinterpret_cast<f32x4*>(Op + vd) =
+              f32x4{o[vb][4 * g] * inv, o[vb][4 * g + 1] * inv, o[vb][4 * g + 2] * inv, o[vb][4 * g + 3] * inv};
+        }
+      if (hh == 0)
+        p.Lpart[row] = (m_run == -INFINITY || l_tot <= 0.f) ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+    }
+    return;
+  }
   if (qvalid) {
     const int64_t obase = (int64_t)b * p.so[0] + (int64_t)h * p.so[1] + (int64_t)q * p.so[2];
 #pragma unroll
@@ -743,6 +768,52 @@ static int launch_dims(const FwdParams& p, int d, int v, int mask_mode, hipStrea
   if (d == 128 && v == 128) return launch_mask<BF16, 128, 128>(p, mask_mode, st);
   if (d == 64 && v == 128) return launch_mask<BF16, 64, 128>(p, mask_mode, st);
   return (int)hipErrorInvalidValue;
+}
+
+// Merge of the split forward's partial results: L = ln sum_s e^{L_s} and
+// O = sum_s e^{L_s - L} O_s (the merge of row summaries in its L form; a
+// split with no allowed key for the row has L_s = -inf and weight 0).  One
+// thread per (row, 4 output columns).
+template <bool BF16, int DV>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
+  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * (DV / 4)) return;
+  const int64_t row = t / (DV / 4);
+  const int c4 = (int)(t % (DV / 4));
+  float mx = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.Lpart[s * rows + row]);
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+  float L = -INFINITY;
+  if (mx != -INFINITY) {
+    float sum = 0.f;
+    for (int s = 0; s < p.splits; ++s) sum += expf(p.Lpart[s * rows + row] - mx);
+    L = mx + logf(sum);
+    for (int s = 0; s < p.splits; ++s) {
+      const float ws = expf(p.Lpart[s * rows + row] - L);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p.Opart + (s * rows + row) * DV + 4 * c4);
+      acc += f32x4{ws * x[0], ws * x[1], ws * x[2], ws * x[3]};
+    }
+  }
+  const int64_t unit = row / p.n, i = row % p.n;
+  const int64_t b = unit / p.H, h = unit % p.H;
+  const int64_t off = b * p.so[0] + h * p.so[1] + i * p.so[2] + 4 * c4;
+  if constexpr (BF16)
+    *reinterpret_cast<u32x2*>((char*)p.O + off * 2) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  else
+    *reinterpret_cast<f32x4*>((char*)p.O + off * 4) = acc;
+  if (c4 == 0) p.L[row] = L;
+}
+
+int launch_fwd_merge(const FwdParams& p, int bf16, int v, void* stream) {
+  const int64_t threads = (int64_t)p.B * p.H * p.n * (v / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  hipStream_t st = (hipStream_t)stream;
+  if (!bf16) return (int)hipErrorInvalidValue;  // splitting is a bf16-only path
+  if (v == 64) hipLaunchKernelGGL((fwd_merge_kernel<true, 64>), grid, block, 0, st, p);
+  else if (v == 128) hipLaunchKernelGGL((fwd_merge_kernel<true, 128>), grid, block, 0, st, p);
+  else return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
 }
 
 int launch_fwd(const FwdParams& p, int bf16, int d, int v, int mask_mode, void* stream) {

@@ -53,6 +53,14 @@ struct FwdParams {
   int64_t grid_pad;  // total rounded up to a multiple of 8
   float scale2;      // c * log2(e): scores kept in the base-2 domain
   DropParams drop;
+  // Split key ranges (pipelined bf16 forward only): splits > 1 runs
+  // B H tq splits workgroups, split s taking its share of a query tile's key
+  // tiles and writing its own normalised output and L (fp32) to Opart
+  // [splits][B H][n][v] and Lpart [splits][B H][n]; fwd_merge_kernel then
+  // combines them (ln-sum-exp of the L_s, exp(L_s - L) weights).
+  int32_t splits;
+  float* Opart;
+  float* Lpart;
 };
 
 struct BwdParams {
@@ -104,6 +112,18 @@ struct MapParams {
 
 // Launchers return a hipError_t value as int (0 = success).
 int launch_fwd(const FwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
+// Key-range splits the forward uses for this problem (1 = none; > 1 only
+// with the pipelined bf16 kernel, for few query tiles against many key tiles).
+inline int fwd_splits(int bf16, int64_t d, int64_t v, int64_t units, int64_t tq, int64_t tk, uint32_t p8) {
+  if (!bf16 || p8 != 0 || !((d == 64 || d == 128) && (v == 64 || v == 128))) return 1;
+  const int64_t wgs = units * tq;
+  if (wgs >= 256) return 1;
+  int64_t s = (512 + wgs - 1) / wgs;
+  if (s > tk / 4) s = tk / 4;  // at least four key tiles per split
+  if (s > 16) s = 16;
+  return s < 2 ? 1 : (int)s;
+}
+int launch_fwd_merge(const FwdParams& p, int bf16, int v, void* stream);
 int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, bool fused, void* stream);
 int launch_bwd_dq(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
 // Pipelined dK / dV kernel of the deterministic path (bf16, d and v in {64, 128}).

@@ -126,8 +126,10 @@ typedef struct {
 } attn_problem;
 
 /* Bytes of device workspace attn_fwd (is_bwd = 0) or attn_bwd (is_bwd = 1)
- * needs for this problem.  Forward: the tile map of bitmask mode (0 bytes
- * otherwise).  Backward: D (4 B H n bytes), plus the fp32 dQ accumulator
+ * needs for this problem.  Forward: the tile map of bitmask mode, and, when
+ * few query tiles face many key tiles (bf16, d and v in {64, 128}, no
+ * dropout), the partial results of the key-range splits, S B H n (v + 1) * 4
+ * bytes for S <= 16 splits (0 bytes if neither applies).  Backward: D (4 B H n bytes), plus the fp32 dQ accumulator
  * (4 B H n d bytes) when deterministic = 0, plus the bitmask tile map(s);
  * every region 256-byte aligned.  Validates the problem like the compute
  * calls. */
@@ -135,7 +137,10 @@ attn_status attn_workspace_size(const attn_problem* p, int is_bwd, size_t* bytes
 
 /* Forward: O [B,H,n,v] (dtype) and L [B,H,n] (fp32, natural-log logsumexp
  * of the scaled allowed scores).  Kernels: bitmask tile classification
- * (bitmask mode only), then one fused tiled kernel per call.  Rectangular
+ * (bitmask mode only), then one fused tiled kernel per call; with key-range
+ * splits (see attn_workspace_size) each split writes its own output and L,
+ * which a merge kernel combines exactly (L = ln sum_s e^{L_s},
+ * O = sum_s e^{L_s - L} O_s).  Rectangular
  * problems: O and L have n rows, K and V nk rows. */
 attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const void* V,
                      void* O, float* L, void* workspace, size_t workspace_bytes,
@@ -184,7 +189,8 @@ typedef enum {
   ATTN_KERNEL_BWD = 3,      /* key-tile-outer backward */
   ATTN_KERNEL_BWD_POST = 4, /* dQ conversion (deterministic = 0) */
   ATTN_KERNEL_BWD_DQ = 5,   /* query-tile-outer dQ (deterministic = 1) */
-  ATTN_KERNEL_COUNT = 6
+  ATTN_KERNEL_FWD_MERGE = 6, /* merge of the forward's key-range splits */
+  ATTN_KERNEL_COUNT = 7
 } attn_kernel;
 
 /* Opt-in kernel timing (off by default; not thread-safe; for measurement

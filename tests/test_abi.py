@@ -178,6 +178,30 @@ def test_dropout_mask_entry_validation():
     assert lib.attn_debug_dropout_mask(ctypes.byref(p), 0, 0, 0, 0, 4, 4, None, 16, None) == 1
 
 
+def test_forward_split_workspace():
+    """Few query tiles against many key tiles (bf16, d, v in {64, 128}): the
+    forward's workspace holds S <= 16 key-range splits of fp32 O and L."""
+    p = problem(B=1, H=2, n=100, d=128, v=128)
+    p.nk = 8192
+    for name, w in (("sk", 128), ("sv", 128)):
+        arr = getattr(p, name)
+        arr[0], arr[1], arr[2] = 2 * 8192 * w, 8192 * w, w
+    S = 16  # 2 query tiles' worth of work is far below one workgroup per CU
+    rows = S * 2 * 100
+    align = lambda x: -(-x // 256) * 256  # noqa: E731
+    assert wsize(p, 0) == (0, align(rows * 128 * 4) + align(rows * 4))
+    p.dropout_p = 0.2  # dropout runs on the register-staged kernel: no splits
+    assert wsize(p, 0) == (0, 0)
+    p.dropout_p, p.nk = 0.0, 1000  # 16 key tiles: four per split at most
+    for name, w in (("sk", 128), ("sv", 128)):
+        arr = getattr(p, name)
+        arr[0], arr[1], arr[2] = 2 * 1000 * w, 1000 * w, w
+    rows = 4 * 2 * 100
+    assert wsize(p, 0) == (0, align(rows * 128 * 4) + align(rows * 4))
+    p.dtype = 0  # fp32: no splits
+    assert wsize(p, 0) == (0, 0)
+
+
 def test_null_and_misaligned_pointers():
     p = problem()
     assert call_fwd(p, Q=0) == 1 and "Q" in err()

@@ -9,6 +9,8 @@ start - key start).  Checked against the float64 oracle:
 * O, L, dQ, dK, dV for none / causal-with-offset / bitmask masks, both dQ
   paths, with rows that allow no key giving O = 0, L = -inf and dQ = 0;
 * the kernels' tile classification, bit for bit;
+* short query blocks against long key ranges, where the forward splits the
+  key range over several workgroups and merges their partial results;
 * the one-GPU share of sequence sharding: results over disjoint key ranges
   merge exactly into the full result (L = ln sum_s e^{L_s},
   O = sum_s e^{L_s - L} O_s), and per-range gradients taken with the full
@@ -169,3 +171,46 @@ def test_key_ranges_merge_into_the_full_result(dtype, d, splits):
         for x, y in ((dQ, dQf), (dK, dKf), (dV, dVf)):
             ref = np.abs(got(y[0, h])).max()
             assert np.abs(got(x[0, h]) - got(y[0, h])).max() <= (1e-5 if dtype == "f32" else 2e-2) * ref
+
+
+SPLIT_SHAPES = [(100, 8192, "causal", 8092), (1, 4096, "causal", 4095), (128, 16384, "none", 0),
+                (64, 5000, "bitmask", 0), (200, 3000, "causal", -100), (129, 2048, "causal", 1919)]
+
+
+@pytest.mark.parametrize("n,nk,mask,off", SPLIT_SHAPES)
+@pytest.mark.parametrize("d,v", [(128, 128), (64, 128), (64, 64)])
+def test_split_key_forward(d, v, n, nk, mask, off):
+    """Few query tiles against many key tiles: the forward runs key-range splits
+    (visible as split workspace) and merges them; O and L against the oracle."""
+    import exact_tiled_attention_attn_amd as E
+
+    H, c, dtype = 2, 1.0 / np.sqrt(d), "bf16"
+    Q, K, V, G, rng = _inputs(H, n, nk, d, v, dtype, seed=n + nk + d + v)
+    As, mdev = _allowed(mask, n, nk, off, H, rng)
+    q, k, val = (_dev(x, dtype) for x in (Q, K, V))
+    o_like = torch.empty((1, H, n, v), dtype=torch.bfloat16, device=DEV)
+    prob = E.make_problem(q, k, val, o_like, c, mask, mdev, causal_offset=off)
+    map_bytes = 0 if mask != "bitmask" else -(-H * -(-n // 128) * -(-nk // 64) // 256) * 256
+    assert E.workspace_size(prob, False) > map_bytes, "key-range splits expected"
+    o, L = E.fwd(q, k, val, c, mask, mdev, causal_offset=off)
+    torch.cuda.synchronize()
+    got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    for h in range(H):
+        Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
+        rO, rL, _, _, _, rows = _oracle_fwd_only(Qh, Kh, Vh, c, As[h])
+        tag = (d, v, n, nk, mask, off, h)
+        empty = np.setdiff1d(np.arange(n), rows)
+        Oh, Lh = got(o[0, h]), got(L[0, h])
+        assert np.all(Oh[empty] == 0) and np.all(Lh[empty] == -np.inf), tag
+        compare("O", Oh[rows], rO[rows], dtype, tag)
+        compare("L", Lh, rL, dtype, tag)
+
+
+def _oracle_fwd_only(Q, K, V, c, A):
+    n, v = Q.shape[0], V.shape[1]
+    rows = np.nonzero(A.any(axis=1))[0]
+    O, L = np.zeros((n, v)), np.full(n, -np.inf)
+    if rows.size:
+        Y, _, _, Lr = dense.forward(Q[rows], K, V, c, A[rows])
+        O[rows], L[rows] = Y, Lr
+    return O, L, None, None, None, rows
