@@ -1,0 +1,113 @@
+"""Seeded sweep over combinations of the options, against the float64 oracle.
+
+Each case draws (dtype and dims, n, nk, mask, causal offset, dropout,
+scale) from a fixed seed, so the list is the same on every run.  The case
+runs attn_fwd and both attn_bwd paths and compares O, L, dQ, dK and dV with
+the oracle: the definition (oracle/dense.py), or with dropout the dropout
+oracle (oracle/dropout.py) under its own mask.  Rows that allow no key must
+give O = 0, L = -inf and dQ = 0.  The point is the interplay of options that
+the focused tests cover one at a time.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import dense, dropout, tiled
+from tests.gpu_common import DEV, compare, stored
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [("f32", 64, 64), ("f32", 80, 80), ("f32", 128, 128), ("f32", 64, 128),
+        ("bf16", 64, 64), ("bf16", 80, 80), ("bf16", 128, 128), ("bf16", 64, 128)]
+
+
+def _cases(count=40, seed=20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        dtype, d, v = DIMS[rng.integers(len(DIMS))]
+        n = int(rng.choice([1, 3, 31, 64, 65, 127, 200, 333, 513, 700]))
+        nk = n if rng.random() < 0.4 else int(rng.choice([1, 5, 64, 129, 300, 640, 1500]))
+        mask = ["none", "causal", "bitmask"][rng.integers(3)]
+        off = int(rng.integers(-n, nk + 1)) if mask == "causal" else 0
+        p = float(rng.choice([0.0, 0.0, 0.15, 0.5]))
+        scale = float(rng.choice([1 / np.sqrt(d), 0.3, -0.2, 0.0]))
+        out.append(pytest.param(i, dtype, d, v, n, nk, mask, off, p, scale,
+                                id=f"{i}-{dtype}-{d}x{v}-n{n}-nk{nk}-{mask}{off}-p{p}-c{scale:.3g}"))
+    return out
+
+
+def _dev(x, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(DEV)
+
+
+@pytest.mark.parametrize("i,dtype,d,v,n,nk,mask,off,p,scale", _cases())
+def test_sweep(i, dtype, d, v, n, nk, mask, off, p, scale):
+    import exact_tiled_attention_attn_amd as E
+
+    H, seed = 2, 1000 + i
+    rng = np.random.default_rng(i)
+    Q = rng.standard_normal((1, H, n, d), dtype=np.float32)
+    K = rng.standard_normal((1, H, nk, d), dtype=np.float32)
+    V = rng.standard_normal((1, H, nk, v), dtype=np.float32)
+    G = rng.standard_normal((1, H, n, v), dtype=np.float32)
+    if dtype == "bf16":
+        Q, K, V, G = (W.round_bf16(x) for x in (Q, K, V, G))
+    if mask == "none":
+        As, mdev = [None] * H, None
+    elif mask == "causal":
+        As, mdev = [W.causal_allowed(n, nk=nk, offset=off)] * H, None
+    else:
+        A = rng.random((H, n, nk)) < 0.35
+        As, mdev = list(A), torch.from_numpy(W.pack_bits(A).view(np.int32)).to(DEV)
+    q, k, val, g = (_dev(x, dtype) for x in (Q, K, V, G))
+    kw = dict(causal_offset=off, dropout_p=p, dropout_seed=seed)
+    o, L = E.fwd(q, k, val, scale, mask, mdev, **kw)
+    res = {"atomic": E.bwd(q, k, val, o, g, L, scale, mask, mdev, **kw),
+           "det": E.bwd(q, k, val, o, g, L, scale, mask, mdev, deterministic=True, **kw)}
+    torch.cuda.synchronize()
+    got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    p8 = dropout.p8_of(p)
+    for h in range(H):
+        Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
+        A = np.ones((n, nk), bool) if As[h] is None else As[h]
+        rows = np.nonzero(A.any(axis=1))[0]
+        empty = np.setdiff1d(np.arange(n), rows)
+        tag = (i, dtype, d, v, n, nk, mask, off, p, scale, h)
+        Oh, Lh = got(o[0, h]), got(L[0, h])
+        assert np.all(Oh[empty] == 0) and np.all(Lh[empty] == -np.inf), tag
+        for _, (dq, _, _) in res.items():
+            assert np.all(got(dq[0, h])[empty] == 0), tag
+        if rows.size == 0:
+            for _, (_, dk, dv) in res.items():
+                assert np.all(got(dk[0, h]) == 0) and np.all(got(dv[0, h]) == 0), tag
+            continue
+        Qr, Gr, Ar = Qh[rows], Gh[rows], A[rows]
+        if p8:
+            Z = dropout.keep_mask(seed, h, n, nk, p8)[rows]
+            Y, Lr = dropout.forward(Qr, Kh, Vh, scale, Ar, Z, p8)
+            rdQ, rdK, rdV = dropout.vjp(Qr, Kh, Vh, scale, Ar, Z, p8, Gr)
+        else:
+            Y, m, ell, Lr = dense.forward(Qr, Kh, Vh, scale, Ar)
+            rdQ, rdK, rdV = tiled.reverse(Qr, Kh, Vh, scale, Ar, nk, stored(Y, dtype), m, ell, Gr)
+        # Magnitude bounds for outputs whose exact value is zero (keys no row allows).
+        mq, mk, mv, mg = (float(np.abs(x).max(initial=0.0)) for x in (Qr, Kh, Vh, Gr))
+        kinv = 256 / (256 - p8)
+        bd = {"dQ": 2 * abs(scale) * mk * mg * mv * v * kinv + 1e-30,
+              "dK": 2 * abs(scale) * mq * mg * mv * v * rows.size * kinv + 1e-30,
+              "dV": mg * rows.size * kinv + 1e-30}
+        few = int(Ar.sum(axis=1).max()) <= 2  # every row has one or two keys: see tests/gpu_common.compare
+        cond = 4.0 if few else 1.0
+        compare("O", Oh[rows], Y, dtype, tag, elementwise=not few)
+        compare("L", Lh[rows], Lr, dtype, tag)
+        for path, (dq, dk, dv) in res.items():
+            for name, x, r in (("dQ", got(dq[0, h])[rows], rdQ), ("dK", got(dk[0, h]), rdK), ("dV", got(dv[0, h]), rdV)):
+                if few and dtype == "bf16" and name in ("dQ", "dK"):
+                    continue  # not asserted for 1-2 key problems in bf16 (the stored O's rounding dominates)
+                compare(name, x, r, dtype, (tag, path), bound=bd[name], elementwise=not few, cond=cond)
