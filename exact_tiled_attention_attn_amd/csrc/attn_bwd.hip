@@ -314,15 +314,26 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
         }
         // P = exp2(s c log2e - L log2e); dS = P (dP - D).  Register r holds
         // query row 32 qb + 8 (r/4) + 4 hh + r%4 of the tile.
+        // Dropout: rows 4g'..4g'+3 (g' = 8 g + 4 hh in the tile) of this lane's
+        // key form one draw group; the quad's lanes hold keys 4a..4a+3, so lane
+        // e of the quad draws group e for all four keys (keep_mask16) and each
+        // lane takes its key's nibble of every group.
+        uint32_t keepg[4] = {0xFu, 0xFu, 0xFu, 0xFu};
+        if constexpr (DROP) {
+          const uint32_t e = (uint32_t)lane & 3u;
+          const uint32_t m = keep_mask16(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8, (uint32_t)key >> 2,
+                                         (uint32_t)(q0 + 32 * qb + 8 * (int)e + 4 * hh) >> 2, (uint32_t)unit, true);
+          keepg[0] = (quad_bcast<0>(m) >> (4 * e)) & 0xFu;
+          keepg[1] = (quad_bcast<1>(m) >> (4 * e)) & 0xFu;
+          keepg[2] = (quad_bcast<2>(m) >> (4 * e)) & 0xFu;
+          keepg[3] = (quad_bcast<3>(m) >> (4 * e)) & 0xFu;
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ql = 32 * qb + 8 * g + 4 * hh;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dsv + ql);
-          // Dropout: query rows ql..ql+3 of this lane's key share one draw.
-          const uint32_t keep = DROP ? keep4_col(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8, (uint32_t)unit,
-                                                 (uint32_t)(q0 + ql), (uint32_t)key)
-                                     : 0xFu;
+          const uint32_t keep = keepg[g];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;

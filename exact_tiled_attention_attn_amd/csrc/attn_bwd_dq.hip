@@ -232,12 +232,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
         if constexpr (MASK == kMaskBitmask) {
           if (cls == kTilePartial && qvalid && k0 + 32 * kb < nk) word = mrow[(k0 + 32 * kb) >> 5];
         }
+        // Dropout: registers 4g..4g+3 hold 4 consecutive keys of this lane's
+        // row; the quad's lanes hold rows 4a..4a+3 (see the forward).
+        uint32_t keepg[4] = {0xFu, 0xFu, 0xFu, 0xFu};
+        if constexpr (DROP) {
+          const uint32_t e = (uint32_t)lane & 3u;
+          const uint32_t m = keep_mask16(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8,
+                                         (uint32_t)(k0 + 32 * kb + 8 * (int)e + 4 * hh) >> 2, (uint32_t)q >> 2,
+                                         (uint32_t)unit, false);
+          keepg[0] = (quad_bcast<0>(m) >> (4 * e)) & 0xFu;
+          keepg[1] = (quad_bcast<1>(m) >> (4 * e)) & 0xFu;
+          keepg[2] = (quad_bcast<2>(m) >> (4 * e)) & 0xFu;
+          keepg[3] = (quad_bcast<3>(m) >> (4 * e)) & 0xFu;
+        }
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          // Dropout: registers 4g..4g+3 hold 4 consecutive keys of this lane's query.
-          const uint32_t keep = DROP ? keep4_row(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8, (uint32_t)unit,
-                                                 (uint32_t)q, (uint32_t)(k0 + 32 * kb + 8 * (r >> 2) + 4 * hh))
-                                     : 0xFu;
+          const uint32_t keep = keepg[r >> 2];
           float ds[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {

@@ -272,15 +272,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       u32x4 pk[S::NKB][2];  // bf16 path: weights packed in pairs, one PV operand per 16 keys
-      // Dropout: registers 4g..4g+3 of block kb hold 4 consecutive keys, one draw.
+      // Dropout: registers 4g..4g+3 of block kb hold 4 consecutive keys of this
+      // lane's row; the quad's lanes hold rows 4a..4a+3, so lane g of the quad
+      // draws group g for all four rows (keep_mask16) and each lane takes its
+      // row's nibble of every group.
       uint32_t keep4[S::NKB][4];
 #pragma unroll
-      for (int kb = 0; kb < S::NKB; ++kb)
+      for (int kb = 0; kb < S::NKB; ++kb) {
+        if constexpr (DROP) {
+          const uint32_t e = (uint32_t)lane & 3u;
+          const uint32_t m = keep_mask16(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8,
+                                         (uint32_t)(k0 + 32 * kb + 8 * (int)e + 4 * hh) >> 2, (uint32_t)q >> 2,
+                                         (uint32_t)unit, false);
+          keep4[kb][0] = (quad_bcast<0>(m) >> (4 * e)) & 0xFu;
+          keep4[kb][1] = (quad_bcast<1>(m) >> (4 * e)) & 0xFu;
+          keep4[kb][2] = (quad_bcast<2>(m) >> (4 * e)) & 0xFu;
+          keep4[kb][3] = (quad_bcast<3>(m) >> (4 * e)) & 0xFu;
+        } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          keep4[kb][g] = DROP ? keep4_row(p.drop.seed_lo, p.drop.seed_hi, p.drop.p8, (uint32_t)unit, (uint32_t)q,
-                                          (uint32_t)(k0 + 32 * kb + 8 * g + 4 * hh))
-                              : 0xFu;
+          for (int g = 0; g < 4; ++g) keep4[kb][g] = 0xFu;
+        }
+      }
 #pragma unroll
       for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll

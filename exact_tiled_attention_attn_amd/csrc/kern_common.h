@@ -368,6 +368,34 @@ __device__ __forceinline__ uint32_t keep4_col(uint32_t seed_lo, uint32_t seed_hi
          (((c2 >> sh) & 0xFFu) >= p8 ? 4u : 0u) | (((c3 >> sh) & 0xFFu) >= p8 ? 8u : 0u);
 }
 
+// The four lanes of a quad share the 4 x 4 blocks of pairs they draw from:
+// in the forward-shaped layouts the quad holds rows 4a..4a+3 of the same
+// keys, in the key-tile-outer layout keys 4a..4a+3 of the same rows.  So
+// each lane computes one of the quad's four Philox calls (its group
+// g = lane % 4) and packs its 16 keep bits; quad_bcast<g> then hands every
+// lane the mask of group g.  keep_mask16 packs bit 4r + b (by_key = false:
+// one nibble per row r, bits over the 4 keys b) or 4b + r (by_key = true:
+// one nibble per key b, bits over the 4 rows r) for row r = word, key b =
+// byte of the call.
+__device__ __forceinline__ uint32_t keep_mask16(uint32_t seed_lo, uint32_t seed_hi, uint32_t p8, uint32_t jblk,
+                                                uint32_t iblk, uint32_t unit, bool by_key) {
+  uint32_t c0 = jblk, c1 = iblk, c2 = unit, c3 = 0;
+  philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
+  const uint32_t w[4] = {c0, c1, c2, c3};
+  uint32_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) m |= (((w[r] >> (8 * b)) & 0xFFu) >= p8 ? 1u : 0u) << (by_key ? 4 * b + r : 4 * r + b);
+  return m;
+}
+
+// Value of lane G of this lane's quad (DPP quad permutation, all lanes from lane G).
+template <int G>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, G | (G << 2) | (G << 4) | (G << 6), 0xF, 0xF, false);
+}
+
 // Classification of a tile from its corners for none/causal masks: the same
 // rule the skip logic and the partial-tile masking follow.  nq query rows,
 // nk key rows; causal: key j allowed for query i iff j <= i + coff.
