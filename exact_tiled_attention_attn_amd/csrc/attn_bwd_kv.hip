@@ -344,25 +344,52 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // started from -D); dni is -D of the next chunk, the start of ndp.  With
   // dload, the second phase also reads -D of chunk 1 of stage nst into dnx.
   f32x4 lv[4];
+  // Row operand i of a step's first phase (S, dP interleaved) for chunk c of stage st.
+  auto arow = [&](int st, int c, int i) -> bf16x8 {
+    const int si = (i * S::NQF) / S::NA, next = ((i + 1) * S::NQF) / S::NA;
+    if (next > si) return *reinterpret_cast<const bf16x8*>(qs + st * S::QTILE + 32 * c * S::QS + qrb + 32 * si);
+    return *reinterpret_cast<const bf16x8*>(os + st * S::OTILE + 32 * c * S::OS + orb + 32 * (i - si));
+  };
+  // First-phase row operands in flight across steps: a chunk-1 step loads the
+  // first kPrefetchA operands of the following step (its stage is already
+  // visible), which then starts without waiting for them.
+  bf16x8 afr[kPrefetchA];
   auto step = [&](auto dofill, f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc,
-                  const f32x16& dni, auto dload, f32x16& dnx, auto hook) {
-    const char* nqb = qs + nst * S::QTILE + 32 * nc * S::QS + qrb;
-    const char* nob = os + nst * S::OTILE + 32 * nc * S::OS + orb;
+                  const f32x16& dni, auto dload, f32x16& dnx, auto hook, auto pre_a) {
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS + qtb;
     const char* ob = os + st * S::OTILE + 32 * c * S::OS + otb;
     const float* nls = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_L) + 32 * nc + 4 * hh;
     const float* nds = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_D) + 32 * 1 + 4 * hh;
 
+    // MFMA j: even j -> dV block, odd -> dK block (while both remain).
+    auto bmfma = [&](int j, bool& is_v, int& blk, int& ks) {
+      constexpr int NV2 = 2 * S::NVB;
+      const int vi = (j * NV2) / S::NB, vnext = ((j + 1) * NV2) / S::NB;
+      is_v = vnext > vi;
+      const int idx = is_v ? vi : j - vi;
+      blk = idx % (is_v ? S::NVB : S::NDB);
+      ks = idx / (is_v ? S::NVB : S::NDB);
+    };
+    auto bread = [&](int j, i16x4& lo, i16x4& hi) {
+      bool is_v;
+      int blk, ks;
+      bmfma(j, is_v, blk, ks);
+      const char* base = is_v ? ob : qb;
+      const int stride = is_v ? S::OS : S::QS;
+      lo = lds_read_tr(base + 16 * ks * stride, 64 * blk);
+      hi = lds_read_tr(base + (16 * ks + 2) * stride, 64 * blk);
+    };
     // ---- phase A ----
     constexpr int PF = kPrefetchA;  // row operands in flight
-    auto aread = [&](int i) -> bf16x8 {  // operand of MFMA i: dP (ks) or S (ks), interleaved
-      const int si = (i * S::NQF) / S::NA, next = ((i + 1) * S::NQF) / S::NA;
-      if (next > si) return *reinterpret_cast<const bf16x8*>(nqb + 32 * si);
-      return *reinterpret_cast<const bf16x8*>(nob + 32 * (i - si));
-    };
-    bf16x8 afr[PF];
+    auto aread = [&](int i) -> bf16x8 { return arow(nst, nc, i); };  // operand of MFMA i (S, dP interleaved)
+    if constexpr (!decltype(pre_a)::value) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) afr[i] = aread(i);
+      for (int i = 0; i < PF; ++i) afr[i] = aread(i);
+    }
+    // Transposed operands of the second phase: the first PB are read during
+    // the first phase's last PB slices.
+    constexpr int PB = kPrefetchB;
+    i16x4 tlo[PB], thi[PB];
     u32x4 pk[2], sk[2];
     // Weights of row pair pr in two halves, issued one slice apart so that
     // the exponentials' latency is covered: e(pr) = exponentials, f(pr) = dS
@@ -393,6 +420,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         else mfma_vacc(ndp, afr[i % PF], vf[i - si]);
       }
       if (i + PF < S::NA) afr[i % PF] = aread(i + PF);
+      if (i >= S::NA - PB) bread(i - (S::NA - PB), tlo[i - (S::NA - PB)], thi[i - (S::NA - PB)]);
       if constexpr (decltype(dofill)::value) {
         if (i < FQ + FO) fill_item(i);
       }
@@ -406,28 +434,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     asm volatile("" ::"v"(dni));  // keep the init registers until its product is done
 
     // ---- phase B ----
-    // MFMA j: even j -> dV block, odd -> dK block (while both remain).
-    auto bmfma = [&](int j, bool& is_v, int& blk, int& ks) {
-      constexpr int NV2 = 2 * S::NVB;
-      const int vi = (j * NV2) / S::NB, vnext = ((j + 1) * NV2) / S::NB;
-      is_v = vnext > vi;
-      const int idx = is_v ? vi : j - vi;
-      blk = idx % (is_v ? S::NVB : S::NDB);
-      ks = idx / (is_v ? S::NVB : S::NDB);
-    };
-    auto bread = [&](int j, i16x4& lo, i16x4& hi) {
-      bool is_v;
-      int blk, ks;
-      bmfma(j, is_v, blk, ks);
-      const char* base = is_v ? ob : qb;
-      const int stride = is_v ? S::OS : S::QS;
-      lo = lds_read_tr(base + 16 * ks * stride, 64 * blk);
-      hi = lds_read_tr(base + (16 * ks + 2) * stride, 64 * blk);
-    };
-    constexpr int PB = kPrefetchB;  // transposed operands in flight (MFMAs ahead)
-    i16x4 tlo[PB], thi[PB];
-#pragma unroll
-    for (int j = 0; j < PB; ++j) bread(j, tlo[j], thi[j]);
     asm volatile("s_nop 1");  // the last packed P / dS operands were just written
     // Slice j: one MFMA, the reads PB MFMAs ahead and, for j < 8, one of the
     // next chunk's L log2(e) / D reads.
@@ -441,6 +447,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       if (is_v) mfma_aacc(dv[blk], a, __builtin_bit_cast(bf16x8, pk[ks]));
       else mfma_aacc(dk[blk], a, __builtin_bit_cast(bf16x8, sk[ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
+      if constexpr (decltype(dofill)::value) {  // chunk 1: the next step's first row operands
+        if (j >= S::NB - PF) afr[j - (S::NB - PF)] = arow(nst, 1, j - (S::NB - PF));
+      }
       if (j < 4) lv[j] = *reinterpret_cast<const f32x4*>(nls + 8 * j);
       if (j == 2) hook();
       if constexpr (decltype(dload)::value) {
@@ -476,6 +485,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       lv[g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds_ld + S::LD_L) + 8 * g + 4 * hh);
     // -D starts of chunk 1 of the current tile (dnA) and chunk 0 of the next (dnB).
     f32x16 dnA = load_dn(0, 1), dnB;
+#pragma unroll
+    for (int i = 0; i < kPrefetchA; ++i) afr[i] = arow(0, 1, i);  // the first step's first operands
     unsigned j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
     while (true) {
       const int st = (int)(j & (S::NSTAGE - 1)), nst = (int)((j + 1) & (S::NSTAGE - 1));
@@ -484,7 +495,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, q0);
       step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, dnA, std::false_type{}, dnA,
-           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); });
+           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); }, std::true_type{});
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3.
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       fill_begin();
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, q0);
-      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA, [] {});
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA, [] {}, std::false_type{});
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;
