@@ -335,23 +335,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // computed from whatever that stage holds (unused after the last chunk).
   //   phase A: MFMA S^T, dP^T (next chunk)   || VALU P, dS (this chunk)
   //   phase B: MFMA dQ^T (this chunk) with transposed K reads
+  // Row operand i of a step's first phase (K, V interleaved) for chunk c of stage st.
+  auto is_k = [](int i) { return ((i + 1) * S::NQF) / S::NR > (i * S::NQF) / S::NR; };
+  auto arow = [&](int st, int c, int i) -> bf16x8 {
+    const int si = (i * S::NQF) / S::NR;
+    if (is_k(i)) return *reinterpret_cast<const bf16x8*>(kts + st * S::KTILE + 32 * c * S::KS + krb + 32 * si);
+    return *reinterpret_cast<const bf16x8*>(vts + st * S::VTILE + 32 * c * S::VS + vrb + 32 * (i - si));
+  };
+  // First-phase row operands in flight across steps: a chunk-1 step loads the
+  // first kDqPrefetchA operands of the following step (its stage is already
+  // visible), which then starts without waiting for them.
+  bf16x8 afr[kDqPrefetchA];
   auto step = [&](auto dofill, f32x16 (&sc)[2], f32x16 (&dp)[2], f32x16 (&nsc)[2], f32x16 (&ndp)[2], int st, int c,
-                  int nst, int nc) {
-    const char* nkb = kts + nst * S::KTILE + 32 * nc * S::KS + krb;
-    const char* nvb = vts + nst * S::VTILE + 32 * nc * S::VS + vrb;
+                  int nst, int nc, auto pre_a) {
     const char* kb = kts + st * S::KTILE + 32 * c * S::KS + ktb;
+    // Phase B's transposed K operands; the first PB are read in phase A's last sub-slices.
+    auto bread = [&](int j, i16x4& lo, i16x4& hi) {
+      const int ks = j / S::NDB, blk = j % S::NDB;
+      lo = lds_read_tr(kb + 16 * ks * S::KS, 64 * blk);
+      hi = lds_read_tr(kb + (16 * ks + 2) * S::KS, 64 * blk);
+    };
+    constexpr int PB = kDqPrefetchB;  // transposed operands in flight
+    i16x4 tlo[PB], thi[PB];
 
     // ---- phase A ----
     constexpr int PF = kDqPrefetchA;  // row operands in flight
-    auto is_k = [](int i) { return ((i + 1) * S::NQF) / S::NR > (i * S::NQF) / S::NR; };
-    auto aread = [&](int i) -> bf16x8 {  // operand i: K (fragment si) or V, interleaved
-      const int si = (i * S::NQF) / S::NR;
-      if (is_k(i)) return *reinterpret_cast<const bf16x8*>(nkb + 32 * si);
-      return *reinterpret_cast<const bf16x8*>(nvb + 32 * (i - si));
-    };
-    bf16x8 afr[PF];
+    auto aread = [&](int i) -> bf16x8 { return arow(nst, nc, i); };  // operand i: K or V, interleaved
+    if constexpr (!decltype(pre_a)::value) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) afr[i] = aread(i);
+      for (int i = 0; i < PF; ++i) afr[i] = aread(i);
+    }
     u32x4 sk[2][2];
     // Weights of row pair pr (half pr / 8, registers 2 (pr % 8) and +1) in
     // three stages, so that each exponential's latency is covered by later
@@ -394,6 +407,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
         else mfma_vacc(ndp[u], afr[i % PF], of[u][vi]);
       }
       if (u == 1 && i + PF < S::NR) afr[i % PF] = aread(i + PF);
+      if (u == 1 && i >= S::NR - PB) bread(i - (S::NR - PB), tlo[i - (S::NR - PB)], thi[i - (S::NR - PB)]);
       if constexpr (decltype(dofill)::value) {
         if (m % 4 == 1 && m / 4 < FK + FV) fill_item(m / 4);
       }
@@ -406,15 +420,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 
     // ---- phase B ----
     // Operand j: key step j / NDB, column block j % NDB; two MFMAs (halves).
-    auto bread = [&](int j, i16x4& lo, i16x4& hi) {
-      const int ks = j / S::NDB, blk = j % S::NDB;
-      lo = lds_read_tr(kb + 16 * ks * S::KS, 64 * blk);
-      hi = lds_read_tr(kb + (16 * ks + 2) * S::KS, 64 * blk);
-    };
-    constexpr int PB = kDqPrefetchB;  // transposed operands in flight
-    i16x4 tlo[PB], thi[PB];
-#pragma unroll
-    for (int j = 0; j < PB; ++j) bread(j, tlo[j], thi[j]);
     asm volatile("s_nop 1");  // the last packed dS operands were just written
     // Slice j: two MFMAs (halves) and the reads PB operands ahead.
 #pragma unroll
@@ -425,6 +430,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) mfma_aacc(dq[u][blk], a, __builtin_bit_cast(bf16x8, sk[u][ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
+      if constexpr (decltype(dofill)::value) {  // chunk 1: the next step's first row operands
+        if (j >= S::NB - PF) afr[j - (S::NB - PF)] = arow(nst, 1, j - (S::NB - PF));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -445,24 +453,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     __syncthreads();
     f32x16 sa[2], pa[2], sb[2], pb[2];
     score_products(sa, pa, 0, 0);
-    int j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
+#pragma unroll
+    for (int i = 0; i < kDqPrefetchA; ++i) afr[i] = arow(0, 1, i);  // the first step's first operands
+    unsigned j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
     while (true) {
-      const int st = j % S::NSTAGE, nst = (j + 1) % S::NSTAGE;
+      const int st = (int)(j & (S::NSTAGE - 1)), nst = (int)((j + 1) & (S::NSTAGE - 1));
       const int k0 = t0 * S::BK;
       const bool partial = tile_class(t0) == kTilePartial;
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, k0);
-      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1);
+      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, std::true_type{});
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3 (empty past the last tile),
       // spread over chunk 1's first phase.
       wait_vm_n<kF>();
       __syncthreads();
-      fill_begin(t3, (j + 3) % S::NSTAGE);
+      fill_begin(t3, (int)((j + 3) & (S::NSTAGE - 1)));
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, k0);
-      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0);
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, std::false_type{});
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;
