@@ -249,17 +249,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   static_assert(4 * (FK + FV) <= 2 * S::NR, "one spread copy per four first-phase MFMAs at most");
   i32x4 frk, frv;
   int fst = 0;
-  auto fill_begin = [&](int kt, int st) {  // descriptors and the uneven rest
-    const int k0 = kt < 0 ? 0 : kt * S::BK;
-    const int64_t rows = kt < 0 ? 0 : nk - k0;
-    frk = rsrc_words(Kb + (int64_t)k0 * krow, rows * krow);
-    frv = rsrc_words(Vb + (int64_t)k0 * vrow, rows * vrow);
+  // Buffer resource of the rows of key tile kt of a [nk, row] slice with rb
+  // bytes per row; the host bounds (nk - 1) rb + the row width by 2^31 - 1,
+  // so the products fit in 32 bits.  kt < 0: an empty range.
+  auto tile_words = [&](const void* base, int kt, int rb) -> i32x4 {
+    const uint32_t k0 = kt < 0 ? 0u : (uint32_t)(kt * S::BK);
+    const uint32_t nb = kt < 0 ? 0u : (uint32_t)(nk - (int)k0) * (uint32_t)rb;
+    const uint64_t a = reinterpret_cast<uint64_t>(base) + k0 * (uint32_t)rb;
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)(nb < 0x7FFFFFFFu ? nb : 0x7FFFFFFFu), 0x00020000};
+  };
+  // The next in-step fill, planned in chunk 0's second phase (its scalar work
+  // issues under the MFMAs): K / V resources, key tile and target stage.
+  int fkt = -1;
+  auto plan_fill = [&](int kt, int st) {
+    frk = tile_words(Kb, kt, krow);
+    frv = tile_words(Vb, kt, vrow);
     fst = st;
+    fkt = kt;
+  };
+  auto fill_begin = [&]() {  // the uneven rest of the planned fill
 #pragma unroll
-    for (int i = FK; i < S::KWIN; ++i) kwin(frk, st, i);
+    for (int i = FK; i < S::KWIN; ++i) kwin(frk, fst, i);
 #pragma unroll
-    for (int i = FV; i < S::VWIN; ++i) vwin(frv, st, i);
-    if constexpr (MASK == kMaskBitmask) fill_mask(mask_rsrc(kt < 0 ? 0 : n - q0), st, k0);
+    for (int i = FV; i < S::VWIN; ++i) vwin(frv, fst, i);
+    if constexpr (MASK == kMaskBitmask)
+      fill_mask(mask_rsrc(fkt < 0 ? 0 : n - q0), fst, fkt < 0 ? 0 : fkt * S::BK);
   };
   auto fill_item = [&](int i) {  // i < FK + FV
     if (i < FK) kwin(frk, fst, i);
@@ -347,7 +361,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // visible), which then starts without waiting for them.
   bf16x8 afr[kDqPrefetchA];
   auto step = [&](auto dofill, f32x16 (&sc)[2], f32x16 (&dp)[2], f32x16 (&nsc)[2], f32x16 (&ndp)[2], int st, int c,
-                  int nst, int nc, auto pre_a) {
+                  int nst, int nc, auto hook, auto pre_a) {
     const char* kb = kts + st * S::KTILE + 32 * c * S::KS + ktb;
     // Phase B's transposed K operands; the first PB are read in phase A's last sub-slices.
     auto bread = [&](int j, i16x4& lo, i16x4& hi) {
@@ -430,6 +444,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) mfma_aacc(dq[u][blk], a, __builtin_bit_cast(bf16x8, sk[u][ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
+      if (j == 2) hook();
       if constexpr (decltype(dofill)::value) {  // chunk 1: the next step's first row operands
         if (j >= S::NB - PF) afr[j - (S::NB - PF)] = arow(nst, 1, j - (S::NB - PF));
       }
@@ -462,17 +477,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       const bool partial = tile_class(t0) == kTilePartial;
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, k0);
-      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, std::true_type{});
+      step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1,
+           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); }, std::true_type{});
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3 (empty past the last tile),
       // spread over chunk 1's first phase.
       wait_vm_n<kF>();
       __syncthreads();
-      fill_begin(t3, (int)((j + 3) & (S::NSTAGE - 1)));
+      fill_begin();
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, k0);
-      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, std::false_type{});
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, [] {}, std::false_type{});
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;
