@@ -402,6 +402,7 @@ struct FwdPipeShape {
   static constexpr int KWINS = KTILE / 1024, VWINS = VTILE / 1024;  // 1 KB fill windows per tile
   static constexpr int KWIN = (KWINS + NW - 1) / NW, VWIN = (VWINS + NW - 1) / NW;  // per wave (max)
   static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "whole fill windows");
+  static_assert(KWIN + VWIN <= (D / 16) * (BK / 32), "one copy per first-phase MFMA at most");
 };
 
 template <int D, int DV, int MASK>
@@ -413,6 +414,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char kbuf1[S::KTILE];
   __shared__ __attribute__((aligned(1024))) char vbuf0[S::VTILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[S::VTILE];
+  __shared__ __attribute__((aligned(1024))) char spare[1024];  // target of the copies a wave has no window for
 
   const int64_t logical0 = xcd_logical(blockIdx.x, p.grid_pad, p.total);
   if (logical0 < 0) return;
@@ -482,6 +484,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < S::KWIN; ++i) koff[i] = S::KT::fill_src((w + S::NW * i) * 1024 + 16 * lane, krow);
 #pragma unroll
   for (int i = 0; i < S::VWIN; ++i) voff[i] = S::VT::fill_src((w + S::NW * i) * 1024 + 16 * lane, vrow);
+  const __amdgpu_buffer_rsrc_t rnone = make_rsrc(Kb, 0);
   auto fill_k = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
@@ -607,8 +610,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto step = [&](f32x16 (&cur)[S::NKB], f32x16 (&nxt)[S::NKB], char* kcur, char* knxt, char* vcur,
                     char* vnxt) {
       const int t2 = t1 < kt_end ? next_tile(t1) : kt_end;
-      if (t2 < kt_end) fill_k(t2, kcur);
-      if (t1 < kt_end) fill_v(t1, vnxt);
+      // This step's copies (K of t2 into kcur, V of t1 into vnxt) issue one per
+      // first-phase MFMA; past the last tile they copy empty ranges.
+      const int k2 = t2 < kt_end ? t2 * S::BK : nk, k1 = t1 < kt_end ? t1 * S::BK : nk;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k2 * krow, (nk - k2) * krow);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k1 * vrow, (nk - k1) * vrow);
+      auto copy_item = [&](int i) {
+        if (i < S::KWIN) {
+          const bool real = S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS;
+          dma16(real ? rk : rnone, real ? kcur + (w + S::NW * i) * 1024 : spare, koff[i]);
+        } else if (i < S::KWIN + S::VWIN) {
+          const int jv = i - S::KWIN;
+          const bool real = S::VWINS % S::NW == 0 || w + S::NW * jv < S::VWINS;
+          dma16(real ? rv : rnone, real ? vnxt + (w + S::NW * jv) * 1024 : spare, voff[jv]);
+        }
+      };
 
       // The instruction order below is the schedule: each micro-step is one
       // MFMA, the LDS reads for a later MFMA, and a slice of VALU work, kept
@@ -653,6 +669,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_sched_barrier(0);
         nxt[i % S::NKB] = mfma_bf16(kfr[i % PF], qf[i / S::NKB], nxt[i % S::NKB]);
         if (i + PF < NS) kfr[i % PF] = kread(i + PF);
+        copy_item(i);
         if (i == NS - 1) {  // first PV operands
           vfr[0] = vread(0, 0);
           vfr[1] = vread(0, 1);
