@@ -165,7 +165,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   // Query tiles are visited from the last down to the first one that can
   // hold an allowed pair (causal: the tile containing row k0 - coff).
   int qt_first = 0;
-  if constexpr (MASK == kMaskCausal) qt_first = k0 - coff > 0 ? (k0 - coff) / S::BQ : 0;
+  if constexpr (MASK == kMaskCausal) {
+    // Row k0 - coff is the first that allows key k0.  Past the last row no
+    // query tile holds an allowed pair: the tile containing that padding row
+    // is empty, not partial, and must not be visited.
+    const int r0 = k0 - coff;
+    qt_first = r0 >= n ? p.tq : (r0 > 0 ? r0 / S::BQ : 0);
+  }
   const uint8_t* map_col = nullptr;
   const uint32_t* mbase = nullptr;
   if constexpr (MASK == kMaskBitmask) {

@@ -122,7 +122,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // an allowed pair (causal: the tile containing row k0 - coff); bitmask tiles come
   // from the tile map, staged in LDS so that the loop issues no loads of its own.
   int qt_first = 0;
-  if constexpr (MASK == kMaskCausal) qt_first = k0 - coff > 0 ? (k0 - coff) / S::BQ : 0;
+  if constexpr (MASK == kMaskCausal) {
+    // Row k0 - coff is the first that allows key k0.  Past the last row no
+    // query tile holds an allowed pair: the tile containing that padding row
+    // is empty, not partial, and must not be visited.
+    const int r0 = k0 - coff;
+    qt_first = r0 >= n ? p.tq : (r0 > 0 ? r0 / S::BQ : 0);
+  }
   if constexpr (MASK == kMaskBitmask) {
     const int64_t mu = p.mask_sb == 0 ? h : unit;
     const uint8_t* map_col = p.map + mu * (int64_t)p.tq * p.tk + kt;

@@ -33,7 +33,10 @@ DIMS = [("f32", 64, 64), ("f32", 80, 80), ("bf16", 128, 128), ("bf16", 64, 128),
 # (n, nk, mask, offset)
 SHAPES = [(300, 777, "causal", 477), (300, 777, "causal", 0), (300, 777, "none", 0),
           (777, 300, "causal", -477), (777, 300, "causal", 50), (777, 300, "bitmask", 0),
-          (1, 513, "causal", 512), (129, 1, "none", 0), (200, 333, "causal", -150)]
+          (1, 513, "causal", 512), (129, 1, "none", 0), (200, 333, "causal", -150),
+          # Key tiles whose first allowing row k0 - offset lies past the last row
+          # but inside the last query tile: no row reaches them (dK = dV = 0).
+          (400, 400, "causal", -144), (1, 255, "causal", 111), (777, 777, "causal", -190)]
 
 
 def _dev(x: np.ndarray, dtype: str) -> torch.Tensor:
