@@ -1,4 +1,4 @@
-"""Seeded sweep over combinations of the options, against the float64 oracle.
+"""Seeded sweeps over combinations of the options, against the float64 oracle.
 
 Each case draws (dtype and dims, n, nk, mask, causal offset, dropout,
 scale) from a fixed seed, so the list is the same on every run.  The case
@@ -7,6 +7,20 @@ the oracle: the definition (oracle/dense.py), or with dropout the dropout
 oracle (oracle/dropout.py) under its own mask.  Rows that allow no key must
 give O = 0, L = -inf and dQ = 0.  The point is the interplay of options that
 the focused tests cover one at a time.
+
+``test_sweep`` holds every output to the stated tolerances relative to its
+largest magnitude.  ``test_sweep_wide`` draws from wider distributions (n
+off the tile grid, offsets near +-n, a handful of rows against thousands of
+keys, dropout up to 0.9), where many gradients are small differences of
+large terms: a row dominated by one key has dP_ij close to D_i, and a
+single row's dQ is a sum of such differences.  No fp32 evaluation reaches
+1e-5 of such a result (a plain fp32 evaluation of the same formulas misses
+it too), so the wide sweep measures each output's error against the size
+of the terms it sums: T(dV_j) = sum_i P~_ij |dO_i|, T(dQ_i) = |c| sum_j
+P_ij (|Z_ij dP_ij / (1-p)| + |D_i|) |K_j| (dK alike with |Q_i|), T(O_i) =
+sum_j P~_ij |V_j|, P~ the dropped and rescaled weights.  Wrong masking, a
+missed or doubled tile, or a wrong row statistic moves an output by a
+multiple of its terms and fails this bound as surely as the strict one.
 """
 
 from __future__ import annotations
@@ -17,7 +31,7 @@ import torch
 
 import workloads as W
 from oracle import dense, dropout, tiled
-from tests.gpu_common import DEV, compare, stored
+from tests.gpu_common import BF16_ABS, BF16_REL, DEV, F32_REL, compare, stored
 
 pytestmark = pytest.mark.gpu
 
@@ -41,14 +55,30 @@ def _cases(count=40, seed=20261202):
     return out
 
 
+def _wide_cases(count=160, seed=777):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(count):
+        i = 5000 + k
+        dtype, d, v = DIMS[rng.integers(len(DIMS))]
+        n = int(rng.choice([1, 2, 7, 32, 33, 63, 96, 128, 129, 191, 255, 256, 257, 400, 511, 777, 1024, 1100]))
+        nk = n if rng.random() < 0.4 else int(rng.choice([1, 2, 31, 32, 63, 127, 128, 255, 256, 257, 1023, 1024, 2049]))
+        mask = ["none", "causal", "bitmask"][rng.integers(3)]
+        off = int(rng.integers(-n - 2, nk + 3)) if mask == "causal" else 0
+        p = float(rng.choice([0.0, 0.0, 0.1, 0.5, 0.9]))
+        scale = float(rng.choice([1 / np.sqrt(d), 0.3, -0.2, 0.0, -0.5]))
+        out.append(pytest.param(i, dtype, d, v, n, nk, mask, off, p, scale,
+                                id=f"{i}-{dtype}-{d}x{v}-n{n}-nk{nk}-{mask}{off}-p{p}-c{scale:.3g}"))
+    return out
+
+
 def _dev(x, dtype):
     if dtype == "bf16":
         return torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(DEV)
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(DEV)
 
 
-@pytest.mark.parametrize("i,dtype,d,v,n,nk,mask,off,p,scale", _cases())
-def test_sweep(i, dtype, d, v, n, nk, mask, off, p, scale):
+def _run(i, dtype, d, v, n, nk, mask, off, p, scale, wide):
     import exact_tiled_attention_attn_amd as E
 
     H, seed = 2, 1000 + i
@@ -96,6 +126,10 @@ def test_sweep(i, dtype, d, v, n, nk, mask, off, p, scale):
         else:
             Y, m, ell, Lr = dense.forward(Qr, Kh, Vh, scale, Ar)
             rdQ, rdK, rdV = tiled.reverse(Qr, Kh, Vh, scale, Ar, nk, stored(Y, dtype), m, ell, Gr)
+        if wide:
+            _check_terms(Oh[rows], Lh[rows], res, h, rows, (Qr, Kh, Vh, Gr, Ar), Y, Lr, (rdQ, rdK, rdV),
+                         Z if p8 else None, p8, scale, dtype, tag, got)
+            continue
         # Magnitude bounds for outputs whose exact value is zero (keys no row allows).
         mq, mk, mv, mg = (float(np.abs(x).max(initial=0.0)) for x in (Qr, Kh, Vh, Gr))
         kinv = 256 / (256 - p8)
@@ -111,3 +145,41 @@ def test_sweep(i, dtype, d, v, n, nk, mask, off, p, scale):
                 if few and dtype == "bf16" and name in ("dQ", "dK"):
                     continue  # not asserted for 1-2 key problems in bf16 (the stored O's rounding dominates)
                 compare(name, x, r, dtype, (tag, path), bound=bd[name], elementwise=not few, cond=cond)
+
+
+def _check_terms(Oh, Lh, res, h, rows, ins, Y, Lr, grads, Z, p8, scale, dtype, tag, got):
+    """Errors against the size of the summed terms (see the module docstring)."""
+    Qr, Kh, Vh, Gr, Ar = ins
+    P = np.where(Ar, np.exp(scale * (Qr @ Kh.T) - Lr[:, None]), 0.0)
+    Zs = np.ones_like(P) if Z is None else Z * (256 / (256 - p8))  # dropped and rescaled: Z / (1 - p)
+    Pt = P * Zs
+    D = np.sum(Gr * Y, axis=1)
+    Wm = P * (np.abs(Zs * (Gr @ Vh.T)) + np.abs(D)[:, None])
+    T = {"O": Pt @ np.abs(Vh), "dQ": abs(scale) * Wm @ np.abs(Kh), "dK": abs(scale) * Wm.T @ np.abs(Qr),
+         "dV": Pt.T @ np.abs(Gr)}
+    compare("L", Lh, Lr, dtype, tag)
+    tol = F32_REL if dtype == "f32" else BF16_REL
+    outs = [("O", "", Oh, Y)]
+    for path, (dq, dk, dv) in res.items():
+        outs += [("dQ", path, got(dq[0, h])[rows], grads[0]), ("dK", path, got(dk[0, h]), grads[1]),
+                 ("dV", path, got(dv[0, h]), grads[2])]
+    for name, path, x, r in outs:
+        t = T[name]
+        scale_t = max(float(t.max(initial=0.0)), 1e-30)
+        err = np.abs(x - r)
+        assert np.all(np.isfinite(x)), (tag, path, name, "non-finite output")
+        e = float(err.max(initial=0.0)) / scale_t
+        assert e <= tol, (tag, path, name, e)
+        if dtype == "bf16":
+            bad = err > BF16_ABS * scale_t + BF16_REL * t
+            assert not bad.any(), (tag, path, name, int(bad.sum()))
+
+
+@pytest.mark.parametrize("i,dtype,d,v,n,nk,mask,off,p,scale", _cases())
+def test_sweep(i, dtype, d, v, n, nk, mask, off, p, scale):
+    _run(i, dtype, d, v, n, nk, mask, off, p, scale, wide=False)
+
+
+@pytest.mark.parametrize("i,dtype,d,v,n,nk,mask,off,p,scale", _wide_cases())
+def test_sweep_wide(i, dtype, d, v, n, nk, mask, off, p, scale):
+    _run(i, dtype, d, v, n, nk, mask, off, p, scale, wide=True)
