@@ -136,6 +136,12 @@ attn_status check_view(const char* name, const int64_t s[3], int64_t B, int64_t 
   // row strides included.
   if ((n - 1) * s[2] * es + w * es > int64_t(0x7FFFFFFF) || s[2] * es > int64_t(0x7FFFFFFF))
     return fail(ATTN_ERR_UNSUPPORTED, "%s: one head spans more than 2 GiB (n * row stride)", name);
+  // Tiles also address the padding rows past the last one, up to n rounded
+  // up to 256 (the tallest tile), with 32-bit offsets: those must land past
+  // the buffer range, not wrap around 2^32 back into it.
+  if ((n + 255) / 256 * 256 * s[2] * es + w * es > int64_t(0xFFFFFFFF))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: row stride too large for the row count (rows padded to 256 span "
+                "more than 4 GiB)", name);
   struct Dim {
     int64_t size, stride;
   } dims[4] = {{B, s[0]}, {H, s[1]}, {n, s[2]}, {w, 1}};
@@ -211,6 +217,17 @@ attn_status validate_problem(const attn_problem* p) {
   return ATTN_OK;
 }
 
+// The backward's extra limit: on the atomic path the fused kernel addresses
+// one head's fp32 dQ accumulator with 32-bit offsets.
+attn_status validate_bwd(const attn_problem* p) {
+  attn_status st = validate_problem(p);
+  if (st != ATTN_OK) return st;
+  if (!p->deterministic && p->n * p->d * 4 > int64_t(0x7FFFFFFF))
+    return fail(ATTN_ERR_UNSUPPORTED, "atomic dQ path: one head's fp32 dQ accumulator (n * d * 4 bytes) exceeds "
+                "2 GiB; use the deterministic path");
+  return ATTN_OK;
+}
+
 attn_status check_ptr(const char* name, const void* ptr) {
   if (!ptr) return fail(ATTN_ERR_NULL, "%s is NULL", name);
   if (reinterpret_cast<uintptr_t>(ptr) % 16) return fail(ATTN_ERR_STRIDE, "%s is not 16-byte aligned", name);
@@ -277,7 +294,7 @@ attn_status timed(int kind, void* stream, const char* what, F&& fn) {
 extern "C" {
 
 attn_status attn_workspace_size(const attn_problem* p, int is_bwd, size_t* bytes) {
-  attn_status st = validate_problem(p);
+  attn_status st = is_bwd ? validate_bwd(p) : validate_problem(p);
   if (st != ATTN_OK) return st;
   if (!bytes) return fail(ATTN_ERR_NULL, "bytes pointer is NULL");
   *bytes = plan(*p, is_bwd).total;
@@ -358,7 +375,7 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
 attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const void* V, const void* O,
                      const void* dO, const float* L, void* dQ, void* dK, void* dV, void* ws,
                      size_t ws_bytes, void* stream) {
-  attn_status st = validate_problem(p);
+  attn_status st = validate_bwd(p);
   if (st != ATTN_OK) return st;
   if ((st = check_ptr("Q", Q)) || (st = check_ptr("K", K)) || (st = check_ptr("V", V)) ||
       (st = check_ptr("O", O)) || (st = check_ptr("dO", dO)) || (st = check_ptr("L", L)) ||

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   if constexpr (FUSED) {
     // Resident K tile in LDS (B operand of dQ), padded columns cleared.
     constexpr int KCH = S::DP * S::ES / 16;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (int64_t)(nk - k0) * krow);
     for (int c = tid; c < S::BK * KCH; c += 256) {
       const int r = c / KCH, cc = c % KCH;
       u32x4 x = u32x4{0, 0, 0, 0};
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   constexpr int NKF = D / S::KSTEP, NVF = DV / S::KSTEP;
   Frag kf[NKF], vf[NVF];
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, nk * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, nk * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, (int64_t)nk * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, (int64_t)nk * vrow);
 #pragma unroll
     for (int s = 0; s < NKF; ++s) {
       if constexpr (BF16)
@@ -195,8 +195,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   uint32_t mreg = 0;
   auto gload = [&](int qt, int bi) {
     const int q0 = qt * S::BQ;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb + (int64_t)q0 * qrow, (n - q0) * qrow);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb + (int64_t)q0 * orow, (n - q0) * orow);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb + (int64_t)q0 * qrow, (int64_t)(n - q0) * qrow);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb + (int64_t)q0 * orow, (int64_t)(n - q0) * orow);
     if constexpr (S::DMA) {
       char* Qs = bufs + bi * S::BUF;
       char* Os = Qs + S::QTILE;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   };
 
   __amdgpu_buffer_rsrc_t rdq;  // fused: dQ accumulator rows of this unit
-  if constexpr (FUSED) rdq = make_rsrc(p.dQacc + (int64_t)unit * n * D, n * D * 4);
+  if constexpr (FUSED) rdq = make_rsrc(p.dQacc + (int64_t)unit * n * D, (int64_t)n * D * 4);
 
   int qt = p.tq - 1;
   if (MASK == kMaskBitmask && qt >= qt_first && tile_class(qt) == kTileEmpty) qt = next_tile(qt);

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
   typedef typename std::conditional<BF16, bf16x8, float>::type Frag;
   Frag qf[S::NQF], of[S::NOF];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, n * qrow);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb, n * orow);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, (int64_t)n * qrow);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb, (int64_t)n * orow);
 #pragma unroll
     for (int s = 0; s < S::NQF; ++s) {
       if constexpr (BF16)
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
   u32x4 kreg[S::KLD], vreg[S::VLD];
   auto gload = [&](int kt) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (nk - k0) * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (int64_t)(nk - k0) * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (int64_t)(nk - k0) * vrow);
 #pragma unroll
     for (int i = 0; i < S::KLD; ++i) {
       const int c = tid + i * 256;

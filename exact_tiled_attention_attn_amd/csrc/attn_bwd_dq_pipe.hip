@@ -158,8 +158,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // Q and dO rows of the wave's queries (B operands; lane column = query).
   bf16x8 qf[2][S::NQF], of[2][S::NVF];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, n * qrow);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb, n * orow);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, (int64_t)n * qrow);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOb, (int64_t)n * orow);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll

@@ -149,8 +149,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // K and V rows of this wave's keys (B operands; lane column = key).
   bf16x8 kf[S::NQF], vf[S::NVF];
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, nk * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, nk * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, (int64_t)nk * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, (int64_t)nk * vrow);
 #pragma unroll
     for (int s = 0; s < S::NQF; ++s)
       kf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * krow + (16 * s + 8 * hh) * 2, 0, 0));

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   typedef typename std::conditional<BF16, bf16x8, float>::type QFrag;
   QFrag qf[S::NQF];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, n * qrow);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, (int64_t)n * qrow);
     const int qoff = q * qrow;
 #pragma unroll
     for (int ks = 0; ks < S::NQF; ++ks) {
@@ -150,8 +150,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   u32x4 kreg[S::KLD], vreg[S::VLD];
   auto gload = [&](int kt) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (nk - k0) * vrow);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k0 * krow, (int64_t)(nk - k0) * krow);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k0 * vrow, (int64_t)(nk - k0) * vrow);
 #pragma unroll
     for (int i = 0; i < S::KLD; ++i) {
       const int c = tid + i * 256;
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float scale2 = fmaxf(fabsf(p.scale2), 1e-30f);
   bf16x8 qf[S::NQF];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, n * qrow);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, (int64_t)n * qrow);
     const int qoff = q * qrow;
 #pragma unroll
     for (int ks = 0; ks < S::NQF; ++ks) {
@@ -487,14 +487,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const __amdgpu_buffer_rsrc_t rnone = make_rsrc(Kb, 0);
   auto fill_k = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (nk - k0) * krow);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (int64_t)(nk - k0) * krow);
 #pragma unroll
     for (int i = 0; i < S::KWIN; ++i)
       if (S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS) dma16(r, buf + (w + S::NW * i) * 1024, koff[i]);
   };
   auto fill_v = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + (int64_t)k0 * vrow, (nk - k0) * vrow);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + (int64_t)k0 * vrow, (int64_t)(nk - k0) * vrow);
 #pragma unroll
     for (int i = 0; i < S::VWIN; ++i)
       if (S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS) dma16(r, buf + (w + S::NW * i) * 1024, voff[i]);
@@ -613,8 +613,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // This step's copies (K of t2 into kcur, V of t1 into vnxt) issue one per
       // first-phase MFMA; past the last tile they copy empty ranges.
       const int k2 = t2 < kt_end ? t2 * S::BK : nk, k1 = t1 < kt_end ? t1 * S::BK : nk;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k2 * krow, (nk - k2) * krow);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k1 * vrow, (nk - k1) * vrow);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k2 * krow, (int64_t)(nk - k2) * krow);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k1 * vrow, (int64_t)(nk - k1) * vrow);
       auto copy_item = [&](int i) {
         if (i < S::KWIN) {
           const bool real = S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS;

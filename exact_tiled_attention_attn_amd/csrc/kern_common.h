@@ -118,8 +118,14 @@ __device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zero (gfx9 descriptor word 3 = 0x00020000, 32-bit data format).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes < 0 ? 0 : bytes, 0x00020000);
+// Buffer resource over [base, base + bytes).  The host bounds every valid
+// access of one (batch, head) slice below 2^31 - 1 bytes, but a size taken as
+// whole rows times the row stride can pass 2^31 (the last row's padding);
+// the size is formed in 64 bits by the callers and clamped here, so it never
+// wraps to a small or negative count that would cut off valid rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nb = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, 0x00020000);
 }
 
 // Swizzled LDS tile layout.  A tile row holds CPR 16-byte chunks.  LDS has

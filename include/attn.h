@@ -32,6 +32,13 @@
  *   Pointers must be 16-byte aligned and row/head/batch strides multiples
  *   of 16 bytes.  L (and the backward's internal D) are contiguous fp32
  *   [B, H, n].
+ * - The kernels address one (batch, head) slice with 32-bit byte offsets,
+ *   which sets three limits (ATTN_ERR_UNSUPPORTED beyond them): in every
+ *   tensor, row 0 to the end of row n - 1 spans at most 2^31 - 1 bytes;
+ *   n rounded up to 256 rows times the row stride stays below 2^32 bytes
+ *   (tiles address the padding rows past the last one); and with
+ *   deterministic = 0, one head's fp32 dQ accumulator, n d 4 bytes, is at
+ *   most 2^31 - 1 bytes.  Batch and head offsets are 64-bit.
  * - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *   asynchronously on it; nothing synchronises.
  * - Every argument is validated before anything is launched; on an error
@@ -60,7 +67,7 @@ typedef enum {
   ATTN_ERR_STRIDE = 3,      /* misaligned pointer or stride, or overlapping rows */
   ATTN_ERR_DTYPE = 4,       /* unknown element type */
   ATTN_ERR_MASK = 5,        /* unknown mask mode, or bitmask mode without mask */
-  ATTN_ERR_UNSUPPORTED = 6, /* (d, v) pair or option not compiled in */
+  ATTN_ERR_UNSUPPORTED = 6, /* (d, v) pair or option not compiled in, or past a size limit */
   ATTN_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than attn_workspace_size */
   ATTN_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
   ATTN_ERR_HIP = 9          /* a HIP launch error (message in attn_last_error) */

@@ -116,6 +116,8 @@ def test_workspace_formula():
     (lambda p: p.sk.__setitem__(1, -6400), 3),
     (lambda p: p.so.__setitem__(1, 64 * 99), 3),  # heads overlap
     (lambda p: (setattr(p, "n", 1), p.sq.__setitem__(2, 1 << 31)), 6),  # row stride past 32-bit offsets
+    (lambda p: (setattr(p, "n", 1), p.sq.__setitem__(2, 1 << 24)), 6),  # 256 padded rows span > 4 GiB
+    (lambda p: (setattr(p, "nk", 3), p.sv.__setitem__(2, 3 << 22)), 6),  # the same for V at nk rows
     (lambda p: setattr(p, "nk", -1), 2),
     (lambda p: setattr(p, "causal_offset", 3), 5),  # offset without the causal mask
     (lambda p: (setattr(p, "mask_mode", 1), setattr(p, "causal_offset", (1 << 30) + 1)), 2),
@@ -245,3 +247,29 @@ def test_missing_library_fails_loudly(tmp_path):
             _binding.load_library(str(tmp_path / "libattn.so"))
         finally:
             _binding._lib = saved
+
+
+def test_size_limits_of_32_bit_slice_addressing():
+    # The largest accepted head: rows 0..n-1 end just below 2^31 bytes.  With a
+    # padded row stride, n times the stride passes 2^31 (the kernels' buffer
+    # sizes are formed in 64 bits and clamped, so this stays valid).
+    es, w = 2, 128
+    stride = (1 << 20) + 8  # elements, 16-byte multiple
+    p = problem(B=1, H=1, n=1024, d=w, v=w)
+    for name in ("sq", "sk", "sv", "so"):
+        arr = getattr(p, name)
+        arr[0] = arr[1] = 1024 * stride
+        arr[2] = stride
+    assert 1024 * stride * es > (1 << 31) and 1023 * stride * es + w * es < (1 << 31)
+    assert wsize(p, 0)[0] == 0 and wsize(p, 1)[0] == 0, err()
+    p.n = 1025  # row 1024 would end past 2^31 - 1
+    assert wsize(p, 0)[0] == 6 and "2 GiB" in err()
+    # Atomic dQ path: one head's fp32 accumulator must stay within 2^31 - 1 bytes.
+    p = problem(B=1, H=1, n=1 << 22, d=128, v=128)
+    assert wsize(p, 0)[0] == 0
+    assert wsize(p, 1)[0] == 6 and "accumulator" in err()
+    assert call_bwd(p) == 6
+    p.deterministic = 1
+    st, need = wsize(p, 1)
+    assert st == 0 and need > 0
+    assert call_bwd(p) == 7  # validation passes; stops at the missing workspace, before any launch
