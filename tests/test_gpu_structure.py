@@ -6,7 +6,8 @@
 * keys that no row allows get exactly zero dK, dV;
 * causal row 0 reproduces V_0 bitwise; empty rows are defined;
 * strided layouts give bitwise the same results as contiguous ones;
-* negative and zero scale, and Q = K = V aliasing, against the oracle.
+* negative and zero scale, and Q = K = V aliasing, against the oracle;
+* bitmask pad bits past nk and padding words of padded mask rows are ignored.
 """
 
 from __future__ import annotations
@@ -217,3 +218,39 @@ def test_self_attention_aliased_inputs():
     compare("L", L[0, 0].cpu().double().numpy(), Lr, "f32")
     dx = (dq + dk + dv)[0, 0].cpu().double().numpy()
     compare("dQ", dx, rdq + rdk + rdv, "f32")
+
+
+@pytest.mark.parametrize("dtype,d,v", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 128), (torch.float32, 80, 80)])
+def test_mask_pad_bits_and_padded_rows_are_ignored(dtype, d, v):
+    """Bits past nk in a row's last word, and words past ceil(nk / 32) in a
+    padded row (mask row stride above the word count), are never read as
+    allowed keys: set to ones, they leave every output bitwise unchanged."""
+    import exact_tiled_attention_attn_amd as E
+
+    H, n, nk = 2, 300, 333  # 11 words per row, the last one with 13 key bits and 19 pad bits
+    rng = np.random.default_rng(d + v)
+    A = rng.random((H, n, nk)) < 0.3
+    A[:, np.arange(n), rng.integers(0, nk, n)] = True
+    words = W.pack_bits(A)  # [H, n, 11] uint32, pad bits 0
+    assert words.shape[-1] == 11
+    padded = np.full((H, n, 16), 0xFFFFFFFF, np.uint32)  # row stride 16 words, padding all ones
+    padded[..., :11] = words
+    padded[..., 10] |= np.uint32(~((1 << (nk % 32)) - 1) & 0xFFFFFFFF)  # pad bits past nk set
+    clean = torch.from_numpy(words.view(np.int32)).to(DEV)
+    dirty = torch.from_numpy(padded.view(np.int32)).to(DEV)
+    g0 = torch.Generator().manual_seed(d)
+    q = torch.randn((1, H, n, d), generator=g0).to(dtype).to(DEV)
+    k = torch.randn((1, H, nk, d), generator=g0).to(dtype).to(DEV)
+    val = torch.randn((1, H, nk, v), generator=g0).to(dtype).to(DEV)
+    g = torch.randn((1, H, n, v), generator=g0).to(dtype).to(DEV)
+    c = d ** -0.5
+    res = []
+    for m in (clean, dirty):
+        o, L = E.fwd(q, k, val, c, "bitmask", m)
+        det = E.bwd(q, k, val, o, g, L, c, "bitmask", m, deterministic=True)
+        maps = [E.debug_tile_map(q, k, val, c, "bitmask", m, is_bwd=i)[0] for i in range(3)]
+        res.append([o, L, *det, *maps])
+    torch.cuda.synchronize()
+    names = ["O", "L", "dQ", "dK", "dV", "map_fwd", "map_bwd", "map_dq"]
+    for name, a, b in zip(names, *res):
+        assert torch.equal(a, b), name
