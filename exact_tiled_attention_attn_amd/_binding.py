@@ -100,6 +100,29 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _on_gpu(name, t, device=None, dtype=None, shape=None):
+    """Checks a tensor argument before its address reaches the library, which
+    sees only pointers: device memory, on the inputs' device, of the expected
+    dtype and shape."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in GPU memory, got a tensor on {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _like(t):
+    """An output with t's shape and strides (also for views with gaps, which
+    torch.empty_like would make contiguous)."""
+    return torch.empty_strided(t.size(), t.stride(), dtype=t.dtype, device=t.device)
+
+
 def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, deterministic=False,
                  causal_offset=0, dropout_p=0.0, dropout_seed=0) -> AttnProblem:
     """Fill the ABI problem struct (strides in elements).
@@ -109,12 +132,17 @@ def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, determinis
     j <= i + causal_offset.  dropout_p / dropout_seed: dropout on the
     weights, replayed by the backward with the same values (include/attn.h).
     """
+    _on_gpu("q", q)
+    _on_gpu("k", k, q.device, q.dtype)
+    _on_gpu("v", v, q.device, q.dtype)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("tensors must be [B, H, rows, dim]")
     B, H, n, d = q.shape
     nk = k.shape[2]
     if tuple(k.shape) != (B, H, nk, d) or tuple(v.shape[:3]) != (B, H, nk):
         raise ValueError(f"shapes do not match: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o_like.device.type != "meta":
+        _on_gpu("O", o_like, q.device, q.dtype, (B, H, n, v.shape[-1]))
     p = AttnProblem()
     p.B, p.H, p.n, p.d, p.v = B, H, n, d, v.shape[-1]
     p.nk = nk
@@ -131,7 +159,7 @@ def make_problem(q, k, v, o_like, scale, mask_mode="none", mask=None, determinis
         for i in range(3):
             arr[i] = t.stride(i)
     if mask is not None:
-        m = mask
+        m = _on_gpu("mask", mask, q.device)
         if m.dtype not in (torch.int32, torch.uint32):
             raise TypeError("mask must be int32/uint32 words")
         words = (nk + 31) // 32
@@ -162,10 +190,19 @@ def workspace_size(p: AttnProblem, is_bwd: bool) -> int:
     return out.value
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor | None:
+def _workspace(nbytes: int, device, given=None) -> torch.Tensor | None:
+    if given is not None:
+        _on_gpu("workspace", given, device)
+        if not given.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        return given
     if nbytes == 0:
         return None
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _ptr(t):
@@ -180,15 +217,20 @@ def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, work
     causal mask (key j allowed for query i iff j <= i + causal_offset).
     """
     lib = load_library()
+    _on_gpu("q", q)
     B, H, n, _ = q.shape
     o = out if out is not None else torch.empty((B, H, n, v.shape[-1]), dtype=q.dtype, device=q.device)
     L = lse if lse is not None else torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    _on_gpu("lse", L, q.device, torch.float32, (B, H, n))
+    if not L.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, n]")
     p = make_problem(q, k, v, o, scale, mask_mode, mask, causal_offset=causal_offset, dropout_p=dropout_p,
                      dropout_seed=dropout_seed)
     need = workspace_size(p, False)
-    ws = workspace if workspace is not None else _workspace(need, q.device)
-    _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
-                        _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel()), _stream()))
+    ws = _workspace(need, q.device, workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L),
+                            _ptr(ws), ctypes.c_size_t(_nbytes(ws)), _stream()))
     return o, L
 
 
@@ -200,23 +242,29 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
     reproducible) instead of fp32 atomics in the key-tile-outer kernel.
     """
     lib = load_library()
+    _on_gpu("q", q)
+    _on_gpu("O", o, q.device, q.dtype)
+    _on_gpu("dO", do, q.device, q.dtype, o.shape)
     if do.stride() != o.stride():
         if not o.is_contiguous():
             raise ValueError("dO must have the strides of O")
         do = do.contiguous()
-    dq = dq if dq is not None else torch.empty_like(q)
-    dk = dk if dk is not None else torch.empty_like(k)
-    dv = dv if dv is not None else torch.empty_like(v)
+    dq = dq if dq is not None else _like(q)
+    dk = dk if dk is not None else _like(k)
+    dv = dv if dv is not None else _like(v)
+    for name, t, ref in (("dQ", dq, q), ("dK", dk, k), ("dV", dv, v)):
+        _on_gpu(name, t, q.device, q.dtype, ref.shape)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("dQ, dK, dV must have the strides of Q, K, V")
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
+    _on_gpu("lse", lse, q.device, torch.float32, q.shape[:3])
+    if not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, H, n]")
     p = make_problem(q, k, v, o, scale, mask_mode, mask, deterministic, causal_offset, dropout_p, dropout_seed)
     need = workspace_size(p, True)
-    ws = workspace if workspace is not None else _workspace(need, q.device)
-    _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
-                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
-                        ctypes.c_size_t(0 if ws is None else ws.numel()), _stream()))
+    ws = _workspace(need, q.device, workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ctypes.c_size_t(_nbytes(ws)), _stream()))
     return dq, dk, dv
 
 

@@ -45,6 +45,10 @@ class _Attention(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, do, _dlse):
+        if torch.is_grad_enabled():
+            # create_graph=True: the library's backward is not itself
+            # differentiable, so a second-order term would silently be zero.
+            raise RuntimeError("attention: double backward (create_graph=True) is not supported")
         q, k, v, o, lse = ctx.saved_tensors
         if do is None:
             return (None,) * 10
@@ -74,6 +78,9 @@ def attention(q, k, v, scale=None, mask_mode="none", mask=None, *, deterministic
     """
     if scale is None:
         scale = q.shape[-1] ** -0.5
+    # The library takes rows with a unit element stride; other layouts are
+    # copied (autograd routes the gradients back through the copies).
+    q, k, v = (t if t.stride(-1) == 1 else t.contiguous() for t in (q, k, v))
     o, lse = _Attention.apply(q, k, v, float(scale), mask_mode, mask, bool(deterministic),
                               int(causal_offset), float(dropout_p), int(dropout_seed))
     return (o, lse) if return_lse else o

@@ -273,3 +273,13 @@ def test_size_limits_of_32_bit_slice_addressing():
     st, need = wsize(p, 1)
     assert st == 0 and need > 0
     assert call_bwd(p) == 7  # validation passes; stops at the missing workspace, before any launch
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU memory"):
+        E.fwd(q, q, q, 0.125)
+    with pytest.raises(ValueError, match="GPU memory"):
+        E.bwd(q, q, q, q, q, torch.zeros((1, 1, 8)), 0.125)

@@ -90,3 +90,78 @@ def test_self_attention_gradient(dtype, mask):
     rdq, rdk, rdv = dense.vjp(X64, X64, X64, 1.0, A, G64)
     compare("O", y[0, 0].detach().float().cpu().double().numpy(), Y, tag, (dtype, mask))
     compare("dQ", x.grad[0, 0].float().cpu().double().numpy(), rdq + rdk + rdv, tag, (dtype, mask))
+
+
+def test_any_gradient_layout_and_input_views():
+    """o.sum() hands the backward an expanded (all-zero-stride) gradient;
+    inputs may be views with gaps between rows, or rows with a non-unit
+    element stride (copied by attention()).  Each gives the library's
+    backward of the same values, bit for bit."""
+    import exact_tiled_attention_attn_amd as E
+
+    B, H, n, d, c = 1, 2, 300, 64, 0.125
+    g = torch.Generator().manual_seed(11)
+    base = [torch.randn((B, H, n, d), generator=g).to(torch.bfloat16).to(DEV) for _ in range(3)]
+    ro, rl = E.fwd(*base, c, "causal")
+    ones = torch.ones_like(ro)
+    ref = E.bwd(*base, ro, ones, rl, c, "causal", deterministic=True)
+
+    # Expanded upstream gradient.
+    q, k, v = (t.clone().requires_grad_(True) for t in base)
+    E.attention(q, k, v, c, "causal").sum().backward()
+    for x, r in zip((q.grad, k.grad, v.grad), ref):
+        assert torch.equal(x, r)
+
+    # Views with gaps: every other row of a twice-as-tall leaf.
+    tall = [torch.zeros((B, H, 2 * n, d), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    for t, b in zip(tall, base):
+        t[:, :, ::2] = b
+        t.requires_grad_(True)
+    E.attention(*(t[:, :, ::2] for t in tall), c, "causal").sum().backward()
+    for t, r in zip(tall, ref):
+        assert torch.equal(t.grad[:, :, ::2], r) and not t.grad[:, :, 1::2].any()
+
+    # Rows with a non-unit element stride: [B, H, d, n] memory seen as [B, H, n, d].
+    wide = [b.transpose(-1, -2).contiguous().requires_grad_(True) for b in base]
+    E.attention(*(w.transpose(-1, -2) for w in wide), c, "causal").sum().backward()
+    for w, r in zip(wide, ref):
+        assert torch.equal(w.grad.transpose(-1, -2), r)
+
+
+def test_double_backward_is_refused():
+    import exact_tiled_attention_attn_amd as E
+
+    g = torch.Generator().manual_seed(3)
+    q, k, v = (torch.randn((1, 1, 64, 64), generator=g).to(DEV).requires_grad_(True) for _ in range(3))
+    with pytest.raises(RuntimeError, match="double backward"):
+        torch.autograd.grad(E.attention(q, k, v).sum(), q, create_graph=True)
+    o = E.attention(q, k, v)  # a plain backward still works
+    o.backward(torch.ones_like(o))
+    assert q.grad is not None and torch.isfinite(q.grad).all()
+
+
+def test_binding_checks_tensor_arguments():
+    """The library sees only pointers: the binding refuses host tensors,
+    mixed dtypes or devices, and outputs of the wrong shape or dtype before
+    any address reaches it."""
+    import exact_tiled_attention_attn_amd as E
+
+    q, k, v, G = _tensors(1, 2, 100, 64, 64, torch.bfloat16, 5)
+    o, L = E.fwd(q, k, v, 0.125)
+    with pytest.raises(ValueError, match="GPU memory"):
+        E.fwd(q.cpu(), k, v, 0.125)
+    with pytest.raises(TypeError, match="dtype"):
+        E.fwd(q, k.float(), v, 0.125)
+    with pytest.raises(ValueError, match="shape"):
+        E.fwd(q, k, v, 0.125, out=torch.empty((1, 2, 99, 64), dtype=q.dtype, device=DEV))
+    with pytest.raises(TypeError, match="dtype"):
+        E.fwd(q, k, v, 0.125, lse=torch.empty((1, 2, 100), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(TypeError, match="dtype"):
+        E.bwd(q, k, v, o, G.float(), L, 0.125)
+    with pytest.raises(ValueError, match="shape"):
+        E.bwd(q, k, v, o, G, L[:, :, :50], 0.125)
+    with pytest.raises(TypeError, match="dtype"):
+        E.bwd(q, k, v, o, G, L, 0.125, dq=torch.empty(q.shape, device=DEV))
+    with pytest.raises(ValueError, match="GPU memory"):
+        E.fwd(q, k, v, 0.125, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    torch.cuda.synchronize()
