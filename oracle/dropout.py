@@ -79,8 +79,15 @@ def forward(Q, K, V, c, allowed, Z, p8):
     return Y, L
 
 
-def vjp(Q, K, V, c, allowed, Z, p8, G):
-    """dQ, dK, dV of <G, Y> with the keep mask Z held fixed."""
+def vjp(Q, K, V, c, allowed, Z, p8, G, Y=None):
+    """dQ, dK, dV of <G, Y> with the keep mask Z held fixed.
+
+    The row term D_i = sum_j P_ij dPd_ij equals <G_i, Y_i>.  By default it
+    is taken in the first form (exact); given ``Y``, in the second, from that
+    forward output: the reverse procedure consumes the output of a forward
+    run (alphabetamath page, "Reverse procedure", delta_i), which a
+    comparison with a bf16 device run passes as stored.
+    """
     Q, K, V, G = (np.asarray(x, np.float64) for x in (Q, K, V, G))
     A = np.ones(Z.shape, bool) if allowed is None else allowed
     S = np.where(A, c * (Q @ K.T), -np.inf)
@@ -89,5 +96,9 @@ def vjp(Q, K, V, c, allowed, Z, p8, G):
     keep = (256 - p8) / 256.0
     dV = (P * Z).T @ G / keep
     dPd = (G @ V.T) * Z / keep
-    dS = P * (dPd - (P * dPd).sum(axis=1, keepdims=True))
+    if Y is None:
+        D = (P * dPd).sum(axis=1, keepdims=True)
+    else:
+        D = np.sum(G * np.asarray(Y, np.float64), axis=1, keepdims=True)
+    dS = P * (dPd - D)
     return c * (dS @ K), c * (dS.T @ Q), dV

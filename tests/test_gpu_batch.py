@@ -89,7 +89,7 @@ def test_every_unit(dtype, d, v, layout, mask, p):
             if p8:
                 Z = dropout.keep_mask(seed, u, n, nk, p8)[rows]
                 Y, Lr = dropout.forward(Qr, Kh, Vh, c, Ar, Z, p8)
-                rdQ, rdK, rdV = dropout.vjp(Qr, Kh, Vh, c, Ar, Z, p8, Gr)
+                rdQ, rdK, rdV = dropout.vjp(Qr, Kh, Vh, c, Ar, Z, p8, Gr, stored(Y, dtype))
             else:
                 Y, m, ell, Lr = dense.forward(Qr, Kh, Vh, c, Ar)
                 rdQ, rdK, rdV = tiled.reverse(Qr, Kh, Vh, c, Ar, nk, stored(Y, dtype), m, ell, Gr)

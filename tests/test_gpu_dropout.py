@@ -19,7 +19,7 @@ import torch
 
 import workloads as W
 from oracle import dropout
-from tests.gpu_common import DEV, compare
+from tests.gpu_common import DEV, compare, stored
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def test_dropout_parity(dtype, d, v, mask):
         Z = dropout.keep_mask(seed, h, n, nk, p8)
         Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
         Y, Lr = dropout.forward(Qh, Kh, Vh, c, A, Z, p8)
-        rdQ, rdK, rdV = dropout.vjp(Qh, Kh, Vh, c, A, Z, p8, Gh)
+        rdQ, rdK, rdV = dropout.vjp(Qh, Kh, Vh, c, A, Z, p8, Gh, stored(Y, dtype))
         tag = (dtype, d, v, mask, h)
         compare("O", got(o[0, h]), Y, dtype, tag)
         compare("L", got(L[0, h]), Lr, dtype, tag)

@@ -123,3 +123,26 @@ def test_dropout_is_unbiased():
                    for s in range(3000)])
     se = ys.std(axis=0) / np.sqrt(len(ys))
     assert np.all(np.abs(ys.mean(axis=0) - Y0) < 6 * se + 1e-12)
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "bitmask"])
+def test_dropout_vjp_row_term_from_a_forward_output(mask):
+    """D_i = sum_j P_ij dPd_ij = <G_i, Y_i>: given the forward's own output,
+    the Y form equals the default; given a perturbed output (as a bf16 run
+    stores it), it equals the reverse procedure of oracle/tiled.py fed the
+    same output (p = 0, where both apply)."""
+    from oracle import tiled
+
+    rng = np.random.default_rng(5)
+    n, nk, d, v, c = 6, 9, 4, 3, 0.7
+    Q, K, V, G = rng.normal(size=(n, d)), rng.normal(size=(nk, d)), rng.normal(size=(nk, v)), rng.normal(size=(n, v))
+    A = _masks(n, nk, rng)[mask]
+    Z = dropout.keep_mask(8, 2, n, nk, 51)
+    Y, _ = dropout.forward(Q, K, V, c, A, Z, 51)
+    for x, r in zip(dropout.vjp(Q, K, V, c, A, Z, 51, G, Y), dropout.vjp(Q, K, V, c, A, Z, 51, G)):
+        assert np.abs(x - r).max() <= 1e-12 * max(1.0, np.abs(r).max()), mask
+    ones = dropout.keep_mask(8, 2, n, nk, 0)
+    Y0, m, ell, _ = dense.forward(Q, K, V, c, A)
+    Yp = Y0 * (1 + 1e-3 * rng.normal(size=Y0.shape))  # an output off by rounding-sized amounts
+    for x, r in zip(dropout.vjp(Q, K, V, c, A, ones, 0, G, Yp), tiled.reverse(Q, K, V, c, A, nk, Yp, m, ell, G)):
+        assert np.abs(x - r).max() <= 1e-12 * max(1.0, np.abs(r).max()), mask
