@@ -231,7 +231,8 @@ def main():
     avg = {kname: (ms / cnt if cnt else 0.0) for kname, (ms, cnt) in kern.items()}
     fwd_ms = avg["fwd"] + avg["fwd_merge"] + (avg["tile_map"] if w.mask == W.MASK_BITMASK else 0.0)
     n_maps_bwd = (2 if args.deterministic else 1) if w.mask == W.MASK_BITMASK else 0
-    bwd_ms = avg["bwd_pre"] + avg["bwd"] + avg["bwd_post"] + avg["bwd_dq"] + n_maps_bwd * avg["tile_map"]
+    bwd_ms = (avg["bwd_pre"] + avg["bwd"] + avg["bwd_post"] + avg["bwd_dq"] + avg["bwd_dq_merge"]
+              + n_maps_bwd * avg["tile_map"])
     peak = PEAK_TFLOPS[w.dtype]
     # Algorithmic FLOPs each main kernel performs per launch: the forward
     # 2#A(d+v); the key-tile-outer backward 2#A(2d+2v) (S, dP, dV, dK) plus

@@ -26,7 +26,7 @@ STATUS = {
 EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask",
            "attn_timing_enable", "attn_timing_read", "attn_timing_reset",
            "attn_status_str", "attn_last_error", "attn_version"]
-KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post", "bwd_dq", "fwd_merge"]
+KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post", "bwd_dq", "fwd_merge", "bwd_dq_merge"]
 
 
 class AttnError(RuntimeError):

@@ -79,6 +79,8 @@ struct Layout {
   size_t map_bytes = 0, map_dq_bytes = 0, dq_bytes = 0;
   int splits = 1;  // forward key-range splits
   size_t off_Op = 0, off_Lp = 0, op_bytes = 0, lp_bytes = 0;
+  int dq_splits = 1;  // key-range splits of the pipelined dQ kernel
+  size_t off_dqp = 0, dqp_bytes = 0;
 };
 
 int fwd_split_count(const attn_problem& p) {
@@ -86,9 +88,19 @@ int fwd_split_count(const attn_problem& p) {
   return eta::fwd_splits(p.dtype == ATTN_BF16, p.d, p.v, p.B * p.H, t.tq, t.tk, drop_p8(p));
 }
 
+// Pipelined dQ kernel's key-range splits (deterministic path only).
+int dq_split_count(const attn_problem& p) {
+  if (!p.deterministic || drop_p8(p) != 0 ||
+      !eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nkeys(p)))
+    return 1;
+  const Tiles t = dq_tiles(p);
+  return eta::dq_splits(p.B * p.H, t.tq, t.tk);
+}
+
 // Backward workspace: D and L log2(e) (fp32 [B,H,n_pad] each, n_pad = n
 // rounded up to kRowPad); the atomic path adds the fp32 dQ accumulator, the
-// deterministic path the bitmask map at the dQ tiling.
+// deterministic path the bitmask map at the dQ tiling and, when the dQ
+// kernel splits the key range, its fp32 partials (splits x [B,H,n,d]).
 Layout plan(const attn_problem& p, int is_bwd) {
   Layout l;
   const int64_t units = p.B * p.H;
@@ -105,7 +117,10 @@ Layout plan(const attn_problem& p, int is_bwd) {
     l.map_bytes = bitmask ? size_t(mask_units(p) * t.tq * t.tk) : 0;
     l.off_map_dq = l.off_map + align_up(l.map_bytes);
     l.map_dq_bytes = (bitmask && det) ? size_t(mask_units(p) * tq.tq * tq.tk) : 0;
-    l.total = l.off_map_dq + align_up(l.map_dq_bytes);
+    l.dq_splits = dq_split_count(p);
+    l.dqp_bytes = l.dq_splits > 1 ? size_t(l.dq_splits) * size_t(units) * size_t(p.n) * size_t(p.d) * 4 : 0;
+    l.off_dqp = l.off_map_dq + align_up(l.map_dq_bytes);
+    l.total = l.off_dqp + align_up(l.dqp_bytes);
   } else {
     const Tiles t = fwd_tiles(p);
     l.off_map = 0;
@@ -446,7 +461,9 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   const Tiles tdq = dq_tiles(*p);
   b.map_dq = lay.map_dq_bytes ? reinterpret_cast<uint8_t*>(wsb + lay.off_map_dq) : nullptr;
   b.tq_dq = (int32_t)tdq.tq;
-  b.total_dq = p->B * p->H * tdq.tq;
+  b.dq_splits = lay.dq_splits;
+  b.dQpart = lay.dqp_bytes ? reinterpret_cast<float*>(wsb + lay.off_dqp) : nullptr;
+  b.total_dq = p->B * p->H * tdq.tq * lay.dq_splits;
   b.grid_pad_dq = pad8(b.total_dq);
   if (b.grid_pad > 0x7FFFFFFF || b.grid_pad_dq > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
   const int bf = p->dtype == ATTN_BF16;
@@ -469,9 +486,14 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
          return eta::launch_bwd(b, bf, (int)p->d, (int)p->v, p->mask_mode, !det, stream);
        })) != ATTN_OK)
     return st;
-  if (det)
-    return timed(ATTN_KERNEL_BWD_DQ, stream, "dQ launch",
-                 [&] { return eta::launch_bwd_dq(b, bf, (int)p->d, (int)p->v, p->mask_mode, stream); });
+  if (det) {
+    if ((st = timed(ATTN_KERNEL_BWD_DQ, stream, "dQ launch", [&] {
+           return eta::launch_bwd_dq(b, bf, (int)p->d, (int)p->v, p->mask_mode, stream);
+         })) != ATTN_OK || b.dq_splits == 1)
+      return st;
+    return timed(ATTN_KERNEL_BWD_DQ_MERGE, stream, "dQ merge launch",
+                 [&] { return eta::launch_bwd_dq_merge(b, (int)p->d, stream); });
+  }
   return timed(ATTN_KERNEL_BWD_POST, stream, "dQ conversion launch",
                [&] { return eta::launch_bwd_post(b, bf, (int)p->d, stream); });
 }
@@ -555,6 +577,6 @@ attn_status attn_timing_reset(void) {
   return ATTN_OK;
 }
 
-int32_t attn_version(void) { return 300; }
+int32_t attn_version(void) { return 400; }
 
 }  // extern "C"

@@ -95,8 +95,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   __shared__ uint8_t cls_s[MASK == kMaskBitmask ? S::MAXTK : 1];
   __shared__ __attribute__((aligned(1024))) char spare[4096];  // target of the padding copies (any immediate offset)
 
-  const int64_t logical = xcd_logical(blockIdx.x, p.grid_pad_dq, p.total_dq);
-  if (logical < 0) return;
+  const int64_t logical0 = xcd_logical(blockIdx.x, p.grid_pad_dq, p.total_dq);
+  if (logical0 < 0) return;
+  const int split = (int)(logical0 % p.dq_splits);  // key-range split (0 when not splitting)
+  const int64_t logical = logical0 / p.dq_splits;
   const int unit = (int)(logical / p.tq_dq);
   const int qt = p.tq_dq - 1 - (int)(logical % p.tq_dq);  // heaviest causal tiles first
   const int b = unit / p.H, h = unit % p.H;
@@ -453,7 +455,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   };
 
   // ---- main loop -------------------------------------------------------------
+  // This split's share of the key tiles [0, kt_end): [t0, kt_end).
   int t0 = 0;
+  if (p.dq_splits > 1) {
+    const int per = (kt_end + p.dq_splits - 1) / p.dq_splits;
+    t0 = split * per < kt_end ? split * per : kt_end;
+    kt_end = t0 + per < kt_end ? t0 + per : kt_end;
+  }
   if (MASK == kMaskBitmask) {
     __syncthreads();  // tile classes staged
     if (t0 < kt_end && tile_class(t0) == kTileEmpty) t0 = next_tile(t0);
@@ -504,6 +512,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     wait_vm_n<0>();  // copies of empty positions
   }
 
+  if (p.dq_splits > 1) {  // this split's unscaled fp32 partial, for bwd_dq_merge_kernel
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = qa + 32 * u;
+      if (q < n) {
+        float* part = p.dQpart + (((int64_t)split * p.B * p.H + unit) * n + q) * D;
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c0 = db * 32 + 8 * g + 4 * hh;
+            *reinterpret_cast<f32x4*>(part + c0) =
+                f32x4{dq[u][db][4 * g], dq[u][db][4 * g + 1], dq[u][db][4 * g + 2], dq[u][db][4 * g + 3]};
+          }
+      }
+    }
+    return;
+  }
   // Epilogue: dQ = c dQ^T (lane = query; 4 consecutive columns per store).
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -536,6 +562,35 @@ static int launch_dq_pipe_mask(const BwdParams& p, int mask_mode, hipStream_t st
     case kMaskCausal: return launch_dq_pipe<D, DV, kMaskCausal>(p, st);
     default: return launch_dq_pipe<D, DV, kMaskBitmask>(p, st);
   }
+}
+
+// Sum of the key-range splits' partial dQ, in split order (so the result is
+// reproducible bit for bit), times c, converted to bf16.  One thread per
+// (row, 4 columns).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_merge_kernel(BwdParams p) {
+  const int64_t rows = (int64_t)p.B * p.H * p.n;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * (D / 4)) return;
+  const int64_t row = t / (D / 4);
+  const int c4 = (int)(t % (D / 4));
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.dq_splits; ++s) acc += *reinterpret_cast<const f32x4*>(p.dQpart + (s * rows + row) * D + 4 * c4);
+  const int64_t unit = row / p.n, i = row % p.n;
+  const int64_t b = unit / p.H, h = unit % p.H;
+  const int64_t off = b * p.sq[0] + h * p.sq[1] + i * p.sq[2] + 4 * c4;
+  *reinterpret_cast<u32x2*>((char*)p.dQ + off * 2) =
+      u32x2{pack_bf16x2(acc[0] * p.scale, acc[1] * p.scale), pack_bf16x2(acc[2] * p.scale, acc[3] * p.scale)};
+}
+
+int launch_bwd_dq_merge(const BwdParams& p, int d, void* stream) {
+  const int64_t threads = (int64_t)p.B * p.H * p.n * (d / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  hipStream_t st = (hipStream_t)stream;
+  if (d == 128) hipLaunchKernelGGL((bwd_dq_merge_kernel<128>), grid, block, 0, st, p);
+  else if (d == 64) hipLaunchKernelGGL((bwd_dq_merge_kernel<64>), grid, block, 0, st, p);
+  else return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
 }
 
 int launch_bwd_dq_pipe(const BwdParams& p, int d, int v, int mask_mode, void* stream) {

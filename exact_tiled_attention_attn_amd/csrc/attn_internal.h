@@ -93,8 +93,13 @@ struct BwdParams {
   // Query-tile-outer dQ kernel (deterministic path): tiles of kDqBq queries.
   const uint8_t* map_dq;  // bitmask tile map at the dQ tiling, else null
   int32_t tq_dq;
-  int64_t total_dq;
+  int64_t total_dq;      // B H tq_dq dq_splits workgroups
   int64_t grid_pad_dq;
+  // Key-range splits of the pipelined dQ kernel (1 = none): split s writes its
+  // fp32 partial dQ (unscaled) for [B, H, n, d] to dQpart + s B H n d, and
+  // bwd_dq_merge_kernel adds the splits in order and applies c.
+  int32_t dq_splits;
+  float* dQpart;
   DropParams drop;
 };
 
@@ -136,6 +141,17 @@ inline bool bwd_dq_pipe_supported(int bf16, int64_t d, int64_t v, int mask_mode,
   return mask_mode != 2 || (nk + kDqPipeBk - 1) / kDqPipeBk <= kDqPipeMaxTk;
 }
 int launch_bwd_dq_pipe(const BwdParams& p, int d, int v, int mask_mode, void* stream);
+// Key-range splits of the pipelined dQ kernel: > 1 only for few query tiles
+// against many key tiles (B H tq_dq < 256), at least four key tiles each.
+inline int dq_splits(int64_t units, int64_t tq_dq, int64_t tk_dq) {
+  const int64_t wgs = units * tq_dq;
+  if (wgs >= 256) return 1;
+  int64_t s = (512 + wgs - 1) / wgs;
+  if (s > tk_dq / 4) s = tk_dq / 4;
+  if (s > 16) s = 16;
+  return s < 2 ? 1 : (int)s;
+}
+int launch_bwd_dq_merge(const BwdParams& p, int d, void* stream);
 // Keep decisions of dropout for rows [i0, i0 + rows) x keys [j0, j0 + cols)
 // of one unit, as bytes 0 / 1 (row-major, `cols` per row); i0, j0 multiples of 4.
 int launch_dropout_mask(const DropParams& d, uint32_t unit, int64_t i0, int64_t j0, int rows, int cols,

@@ -136,10 +136,14 @@ typedef struct {
  * needs for this problem.  Forward: the tile map of bitmask mode, and, when
  * few query tiles face many key tiles (bf16, d and v in {64, 128}, no
  * dropout), the partial results of the key-range splits, S B H n (v + 1) * 4
- * bytes for S <= 16 splits (0 bytes if neither applies).  Backward: D (4 B H n bytes), plus the fp32 dQ accumulator
- * (4 B H n d bytes) when deterministic = 0, plus the bitmask tile map(s);
- * every region 256-byte aligned.  Validates the problem like the compute
- * calls. */
+ * bytes for S <= 16 splits (0 bytes if neither applies).  Backward: D and
+ * L log2(e) (4 B H n_pad bytes each, n_pad = n rounded up to 128), plus the
+ * fp32 dQ accumulator (4 B H n d bytes) when deterministic = 0, plus the
+ * bitmask tile map(s), plus, when deterministic = 1 and few query tiles face
+ * many key tiles (bf16 with (d, v) in {(128,128), (64,128), (64,64)}, no
+ * dropout), the dQ kernel's key-range partials, S B H n d * 4 bytes for
+ * S <= 16 splits; every region 256-byte aligned.  Validates the problem like
+ * the compute calls. */
 attn_status attn_workspace_size(const attn_problem* p, int is_bwd, size_t* bytes);
 
 /* Forward: O [B,H,n,v] (dtype) and L [B,H,n] (fp32, natural-log logsumexp
@@ -159,7 +163,10 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
  * mode), the key-tile-outer recompute kernel (dK, dV in registers), then
  * either dQ by fp32 atomics in that kernel plus a conversion pass
  * (deterministic = 0; dQ may differ run to run in the last bits) or a
- * query-tile-outer dQ kernel (deterministic = 1; bitwise reproducible). */
+ * query-tile-outer dQ kernel (deterministic = 1; bitwise reproducible).
+ * With key-range splits of that kernel (see attn_workspace_size) each split
+ * writes an fp32 partial dQ and a merge kernel adds them in split order
+ * (still bitwise reproducible). */
 attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const void* V,
                      const void* O, const void* dO, const float* L,
                      void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
@@ -197,7 +204,8 @@ typedef enum {
   ATTN_KERNEL_BWD_POST = 4, /* dQ conversion (deterministic = 0) */
   ATTN_KERNEL_BWD_DQ = 5,   /* query-tile-outer dQ (deterministic = 1) */
   ATTN_KERNEL_FWD_MERGE = 6, /* merge of the forward's key-range splits */
-  ATTN_KERNEL_COUNT = 7
+  ATTN_KERNEL_BWD_DQ_MERGE = 7, /* sum of the dQ kernel's key-range splits */
+  ATTN_KERNEL_COUNT = 8
 } attn_kernel;
 
 /* Opt-in kernel timing (off by default; not thread-safe; for measurement

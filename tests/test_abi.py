@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(E.EXPORTS)
     for name in names:
         assert getattr(lib, name) is not None
-    assert lib.attn_version() == 300
+    assert lib.attn_version() == 400
 
 
 def problem(B=1, H=2, n=100, d=64, v=64, dtype=1, mask_mode=0, contiguous=True):
