@@ -37,22 +37,39 @@ __global__ __launch_bounds__(256) void tile_map_kernel(MapParams p) {
   const int64_t W = (nk + 31) / 32;
   const uint32_t tail_bits = (nk % 32) ? ((1u << (nk % 32)) - 1u) : 0xFFFFFFFFu;
   const int wpt = p.bk / 32;  // words per key tile
-  for (int kt = threadIdx.x; kt < p.tk; kt += blockDim.x) {
+  // 64 key tiles per pass, each shared by four row groups (rows q0 + g,
+  // q0 + g + 4, ...); the groups' any / all are combined through LDS.
+  constexpr int kGroups = 4;
+  __shared__ uint32_t s_any[kGroups][64];
+  __shared__ uint32_t s_all[kGroups][64];
+  const int col = threadIdx.x & 63, g = threadIdx.x >> 6;
+  for (int k0 = 0; k0 < p.tk; k0 += 64) {  // uniform trip count: every thread reaches the barriers
+    const int kt = k0 + col;
     uint32_t any = 0;
     bool all = (int64_t)(kt + 1) * p.bk <= nk;
-    for (int64_t r = q0; r < q1; ++r) {
-      const uint32_t* row = p.mask + base + r * p.mask_si;
-      for (int wi = 0; wi < wpt; ++wi) {
-        const int64_t wd = (int64_t)kt * wpt + wi;
-        if (wd < W) {
-          const uint32_t valid = (wd == W - 1) ? tail_bits : 0xFFFFFFFFu;
-          const uint32_t x = row[wd] & valid;
-          any |= x;
-          all = all && (x == valid);
+    if (kt < p.tk) {
+      for (int64_t r = q0 + g; r < q1; r += kGroups) {
+        const uint32_t* row = p.mask + base + r * p.mask_si;
+        for (int wi = 0; wi < wpt; ++wi) {
+          const int64_t wd = (int64_t)kt * wpt + wi;
+          if (wd < W) {
+            const uint32_t valid = (wd == W - 1) ? tail_bits : 0xFFFFFFFFu;
+            const uint32_t x = row[wd] & valid;
+            any |= x;
+            all = all && (x == valid);
+          }
         }
       }
     }
-    out[kt] = any ? (all ? kTileFull : kTilePartial) : kTileEmpty;
+    s_any[g][col] = any;
+    s_all[g][col] = all ? 1u : 0u;
+    __syncthreads();
+    if (g == 0 && kt < p.tk) {
+      const uint32_t an = s_any[0][col] | s_any[1][col] | s_any[2][col] | s_any[3][col];
+      const uint32_t al = s_all[0][col] & s_all[1][col] & s_all[2][col] & s_all[3][col];
+      out[kt] = an ? (al ? kTileFull : kTilePartial) : kTileEmpty;
+    }
+    __syncthreads();
   }
 }
 
