@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
               bool ok = kvalid;
               if constexpr (MASK == kMaskCausal) ok = ok && key <= qq + coff;
               if constexpr (MASK == kMaskBitmask)
-                ok = ok && ((Ms[(ql + e) * S::MWORDS + (klocal >> 5)] >> (klocal & 31)) & 1u);
+                ok = ok & (((Ms[(ql + e) * S::MWORDS + (klocal >> 5)] >> (klocal & 31)) & 1u) != 0u);  // no short-circuit: no branch per read
               pv = ok ? pv : 0.f;
             }
             if constexpr (DROP) {

@@ -334,7 +334,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       const int ql = 32 * c + perm(8 * (r >> 2) + 4 * hh + (r & 3));
       bool ok = kvalid;
       if constexpr (MASK == kMaskCausal) ok = ok && key <= q0 + ql + coff;
-      if constexpr (MASK == kMaskBitmask) ok = ok && ((ms[ql * S::MWORDS + w] >> (lane & 31)) & 1u);
+      // The word is read by every lane (the stage always holds the tile's words) and
+      // combined without short-circuit, so the 16 reads issue together, not as 16
+      // branches that each wait for their own read.
+      if constexpr (MASK == kMaskBitmask) ok = ok & (((ms[ql * S::MWORDS + w] >> (lane & 31)) & 1u) != 0u);
       sc[r] = ok ? sc[r] : masked_score;
     }
   };
