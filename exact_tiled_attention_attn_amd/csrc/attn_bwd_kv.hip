@@ -112,11 +112,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const uint32_t* mbase = nullptr;
   if constexpr (MASK == kMaskBitmask) mbase = p.mask + b * p.mask_sb + h * p.mask_sh;
 
-  // Clear the ring once: tile rows that a fill leaves untouched (past n)
-  // then always hold finite values.
-  for (int c = tid; c < S::NSTAGE * S::QTILE / 16; c += 256) reinterpret_cast<u32x4*>(qs)[c] = u32x4{0, 0, 0, 0};
-  for (int c = tid; c < S::NSTAGE * S::OTILE / 16; c += 256) reinterpret_cast<u32x4*>(os)[c] = u32x4{0, 0, 0, 0};
-  for (int c = tid; c < S::NSTAGE * S::LDB / 16; c += 256) reinterpret_cast<u32x4*>(lds_ld)[c] = u32x4{0, 0, 0, 0};
+  // Clear the ring once when the last query tile is partial: tile rows that a
+  // fill leaves untouched (past n) then always hold finite values.  With n a
+  // multiple of the tile height every fill writes every row the kernel reads
+  // (row pads are never read), so short workgroups skip the 34 stores per
+  // thread.
+  if (n % S::BQ != 0) {
+    for (int c = tid; c < S::NSTAGE * S::QTILE / 16; c += 256) reinterpret_cast<u32x4*>(qs)[c] = u32x4{0, 0, 0, 0};
+    for (int c = tid; c < S::NSTAGE * S::OTILE / 16; c += 256) reinterpret_cast<u32x4*>(os)[c] = u32x4{0, 0, 0, 0};
+    for (int c = tid; c < S::NSTAGE * S::LDB / 16; c += 256) reinterpret_cast<u32x4*>(lds_ld)[c] = u32x4{0, 0, 0, 0};
+  }
 
   // Query-tile sequence: from the last tile down to the first that can hold
   // an allowed pair (causal: the tile containing row k0 - coff); bitmask tiles come
