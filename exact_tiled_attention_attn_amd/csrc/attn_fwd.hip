@@ -504,11 +504,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kbase = (lane & 31) * S::KS + 16 * hh;
   const int vbase = (4 * hh + ((lane & 15) >> 2)) * S::VS + (16 * g1 + 4 * (lane & 3)) * 2;
 
-  // V rows past nk are multiplied by zero weights: clear both V buffers once
-  // so that they never hold non-finite bit patterns.
-  for (int c = tid; c < S::VTILE / 16; c += 256) {
-    reinterpret_cast<u32x4*>(vbuf0)[c] = u32x4{0, 0, 0, 0};
-    reinterpret_cast<u32x4*>(vbuf1)[c] = u32x4{0, 0, 0, 0};
+  // V rows past nk are multiplied by zero weights: when the last key tile is
+  // partial, clear both V buffers once so that they never hold non-finite bit
+  // patterns.  With nk a multiple of the tile height every fill writes every
+  // row that is read.
+  if (nk % S::BK != 0) {
+    for (int c = tid; c < S::VTILE / 16; c += 256) {
+      reinterpret_cast<u32x4*>(vbuf0)[c] = u32x4{0, 0, 0, 0};
+      reinterpret_cast<u32x4*>(vbuf1)[c] = u32x4{0, 0, 0, 0};
+    }
   }
 
   float m_run = -INFINITY, l_run = 0.f;
