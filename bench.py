@@ -98,51 +98,145 @@ def calibrate_copy():
                       "launches": 3}), flush=True)
 
 
-def cpu_baseline(prob, budget_s: float) -> dict:
-    """The oracle (dense float64 forward + VJP) on one unit of the workload.
-
-    Starts with the first 2048 query rows and keys of unit (0, 0) -- a
-    sub-problem of the same recipe -- and doubles the size while the
-    predicted time stays within the budget, up to the full unit.
-    """
+def host_info() -> dict:
+    """CPU model, usable cores and the BLAS library numpy runs on."""
     import threadpoolctl
 
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    return {"cpu": model, "usable_cores": len(os.sched_getaffinity(0)),
+            "blas": ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "unknown",
+            "blas_threads": max((p.get("num_threads", 1) for p in blas), default=1)}
+
+
+def _time_route(prob, route: str, budget_s: float):
+    """Time one oracle route on growing leading sub-problems of unit (0, 0).
+
+    Starts at 2048 query rows and keys (the same recipe, cut to its leading
+    block; rows left without an allowed key get their diagonal key) and
+    doubles while the predicted time stays within the budget, up to the full
+    unit.  Returns (rows, pairs, seconds, flops) of the last size timed.
+    """
     import workloads as W
-    from oracle import dense
+    from oracle import dense, tiled
 
     w = prob.w
     n = w.n
     Q, K, V, G = (getattr(prob, x)[0, 0].astype(np.float64) for x in "QKVG")
-    ns = min(2048, n)
-    result = None
-    spent = 0.0
+    ns, spent, result = min(2048, n), 0.0, None
     while True:
         A = None if w.mask == W.MASK_NONE else prob.allowed(0)[:ns, :ns]
         if A is not None and not A.any(axis=1).all():
             A = A.copy()
-            A[np.arange(ns), np.arange(ns)] = True  # keep the sub-problem's rows nonempty
+            A[np.arange(ns), np.arange(ns)] = True
         pairs = ns * ns if A is None else int(A.sum())
         t0 = time.perf_counter()
-        dense.forward(Q[:ns], K[:ns], V[:ns], w.scale, A)
-        dense.vjp(Q[:ns], K[:ns], V[:ns], w.scale, A, G[:ns])
+        if route == "dense":
+            dense.forward(Q[:ns], K[:ns], V[:ns], w.scale, A)
+            dense.vjp(Q[:ns], K[:ns], V[:ns], w.scale, A, G[:ns])
+        else:
+            b = w.oracle_blocks[0]
+            Y, m, ell, _ = tiled.forward(Q[:ns], K[:ns], V[:ns], w.scale, A, b)
+            tiled.reverse(Q[:ns], K[:ns], V[:ns], w.scale, A, b, Y, m, ell, G[:ns])
         dt = time.perf_counter() - t0
         spent += dt
-        flops = 2.0 * pairs * (w.d + w.v) + 2.0 * pairs * (3 * w.d + 2 * w.v)
-        result = (ns, pairs, dt, flops)
+        result = (ns, pairs, dt, 2.0 * pairs * (w.d + w.v) + 2.0 * pairs * (3 * w.d + 2 * w.v))
         if ns >= n or spent + 4.2 * dt > budget_s:
-            break
+            return result
         ns = min(n, 2 * ns)
-    ns, pairs, dt, flops = result
-    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+
+
+def cpu_baseline(prob, budget_s: float) -> dict:
+    """The oracle as it stands, timed on the host cores: the dense definition
+    (forward + VJP, oracle/dense.py) as ``value``, the key-block procedure
+    (forward + reverse, oracle/tiled.py, at the workload's oracle block size)
+    beside it; half the budget each."""
+    w = prob.w
+    host = host_info()
+    out = {}
+    for route in ("dense", "tiled"):
+        ns, pairs, dt, flops = _time_route(prob, route, budget_s / 2)
+        what = ("dense float64 forward + VJP" if route == "dense"
+                else f"key-block float64 forward + reverse, block {w.oracle_blocks[0]}")
+        out[route] = {"value": flops / dt / 1e12, "seconds": round(dt, 3),
+                      "sample": f"unit (b=0, h=0), query rows and keys 0..{ns - 1} of {w.n} ({pairs} allowed pairs): "
+                                f"{what}"}
+    d = out["dense"]
     return {
-        "value": flops / dt / 1e12,
+        "value": d["value"],
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(host["blas_threads"]),
         "kind": "oracle",
-        "sample": (f"unit (b=0, h=0), query rows and keys 0..{ns - 1} of {n} ({pairs} allowed pairs): "
-                   f"dense float64 forward + VJP, {dt:.2f} s; host has "
-                   f"{len(os.sched_getaffinity(0))} usable cores"),
+        "sample": d["sample"] + f", {d['seconds']:.2f} s",
+        "tiled": {"value": out["tiled"]["value"], "unit": "TFLOP/s",
+                  "sample": out["tiled"]["sample"] + f", {out['tiled']['seconds']:.2f} s"},
+        "host": host,
     }
+
+
+class ClockSampler:
+    """Samples the GPU engine clock (amdsmi, current GFX clock) on a host
+    thread while the timed steps run; a missing or failing amdsmi gives no
+    samples, not an error."""
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._handle = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            self._amdsmi = None
+
+    def _read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._handle is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+        if self._amdsmi is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
+
+    def summary(self):
+        if not self.samples:
+            return None
+        x = sorted(self.samples)
+        return {"median_mhz": x[len(x) // 2], "min_mhz": x[0], "max_mhz": x[-1], "samples": len(x),
+                "source": "amdsmi current GFX clock, sampled every 2 ms during the timed steps"}
 
 
 def main():
@@ -215,12 +309,14 @@ def main():
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    sclk = clock.summary()
     kern = E.timing_read()
     E.timing_enable(False)
     for t in (o, lse, dq, dk, dv):
@@ -269,7 +365,13 @@ def main():
                      "frac": round(achieved / peak, 4),
                      "traffic": (recorded_traffic(w.name, args.deterministic, dominant)
                                  if nq == w.n and not args.dropout else None)},
+        "sclk": sclk,
     }
+    if sclk:
+        # The published peak assumes the 2.4 GHz engine clock; against the
+        # clock measured during the steps:
+        at = peak * sclk["median_mhz"] / 2400.0
+        out["roofline"].update(peak_at_sclk=round(at, 1), frac_at_sclk=round(achieved / at, 4))
     if args.dropout:
         out["config"].update(dropout_p=args.dropout, dropout_seed=1234)
     if nq != w.n:

@@ -24,7 +24,7 @@ STATUS = {
     7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP",
 }
 EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask",
-           "attn_timing_enable", "attn_timing_read", "attn_timing_reset",
+           "attn_debug_count_tiles", "attn_timing_enable", "attn_timing_read", "attn_timing_reset",
            "attn_status_str", "attn_last_error", "attn_version"]
 KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post", "bwd_dq", "fwd_merge", "bwd_dq_merge"]
 
@@ -72,7 +72,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_debug_tile_map.argtypes = [P, ctypes.c_int, vp, sz, i32p, i32p, i32p, i32p, vp, sz, vp]
     lib.attn_debug_dropout_mask.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_int32, vp, sz, vp]
-    for f in ("attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask"):
+    lib.attn_debug_count_tiles.argtypes = [vp]
+    for f in ("attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask",
+              "attn_debug_count_tiles"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -298,6 +300,16 @@ def dropout_mask(q, k, v, dropout_p, dropout_seed, b, h, i0, j0, rows, cols):
     _check(lib.attn_debug_dropout_mask(ctypes.byref(p), b, h, i0, j0, rows, cols, _ptr(out), out.numel(),
                                        _stream()))
     return out
+
+
+def count_tiles(counters):
+    """Set (an int64 device tensor of 3 zeros) or clear (None) the executed-tile
+    counters: forward, key-tile-outer backward, query-tile-outer dQ."""
+    if counters is not None:
+        _on_gpu("counters", counters, dtype=torch.int64, shape=(3,))
+        if not counters.is_contiguous():
+            raise ValueError("counters must be contiguous")
+    _check(load_library().attn_debug_count_tiles(_ptr(counters)))
 
 
 def timing_enable(on: bool = True):

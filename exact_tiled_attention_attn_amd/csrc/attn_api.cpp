@@ -16,6 +16,9 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Executed-tile counters of attn_debug_count_tiles (device words), or null.
+unsigned long long* g_tile_counters = nullptr;
+
 attn_status fail(attn_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -378,6 +381,7 @@ attn_status attn_fwd(const attn_problem* p, const void* Q, const void* K, const 
   f.grid_pad = pad8(f.total);
   f.scale2 = (float)(p->scale * 1.4426950408889634);
   f.drop = drop_params(*p);
+  f.tile_count = g_tile_counters;
   if (f.grid_pad > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
   if ((st = timed(ATTN_KERNEL_FWD, stream, "forward launch", [&] {
          return eta::launch_fwd(f, p->dtype == ATTN_BF16, (int)p->d, (int)p->v, p->mask_mode, stream);
@@ -465,6 +469,8 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.dQpart = lay.dqp_bytes ? reinterpret_cast<float*>(wsb + lay.off_dqp) : nullptr;
   b.total_dq = p->B * p->H * tdq.tq * lay.dq_splits;
   b.grid_pad_dq = pad8(b.total_dq);
+  b.tile_count_kv = g_tile_counters ? g_tile_counters + 1 : nullptr;
+  b.tile_count_dq = g_tile_counters ? g_tile_counters + 2 : nullptr;
   if (b.grid_pad > 0x7FFFFFFF || b.grid_pad_dq > 0x7FFFFFFF) return fail(ATTN_ERR_SHAPE, "grid too large");
   const int bf = p->dtype == ATTN_BF16;
   if ((st = timed(ATTN_KERNEL_BWD_PRE, stream, "D preprocess launch",
@@ -540,6 +546,13 @@ attn_status attn_debug_dropout_mask(const attn_problem* p, int64_t b, int64_t h,
                     "dropout mask launch");
 }
 
+attn_status attn_debug_count_tiles(uint64_t* counters_dev) {
+  if (reinterpret_cast<uintptr_t>(counters_dev) % 8)
+    return fail(ATTN_ERR_STRIDE, "tile counters must be 8-byte aligned");
+  g_tile_counters = reinterpret_cast<unsigned long long*>(counters_dev);
+  return ATTN_OK;
+}
+
 const char* attn_status_str(int s) {
   switch (s) {
     case ATTN_OK: return "ok";
@@ -577,6 +590,6 @@ attn_status attn_timing_reset(void) {
   return ATTN_OK;
 }
 
-int32_t attn_version(void) { return 400; }
+int32_t attn_version(void) { return 500; }
 
 }  // extern "C"

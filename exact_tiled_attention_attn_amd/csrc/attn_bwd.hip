@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   }
   if constexpr (S::DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct loads landed
   __syncthreads();
-  int buf = 0;
+  int buf = 0, ntiles = 0;
 
   while (qt >= 0) {
     const int nq = next_tile(qt);
@@ -472,7 +472,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     __syncthreads();
     buf ^= 1;
     qt = nq;
+    ++ntiles;
   }
+  count_tiles(p.tile_count_kv, ntiles);
 
   // Epilogue: dK = c dK^T, dV = dV^T (lane = key; 4 consecutive columns per store).
   if (kvalid) {

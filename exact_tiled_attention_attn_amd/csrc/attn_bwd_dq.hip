@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
     lstore(0);
   }
   __syncthreads();
-  int buf = 0;
+  int buf = 0, ntiles = 0;
   const int wave_k_hi = q0 + 32 * w + 31 + coff;  // last key this wave's rows can allow
   const float scale2 = p.scale2;
 
@@ -306,7 +306,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
     __syncthreads();
     buf ^= 1;
     kt = kn;
+    ++ntiles;
   }
+  count_tiles(p.tile_count_dq, ntiles);
 
   // dQ = c dQ^T (lane = query row; 4 consecutive columns per store).
   if (qvalid) {

@@ -468,6 +468,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   }
   if (t0 >= kt_end) t0 = -1;
   int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
+  int ntiles = 0;
   if (t0 >= 0) {  // workgroup-uniform
     fill(t0, 0);
     fill(t1, 1);
@@ -497,6 +498,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, k0);
       step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, [] {}, std::false_type{});
+      ++ntiles;
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;
@@ -511,6 +513,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       for (int i = 0; i < S::NDB; ++i) after_nops_a(dq[u][i]);
     wait_vm_n<0>();  // copies of empty positions
   }
+  count_tiles(p.tile_count_dq, ntiles);
 
   if (p.dq_splits > 1) {  // this split's unscaled fp32 partial, for bwd_dq_merge_kernel
 #pragma unroll

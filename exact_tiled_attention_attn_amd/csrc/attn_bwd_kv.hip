@@ -485,6 +485,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   }
   if (t0 < qt_first) t0 = -1;
   int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
+  int ntiles = 0;
   __syncthreads();  // ring cleared
   if (t0 >= 0) {  // workgroup-uniform
     fill(t0, 0);
@@ -520,6 +521,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, q0);
       step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA, [] {}, std::false_type{});
+      ++ntiles;
       if (t1 < 0) break;
       t0 = t1;
       t1 = t2;
@@ -534,6 +536,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     for (int i = 0; i < S::NVB; ++i) after_nops_a(dv[i]);
     wait_vm_n<0>();  // copies of empty positions
   }
+  count_tiles(p.tile_count_kv, ntiles);
 
   // Epilogue: dK = c dK^T, dV = dV^T (lane = key; 4 consecutive columns per store).
   if (kvalid) {

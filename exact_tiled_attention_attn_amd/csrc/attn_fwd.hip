@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int vb = 0; vb < S::NVB; ++vb) o[vb] = f32x16{};
 
-  int kt = 0;
+  int kt = 0, ntiles = 0;
   if (MASK == kMaskBitmask && kt < kt_end && tile_class(kt) == kTileEmpty) kt = next_tile(kt);
   if (kt < kt_end) {
     gload(kt);
@@ -344,7 +344,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     buf ^= 1;
     kt = kn;
+    ++ntiles;
   }
+  count_tiles(p.tile_count, ntiles);
 
   // Epilogue: O = acc / l, L = (m + log2 l) ln 2.
   const float l_tot = sum_halves(l_run);
@@ -591,6 +593,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     kt_end = t0 + per < kt_end ? t0 + per : kt_end;
   }
   if (MASK == kMaskBitmask && t0 < kt_end && tile_class(t0) == kTileEmpty) t0 = next_tile(t0);
+  int ntiles = 0;
   __syncthreads();  // V buffers cleared
   if (t0 < kt_end) {  // workgroup-uniform
     int t1 = next_tile(t0);
@@ -735,11 +738,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     while (true) {
       step(sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
+      ++ntiles;
       if (t0 >= kt_end) break;
       step(sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
+      ++ntiles;
       if (t0 >= kt_end) break;
     }
   }
+  count_tiles(p.tile_count, ntiles);
 
   const float l_tot = sum_halves(l_run);
   const float l_norm = l_tot;

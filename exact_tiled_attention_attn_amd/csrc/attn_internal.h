@@ -61,6 +61,9 @@ struct FwdParams {
   int32_t splits;
   float* Opart;
   float* Lpart;
+  // Debug tile counter (attn_debug_count_tiles), else null: each workgroup
+  // adds the number of (query tile, key tile) pairs it computed.
+  unsigned long long* tile_count;
 };
 
 struct BwdParams {
@@ -101,6 +104,11 @@ struct BwdParams {
   int32_t dq_splits;
   float* dQpart;
   DropParams drop;
+  // Debug tile counters (attn_debug_count_tiles), else null: the key-tile-
+  // outer kernel adds its computed tiles to tile_count_kv, the query-tile-
+  // outer dQ kernel to tile_count_dq.
+  unsigned long long* tile_count_kv;
+  unsigned long long* tile_count_dq;
 };
 
 struct MapParams {

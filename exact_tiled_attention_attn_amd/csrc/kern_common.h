@@ -402,6 +402,12 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, G | (G << 2) | (G << 4) | (G << 6), 0xF, 0xF, false);
 }
 
+// Debug tile counter: one 64-bit atomic add per workgroup, by its first lane,
+// of the tiles the workgroup computed (ntiles is workgroup-uniform).
+__device__ __forceinline__ void count_tiles(unsigned long long* counter, int ntiles) {
+  if (counter != nullptr && threadIdx.x == 0 && ntiles > 0) atomicAdd(counter, (unsigned long long)ntiles);
+}
+
 // Classification of a tile from its corners for none/causal masks: the same
 // rule the skip logic and the partial-tile masking follow.  nq query rows,
 // nk key rows; causal: key j allowed for query i iff j <= i + coff.

@@ -195,6 +195,22 @@ attn_status attn_debug_dropout_mask(const attn_problem* p, int64_t b, int64_t h,
                                     int32_t rows, int32_t cols, uint8_t* out_dev, size_t out_bytes,
                                     void* stream);
 
+/* Debug: count the tiles the kernels compute.  The classification of
+ * attn_debug_tile_map fixes which (query tile x key tile) pairs hold an
+ * allowed pair; the kernels must compute exactly those and skip the rest
+ * (alphabetamath page, forward procedure: blocks whose intersection with A_i
+ * is empty are skipped; ob1 page, part 3: key blocks right of the causal
+ * diagonal are skipped).  While counters_dev is set, every forward kernel
+ * adds the number of tiles it computed (at the forward's tiling, is_bwd = 0
+ * of attn_debug_tile_map) to counters_dev[0], every key-tile-outer backward
+ * kernel to counters_dev[1] (is_bwd = 1), every query-tile-outer dQ kernel
+ * to counters_dev[2] (is_bwd = 2), with one 64-bit atomic add per
+ * workgroup; key-range splits add their shares.  counters_dev: three
+ * caller-owned uint64 device words, 8-byte aligned, cleared by the caller;
+ * NULL (the default) switches counting off.  A process-wide setting, not
+ * thread-safe; ATTN_ERR_STRIDE for a misaligned pointer. */
+attn_status attn_debug_count_tiles(uint64_t* counters_dev);
+
 /* Kernel classes reported by the timing facility below. */
 typedef enum {
   ATTN_KERNEL_TILE_MAP = 0, /* bitmask tile classification */
@@ -225,7 +241,8 @@ const char* attn_status_str(int status);
 /* Thread-local detail of the last failing call on this thread ("" if none). */
 const char* attn_last_error(void);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
+/* Library version, major * 10000 + minor * 100 + patch (0.5.0 added
+ * attn_debug_count_tiles). */
 int32_t attn_version(void);
 
 #ifdef __cplusplus

@@ -10,35 +10,42 @@ too: the figure is what the backward graph can reach.
 
 from __future__ import annotations
 
+from dataclasses import dataclass, field
+
 import torch
 
 
-class SavedBytes:
-    def __init__(self):
-        self.keys = set()
-        self.bytes = 0
-        self.events = 0
-
-    def pack(self, t: torch.Tensor):
-        self.events += 1
-        key = (t.untyped_storage().data_ptr(), t.storage_offset(), tuple(t.shape), tuple(t.stride()), t.dtype)
-        if key not in self.keys:
-            self.keys.add(key)
-            self.bytes += t.numel() * t.element_size()
-        return t.detach()  # same storage; the hook must not keep the graph's own tensor
+def buffer_key(t: torch.Tensor) -> tuple:
+    """Identity of one retained buffer: the page's definition, kept so that
+    the figures compare with its own."""
+    return (t.untyped_storage().data_ptr(), t.storage_offset(), tuple(t.shape), tuple(t.stride()), t.dtype)
 
 
-def payload(fn, *args, grad=None):
-    """Run fn forward and backward under the hook; the counter afterwards."""
-    c = SavedBytes()
-    with torch.autograd.graph.saved_tensors_hooks(c.pack, lambda t: t):
-        out = fn(*args)
-        out = out[0] if isinstance(out, tuple) else out
-        if grad is None:
-            out.sum().backward()
-        else:
-            out.backward(grad)
-    return c
+@dataclass
+class Retained:
+    """Buffers the pack hook saw: bytes per distinct buffer, and hook calls."""
+
+    sizes: dict = field(default_factory=dict)
+    events: int = 0
+
+    @property
+    def bytes(self) -> int:
+        return sum(self.sizes.values())
+
+
+def retained_by(run) -> Retained:
+    """Call ``run()`` -- a forward pass and its backward -- with a pack hook
+    that records every tensor autograd saves for the backward."""
+    seen = Retained()
+
+    def pack(t):
+        seen.events += 1
+        seen.sizes.setdefault(buffer_key(t), t.numel() * t.element_size())
+        return (t.detach(),)  # a fresh alias: the hook keeps no reference to the graph's tensor
+
+    with torch.autograd.graph.saved_tensors_hooks(pack, lambda packed: packed[0]):
+        run()
+    return seen
 
 
 def traced_tiled_forward(q, k, v, scale, block):

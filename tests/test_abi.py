@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(E.EXPORTS)
     for name in names:
         assert getattr(lib, name) is not None
-    assert lib.attn_version() == 400
+    assert lib.attn_version() == 500
 
 
 def problem(B=1, H=2, n=100, d=64, v=64, dtype=1, mask_mode=0, contiguous=True):
@@ -230,6 +230,15 @@ def test_workspace_checks():
     assert call_bwd(p, ws=FAKE + (20 << 30), ws_bytes=need - 1) == 7
     assert call_bwd(p, ws=FAKE + (20 << 30) + 16, ws_bytes=need) == 7  # not 256-byte aligned
     assert call_bwd(p, ws=FAKE, ws_bytes=need) == 8  # workspace overlaps Q
+
+
+def test_tile_counter_setting():
+    """attn_debug_count_tiles only records the pointer (no device access):
+    misaligned pointers are refused, NULL switches counting off."""
+    lib = E.load_library()
+    assert lib.attn_debug_count_tiles(ctypes.c_void_p(FAKE + 4)) == 3 and "aligned" in err()
+    assert lib.attn_debug_count_tiles(ctypes.c_void_p(FAKE)) == 0
+    assert lib.attn_debug_count_tiles(None) == 0
 
 
 def test_status_strings():

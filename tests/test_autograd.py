@@ -20,7 +20,7 @@ import workloads as W
 from exact_tiled_attention_attn_amd import _binding
 from exact_tiled_attention_attn_amd import autograd as AG
 from oracle import dense
-from tests.payload import payload, traced_tiled_forward
+from tests.payload import retained_by, traced_tiled_forward
 
 
 def _allowed(mask_mode, mask, n, nk, offset=0):
@@ -93,7 +93,7 @@ def test_saved_state_is_q_k_v_o_l(cpu_kernels):
     q, k, val, G = _inputs(B, H, n, d, v)
     for t in (q, k, val):
         t.requires_grad_(True)
-    c = payload(lambda a, b_, c_: AG.attention(a, b_, c_, 0.3, "causal"), q, k, val, grad=G)
+    c = retained_by(lambda: AG.attention(q, k, val, 0.3, "causal").backward(G))
     es = q.element_size()
     assert c.events == 5
     assert c.bytes == es * B * H * n * (2 * d + 2 * v) + 4 * B * H * n
@@ -164,7 +164,7 @@ def test_traced_tiled_forward_retains_quadratic_state():
     for T in (128, 256, 512):
         g = torch.Generator().manual_seed(T)
         q, k, v = (torch.randn((T, d), generator=g, requires_grad=True) for _ in range(3))
-        c = payload(lambda a, b_, c_: traced_tiled_forward(a, b_, c_, d ** -0.5, block), q, k, v)
+        c = retained_by(lambda: traced_tiled_forward(q, k, v, d ** -0.5, block).sum().backward())
         traced.append(c.bytes)
         ours.append(3 * T * d * 4 + T * d * 4 + 4 * T)  # fp32 Q, K, V, O and L
         # The traced forward computes the same function as the definition.

@@ -19,7 +19,7 @@ import torch
 
 import workloads as W
 from oracle import dense, dropout, tiled
-from tests.gpu_common import DEV, compare, stored
+from tests.gpu_common import DEV, allowance_full, compare, one_key_rows, zero_key_rows, stored
 
 pytestmark = pytest.mark.gpu
 
@@ -93,7 +93,8 @@ def test_every_unit(dtype, d, v, layout, mask, p):
             else:
                 Y, m, ell, Lr = dense.forward(Qr, Kh, Vh, c, Ar)
                 rdQ, rdK, rdV = tiled.reverse(Qr, Kh, Vh, c, Ar, nk, stored(Y, dtype), m, ell, Gr)
-            compare("O", Oh[rows], Y, dtype, tag)
+            al = allowance_full(Qr, Kh, Vh, Gr, c, Ar, stored(Y, dtype), Lr, dtype, Z if p8 else None, p8)
+            compare("O", Oh[rows], Y, dtype, tag, extra=al.get("O"))
             compare("L", Lh[rows], Lr, dtype, tag)
             mq, mk, mv, mg = (float(np.abs(x).max()) for x in (Qr, Kh, Vh, Gr))
             kinv = 256 / (256 - p8)
@@ -102,6 +103,8 @@ def test_every_unit(dtype, d, v, layout, mask, p):
             for path, (dq, dk, dv) in res.items():
                 dqh = got(dq[b, h])
                 assert np.all(dqh[empty] == 0), (tag, path)
-                compare("dQ", dqh[rows], rdQ, dtype, (tag, path), bound=bd["dQ"])
-                compare("dK", got(dk[b, h]), rdK, dtype, (tag, path), bound=bd["dK"])
-                compare("dV", got(dv[b, h]), rdV, dtype, (tag, path), bound=bd["dV"])
+                compare("dQ", dqh[rows], rdQ, dtype, (tag, path), bound=bd["dQ"], extra=al.get("dQ"),
+                        zero_rows=one_key_rows(Ar))
+                compare("dK", got(dk[b, h]), rdK, dtype, (tag, path), bound=bd["dK"], extra=al.get("dK"),
+                        zero_rows=zero_key_rows(Ar))
+                compare("dV", got(dv[b, h]), rdV, dtype, (tag, path), bound=bd["dV"], extra=al.get("dV"))

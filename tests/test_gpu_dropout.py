@@ -19,7 +19,7 @@ import torch
 
 import workloads as W
 from oracle import dropout
-from tests.gpu_common import DEV, compare, stored
+from tests.gpu_common import DEV, allowance_full, compare, stored
 
 pytestmark = pytest.mark.gpu
 
@@ -86,12 +86,13 @@ def test_dropout_parity(dtype, d, v, mask):
         Y, Lr = dropout.forward(Qh, Kh, Vh, c, A, Z, p8)
         rdQ, rdK, rdV = dropout.vjp(Qh, Kh, Vh, c, A, Z, p8, Gh, stored(Y, dtype))
         tag = (dtype, d, v, mask, h)
-        compare("O", got(o[0, h]), Y, dtype, tag)
+        al = allowance_full(Qh, Kh, Vh, Gh, c, A, stored(Y, dtype), Lr, dtype, Z, p8)
+        compare("O", got(o[0, h]), Y, dtype, tag, extra=al.get("O"))
         compare("L", got(L[0, h]), Lr, dtype, tag)
         for path, (dq, dk, dv) in grads.items():
-            compare("dQ", got(dq[0, h]), rdQ, dtype, (tag, path))
-            compare("dK", got(dk[0, h]), rdK, dtype, (tag, path))
-            compare("dV", got(dv[0, h]), rdV, dtype, (tag, path))
+            compare("dQ", got(dq[0, h]), rdQ, dtype, (tag, path), extra=al.get("dQ"))
+            compare("dK", got(dk[0, h]), rdK, dtype, (tag, path), extra=al.get("dK"))
+            compare("dV", got(dv[0, h]), rdV, dtype, (tag, path), extra=al.get("dV"))
 
 
 def test_autograd_passes_dropout_through():

@@ -1,0 +1,77 @@
+"""Device memory of a forward + backward step: outputs plus the library's
+workspace, nothing quadratic (needs an MI355X).
+
+The method keeps no n x n score or probability matrix (ob1 page,
+"Verification results": the largest block temporary stays constant as n
+grows and peak memory is linear; maitreyasuin page, "Two things this number
+is and isn't": the allocator's peak is a different instrument from the
+saved-tensor payload, so it is measured here on its own).  Three
+instruments: torch's allocator peak, which must equal the outputs plus
+attn_workspace_size exactly; the device's free memory, which must fall by
+no more than torch's own reservations (the library allocates nothing); and
+the peak at n and 2n, which must be exactly twice as large.
+"""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _rounded(nbytes):  # torch's caching allocator rounds every block to 512 bytes
+    return (nbytes + 511) // 512 * 512
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _step_peak(n, H=32, d=128, dtype=torch.bfloat16, mask="causal", seed=3):
+    import exact_tiled_attention_attn_amd as E
+
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    q, k, val, do = (torch.randn((1, H, n, d), generator=g, device=DEV).to(dtype) for _ in range(4))
+    scale = d ** -0.5
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    free0, res0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_reserved()
+    o, L = E.fwd(q, k, val, scale, mask)
+    dq, dk, dv = E.bwd(q, k, val, o, do, L, scale, mask, deterministic=True)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    free1, res1 = torch.cuda.mem_get_info()[0], torch.cuda.memory_reserved()
+    pf = E.make_problem(q, k, val, o, scale, mask)
+    pb = E.make_problem(q, k, val, o, scale, mask, deterministic=True)
+    ws_f, ws_b = E.workspace_size(pf, False), E.workspace_size(pb, True)
+    # Live at the forward: O, L, its workspace; at the backward: O, L, dQ,
+    # dK, dV and the backward's workspace (each workspace is freed on return).
+    keep = _rounded(_nbytes(o)) + _rounded(_nbytes(L))
+    grads = sum(_rounded(_nbytes(t)) for t in (dq, dk, dv))
+    expected = keep + max(_rounded(ws_f) if ws_f else 0, grads + (_rounded(ws_b) if ws_b else 0))
+    print(f"n={n}: peak {peak} B, expected {expected} B (workspace fwd {ws_f} B, bwd {ws_b} B); "
+          f"free memory fell by {free0 - free1} B, torch reserved {res1 - res0} B more", flush=True)
+    assert peak == expected, (n, peak, expected)
+    assert free0 - free1 <= res1 - res0, (n, free0 - free1, res1 - res0)
+    # The workspace is linear in n: D and L log2(e) rows (fp32), no n x n term.
+    assert ws_b == 2 * 4 * H * ((n + 127) // 128 * 128), ws_b
+    del q, k, val, do, o, L, dq, dk, dv
+    return peak
+
+
+def test_step_memory_is_outputs_plus_workspace_and_linear():
+    import exact_tiled_attention_attn_amd as E
+
+    # Load the code objects (and any per-queue runtime buffers) first.
+    x = torch.randn((1, 2, 256, 128), device=DEV).to(torch.bfloat16)
+    o, L = E.fwd(x, x, x, 0.1, "causal")
+    E.bwd(x, x, x, o, x, L, 0.1, "causal", deterministic=True)
+    _step_peak(16384)  # the headline shape, once to warm every kernel at full size
+    torch.cuda.empty_cache()
+    p1 = _step_peak(8192)
+    p2 = _step_peak(16384)
+    assert p2 == 2 * p1, (p1, p2)

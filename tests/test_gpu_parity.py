@@ -1,9 +1,17 @@
 """HIP path vs the float64 oracle, element by element (needs an MI355X).
 
-Small and ragged problems are compared in full; the large workloads run at
-full size in the benchmark's launch configuration and are compared on
-sampled query rows (O, L, dQ) and key columns (dK, dV) that the oracle
-evaluates one by one.
+Small and ragged problems are compared in full.  The large workloads run at
+full size in the benchmark's launch configuration: O and L are compared on
+every row of every (batch, head) unit against the dense definition, and the
+gradients on sampled query rows (dQ) and key columns (dK, dV) of every unit,
+which the oracle evaluates one by one.
+
+Gradients have two references: the reverse procedure with delta_i taken on
+the forward output as stored (the procedure consumes a forward run's Y), and
+the exact VJP (float64 Y, or the rowsum(P o dP) form of oracle/dense.py).
+Every device result is held to the same bar against both: eps <= 2e-2 of
+the largest magnitude, and elementwise 1e-2 rms(R) + 2e-2 |R| plus the
+rounding allowance of the bf16 path (gpu_common.allowance_full).
 """
 
 from __future__ import annotations
@@ -13,44 +21,51 @@ import pytest
 
 import workloads as W
 from oracle import dense
-from tests.gpu_common import compare, magnitude_bounds, oracle_unit, run_gpu, stored
+from tests.gpu_common import (allowance_full, compare, magnitude_bounds, margins_report, margins_scope,
+                              one_key_rows,
+                              operand_rounding_bound, oracle_unit, output_rounding_bound, run_gpu, stored,
+                              term_bound, zero_key_rows)
 
 pytestmark = pytest.mark.gpu
 
 
-def _full_compare(prob, tag, exact_vjp=False):
+def _full_compare(prob, tag):
+    """Every output of every unit against the forward definition, the
+    stored-Y reverse procedure and the exact dense VJP."""
     got = run_gpu(prob)
     w = prob.w
     errs = {}
-    names = ["O", "L", "dQ", "dK", "dV"]
     for b in range(w.B):
         for h in range(w.H):
-            ref = oracle_unit(prob, b, h, exact_vjp=exact_vjp)
+            ref = oracle_unit(prob, b, h, exact_vjp=True)
             bounds = magnitude_bounds(prob, b, h)
-            pairs = [(x, x) for x in names] + [(x + "_det", x) for x in ("dQ", "dK", "dV")]
-            if exact_vjp:
-                pairs += [(x, x + "_exact") for x in ("dQ", "dK", "dV")]
+            A = None if w.mask == W.MASK_NONE else prob.allowed(h)
+            Q, K, V, G = (getattr(prob, x)[b, h] for x in "QKVG")
+            # Rounding allowances of the bf16 path (both references).
+            allow = allowance_full(Q, K, V, G, w.scale, A, stored(ref["O"], w.dtype), ref["L"], w.dtype)
+            zq, zk = one_key_rows(A), zero_key_rows(A)
+            if w.n <= 2:
+                # One or two keys per row: dQ and dK are differences of two
+                # terms; their rounding allowance (gpu_common.term_bound)
+                # applies to the eps check as well.
+                eq, ek = term_bound(Q, K, V, G, w.scale, A, w.dtype)
+                allow = dict(allow, dQ=eq + allow.get("dQ", 0.0), dK=ek + allow.get("dK", 0.0))
+            pairs = [("O", "O"), ("L", "L")]
+            for g in ("dQ", "dK", "dV"):
+                pairs += [(g, g), (g + "_det", g), (g, g + "_exact"), (g + "_det", g + "_exact")]
             for gname, rname in pairs:
-                if w.dtype == "bf16" and w.n <= 2 and gname[:2] in ("dQ", "dK"):
-                    # With at most two keys, dQ and dK are the difference of two
-                    # terms p_ij (dP_ij - D_i); D_i = <dO_i, O_i> on the
-                    # bf16-stored O carries O's +-1 ulp, which can exceed the
-                    # difference.  Reported, not asserted (fp32 covers n <= 2).
-                    e = np.abs(got[gname][b, h] - ref[rname]).max() / max(np.abs(ref[rname]).max(), 1e-30)
-                    print(tag, gname, f"bf16 two-key relative error {e:.2e} (not asserted)")
-                    assert np.all(np.isfinite(got[gname][b, h]))
-                    continue
-                errs[gname + "/" + rname] = max(
-                    errs.get(gname + "/" + rname, 0.0),
-                    compare(gname[:2], got[gname][b, h], ref[rname], w.dtype, (tag, b, h, gname),
-                            bounds.get(gname[:2]), elementwise=w.n > 2, cond=1.0 if w.n > 2 else 4.0))
+                key = gname + "/" + rname
+                e = compare(gname[:2] if gname != "L" else "L", got[gname][b, h], ref[rname], w.dtype,
+                            (tag, b, h, key), bounds.get(gname[:2]), extra=allow.get(gname[:2]),
+                            extra_eps=w.n <= 2, zero_rows={"dQ": zq, "dK": zk}.get(gname[:2]))
+                errs[key] = max(errs.get(key, 0.0), e)
     print(tag, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     return errs
 
 
 @pytest.mark.parametrize("name", ["f32_n256_d64", "f32_causal_n1000_d80"])
 def test_fp32_workloads_full(name):
-    _full_compare(W.generate(name), name, exact_vjp=True)
+    _full_compare(W.generate(name), name)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -74,53 +89,93 @@ def test_ragged_small(dtype, mask, dims, n):
     _full_compare(prob, prob.w.name)
 
 
-def _sampled_compare(prob, units, n_rows=48, seed=0):
-    """Full-size GPU run; oracle on sampled rows / columns of a few units."""
+def _full_size_compare(prob, n_edge=256, n_rand=48, seed=0):
+    """Full-size run in the benchmark's launch configuration.
+
+    O and L: every row of every unit.  dQ: the first and last ``n_edge``
+    rows plus ``n_rand`` random rows of every unit; dK, dV: the same choice
+    of key columns.  Both gradient references, both dQ paths.  The oracle
+    work of the units runs on a thread pool (one-thread BLAS each).
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    import threadpoolctl
+
     w = prob.w
-    got = run_gpu(prob)
-    rng = np.random.default_rng(seed)
     n = w.n
-    pick = lambda: np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),  # noqa: E731
-                                             rng.choice(n, n_rows, replace=False)]))
-    errs = {}
-    for (b, h) in units:
-        Q, K, V, G = (getattr(prob, x)[b, h] for x in ("Q", "K", "V", "G"))
-        A_rows = (lambda r, h=h: np.ones((len(r), n), bool)) if w.mask == W.MASK_NONE \
-            else (lambda r, h=h: prob.allowed(h, r))
-        Y, _, _, L = dense.forward(Q, K, V, w.scale, None if w.mask == W.MASK_NONE else prob.allowed(h))
-        rows, cols = pick(), pick()
-        # delta from the forward output as stored (see oracle_unit).
-        dQ, dK, dV = dense.grads_sampled(Q, K, V, w.scale, A_rows, G, L, stored(Y, w.dtype), rows, cols)
+    print(f"[{w.name}] device run", flush=True)
+    got = run_gpu(prob)
+    print(f"[{w.name}] oracle on {w.B * w.H} units", flush=True)
+    causal = prob.allowed(0) if w.mask == W.MASK_CAUSAL else None
+    rng = np.random.default_rng(seed)
+    picks = {}
+    for b in range(w.B):
+        for h in range(w.H):
+            picks[(b, h)] = [np.unique(np.concatenate([np.arange(min(n_edge, n)), np.arange(max(0, n - n_edge), n),
+                                                       rng.choice(n, n_rand, replace=False)])) for _ in range(2)]
+
+    def unit(bh):
+        b, h = bh
+        errs = {}
+
+        def check(name, g, r, tag, extra=None, zero_rows=None):
+            errs[name] = max(errs.get(name, 0.0), compare(name[:2] if name != "L" else "L", g, r, w.dtype, tag,
+                                                          extra=extra, zero_rows=zero_rows))
+
+        Q, K, V, G = (getattr(prob, x)[b, h] for x in "QKVG")
+        Ah = None if w.mask == W.MASK_NONE else (causal if causal is not None else prob.allowed(h))
+        Y, _, _, L = dense.forward(Q, K, V, w.scale, Ah)
         tag = (w.name, b, h)
-        checks = [("O", got["O"][b, h][rows], Y[rows]), ("L", got["L"][b, h][rows], L[rows])]
+        if Ah is None:
+            def A_rows(r):
+                return np.ones((len(r), n), bool)
+        else:
+            def A_rows(r):
+                return Ah if len(r) == n else Ah[r]
+        E_O = output_rounding_bound(Q, K, V, L, w.scale, A_rows, w.dtype)
+        check("O", got["O"][b, h], Y, tag, E_O)
+        check("L", got["L"][b, h], L, tag)
+        rows, cols = picks[bh]
+        Ys = stored(Y, w.dtype)
+        allow = operand_rounding_bound(Q, K, V, G, Ys, L, E_O, w.scale, A_rows, rows, cols, w.dtype)
+        zq = None if Ah is None else one_key_rows(A_rows(rows))
+        for ref_name, Yd in (("stored", Ys), ("exact", Y)):
+            dQ, dK, dV = dense.grads_sampled(Q, K, V, w.scale, A_rows, G, L, Yd, rows, cols)
+            for sfx in ("", "_det"):
+                check("dQ" + sfx + "/" + ref_name, got["dQ" + sfx][b, h][rows], dQ, tag, allow.get("dQ"), zq)
+                check("dK" + sfx + "/" + ref_name, got["dK" + sfx][b, h][cols], dK, tag, allow.get("dK"))
+                check("dV" + sfx + "/" + ref_name, got["dV" + sfx][b, h][cols], dV, tag, allow.get("dV"))
+        # Whole-tensor invariants at any size: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i.
         for sfx in ("", "_det"):
-            checks += [("dQ" + sfx, got["dQ" + sfx][b, h][rows], dQ),
-                       ("dK" + sfx, got["dK" + sfx][b, h][cols], dK),
-                       ("dV" + sfx, got["dV" + sfx][b, h][cols], dV)]
-        for name, g, r in checks:
-            errs[name] = max(errs.get(name, 0.0), compare(name[:2] if name != "L" else name, g, r, w.dtype, (tag, name)))
-        # Whole-tensor invariants at any size: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
-        sdk = got["dK"][b, h].sum(0)
-        assert np.abs(sdk).max() <= 2e-2 * np.abs(got["dK"][b, h]).sum(0).max() + 1e-6, tag
-        sdv, sg = got["dV"][b, h].sum(0), G.astype(np.float64).sum(0)
-        assert np.abs(sdv - sg).max() <= 2e-2 * np.abs(G).sum(0).max(), tag
-    print(w.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    return errs
+            sdk = got["dK" + sfx][b, h].sum(0)
+            assert np.abs(sdk).max() <= 2e-2 * np.abs(got["dK" + sfx][b, h]).sum(0).max() + 1e-6, tag
+            sdv, sg = got["dV" + sfx][b, h].sum(0), G.astype(np.float64).sum(0)
+            assert np.abs(sdv - sg).max() <= 2e-2 * np.abs(G).sum(0).max(), tag
+        return errs
+
+    import os
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    total = {}
+    with margins_scope(), threadpoolctl.threadpool_limits(1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        for errs in ex.map(unit, list(picks)):
+            for k_, v_ in errs.items():
+                total[k_] = max(total.get(k_, 0.0), v_)
+        print(w.name, {k: f"{v:.2e}" for k, v in total.items()}, flush=True)
+        print(margins_report(w.name), flush=True)
+    return total
 
 
 def test_bf16_noncausal_b4h16_n4096_full_size():
-    prob = W.generate("bf16_b4h16_n4096_d128")
-    _sampled_compare(prob, [(0, 0), (1, 7), (3, 15)])
+    _full_size_compare(W.generate("bf16_b4h16_n4096_d128"))
 
 
 def test_bf16_causal_h32_n16384_full_size():
-    prob = W.generate("bf16_causal_h32_n16384_d128")
-    _sampled_compare(prob, [(0, 0), (0, 15), (0, 31)])
+    _full_size_compare(W.generate("bf16_causal_h32_n16384_d128"))
 
 
 def test_bf16_bitmask_b2h8_n8192_full_size():
-    prob = W.generate("bf16_bitmask_b2h8_n8192_d64v128")
-    _sampled_compare(prob, [(0, 0), (1, 3), (1, 7)])
+    _full_size_compare(W.generate("bf16_bitmask_b2h8_n8192_d64v128"))
 
 
 @pytest.mark.parametrize("name", ["bf16_b4h16_n4096_d128", "bf16_causal_h32_n16384_d128",
@@ -128,7 +183,7 @@ def test_bf16_bitmask_b2h8_n8192_full_size():
 def test_bf16_workloads_reduced_full_compare(name):
     """Same recipe with fewer heads and n = 1000 (ragged tail): compare everything."""
     prob = W.generate(name, heads=2, n=1000)
-    _full_compare(prob, name + "_reduced", exact_vjp=True)
+    _full_compare(prob, name + "_reduced")
 
 
 @pytest.mark.parametrize("name", ["bf16_causal_h32_n16384_d128", "bf16_bitmask_b2h8_n8192_d64v128",

@@ -25,7 +25,8 @@ import torch
 
 import workloads as W
 from oracle import dense, tiled, tilemap
-from tests.gpu_common import DEV, compare, stored
+from tests.gpu_common import (DEV, allowance_full, compare, one_key_rows, output_rounding_bound, stored,
+                              zero_key_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,17 +68,21 @@ def _allowed(mask, n, nk, off, H, rng):
 
 
 def _oracle(Q, K, V, G, c, A, dtype):
-    """O, L, dQ over every row (zero / -inf where a row allows no key), dK, dV."""
+    """O, L, dQ over every row (zero / -inf where a row allows no key), dK, dV,
+    the rows with an allowed key, and the bf16 operand rounding allowances
+    (O, dQ of those rows; dK, dV of every key)."""
     n, v = Q.shape[0], V.shape[1]
     rows = np.nonzero(A.any(axis=1))[0]
     O, L, dQ = np.zeros((n, v)), np.full(n, -np.inf), np.zeros_like(Q, dtype=np.float64)
     dK, dV = np.zeros_like(K, dtype=np.float64), np.zeros_like(V, dtype=np.float64)
+    al = {}
     if rows.size:
         Y, m, ell, Lr = dense.forward(Q[rows], K, V, c, A[rows])
         O[rows], L[rows] = Y, Lr
         dq, dK, dV = tiled.reverse(Q[rows], K, V, c, A[rows], K.shape[0], stored(Y, dtype), m, ell, G[rows])
         dQ[rows] = dq
-    return O, L, dQ, dK, dV, rows
+        al = allowance_full(Q[rows], K, V, G[rows], c, A[rows], stored(Y, dtype), Lr, dtype)
+    return O, L, dQ, dK, dV, rows, al
 
 
 def _bounds(Q, K, V, G, c, nq, nk):
@@ -102,7 +107,7 @@ def test_rectangular_parity(dtype, d, v, n, nk, mask, off):
     got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     for h in range(H):
         Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
-        rO, rL, rdQ, rdK, rdV, rows = _oracle(Qh, Kh, Vh, Gh, c, As[h], dtype)
+        rO, rL, rdQ, rdK, rdV, rows, al = _oracle(Qh, Kh, Vh, Gh, c, As[h], dtype)
         tag = (dtype, d, v, n, nk, mask, off, h)
         empty = np.setdiff1d(np.arange(n), rows)
         Oh, Lh = got(o[0, h]), got(L[0, h])
@@ -110,14 +115,16 @@ def test_rectangular_parity(dtype, d, v, n, nk, mask, off):
         if rows.size == 0:
             continue
         bd = _bounds(Qh, Kh, Vh, Gh, c, rows.size, nk)
-        compare("O", Oh[rows], rO[rows], dtype, tag, bound=bd["O"])
+        compare("O", Oh[rows], rO[rows], dtype, tag, bound=bd["O"], extra=al.get("O"))
         compare("L", Lh, rL, dtype, tag)
         for path, (dq, dk, dv) in res.items():
             dqh = got(dq[0, h])
             assert np.all(dqh[empty] == 0), (tag, path)
-            compare("dQ", dqh[rows], rdQ[rows], dtype, (tag, path), bound=bd["dQ"])
-            compare("dK", got(dk[0, h]), rdK, dtype, (tag, path), bound=bd["dK"])
-            compare("dV", got(dv[0, h]), rdV, dtype, (tag, path), bound=bd["dV"])
+            compare("dQ", dqh[rows], rdQ[rows], dtype, (tag, path), bound=bd["dQ"], extra=al.get("dQ"),
+                    zero_rows=one_key_rows(As[h][rows]))
+            compare("dK", got(dk[0, h]), rdK, dtype, (tag, path), bound=bd["dK"], extra=al.get("dK"),
+                    zero_rows=zero_key_rows(As[h][rows]))
+            compare("dV", got(dv[0, h]), rdV, dtype, (tag, path), bound=bd["dV"], extra=al.get("dV"))
 
 
 @pytest.mark.parametrize("is_bwd", [0, 1, 2])
@@ -161,13 +168,14 @@ def test_key_ranges_merge_into_the_full_result(dtype, d, splits):
     got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     for h in range(H):
         Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
-        rO, rL, rdQ, rdK, rdV, _ = _oracle(Qh, Kh, Vh, Gh, c, A, dtype)
+        rO, rL, rdQ, rdK, rdV, _, al = _oracle(Qh, Kh, Vh, Gh, c, A, dtype)
         tag = (dtype, splits, h)
-        compare("O", got(Om[0, h]), rO, dtype, tag)
+        # The merged output carries the rounding of each range's output too.
+        compare("O", got(Om[0, h]), rO, dtype, tag, extra=None if "O" not in al else 2 * al["O"])
         compare("L", got(Lm[0, h]), rL, dtype, tag)
-        compare("dQ", got(dQ[0, h]), rdQ, dtype, tag)
-        compare("dK", got(dK[0, h]), rdK, dtype, tag)
-        compare("dV", got(dV[0, h]), rdV, dtype, tag)
+        compare("dQ", got(dQ[0, h]), rdQ, dtype, tag, extra=al.get("dQ"))
+        compare("dK", got(dK[0, h]), rdK, dtype, tag, extra=al.get("dK"))
+        compare("dV", got(dV[0, h]), rdV, dtype, tag, extra=al.get("dV"))
         # The same rows from the single square call: agreement at rounding level.
         assert np.abs(got(Om[0, h]) - got(o[0, h])).max() <= (1e-5 if dtype == "f32" else 1e-2) * np.abs(rO).max()
         assert np.abs(got(Lm[0, h]) - got(L[0, h])).max() <= 1e-4
@@ -205,7 +213,9 @@ def test_split_key_forward(d, v, n, nk, mask, off):
         empty = np.setdiff1d(np.arange(n), rows)
         Oh, Lh = got(o[0, h]), got(L[0, h])
         assert np.all(Oh[empty] == 0) and np.all(Lh[empty] == -np.inf), tag
-        compare("O", Oh[rows], rO[rows], dtype, tag)
+        Arows = As[h][rows]
+        orb = output_rounding_bound(Qh[rows], Kh, Vh, rL[rows], c, lambda r: Arows[r], dtype)
+        compare("O", Oh[rows], rO[rows], dtype, tag, extra=orb)
         compare("L", Lh, rL, dtype, tag)
 
 
@@ -235,7 +245,7 @@ def test_split_key_backward(d, v, n, nk, mask, off):
     got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     for h in range(H):
         Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
-        rO, rL, rdQ, rdK, rdV, rows = _oracle(Qh, Kh, Vh, Gh, c, As[h], dtype)
+        rO, rL, rdQ, rdK, rdV, rows, al = _oracle(Qh, Kh, Vh, Gh, c, As[h], dtype)
         if rows.size == 0:
             continue
         bd = _bounds(Qh, Kh, Vh, Gh, c, rows.size, nk)
@@ -244,9 +254,11 @@ def test_split_key_backward(d, v, n, nk, mask, off):
             tag = (d, v, n, nk, mask, off, h, path)
             dqh = got(dq[0, h])
             assert np.all(dqh[empty] == 0), tag
-            compare("dQ", dqh[rows], rdQ[rows], dtype, tag, bound=bd["dQ"])
-            compare("dK", got(dk[0, h]), rdK, dtype, tag, bound=bd["dK"])
-            compare("dV", got(dv[0, h]), rdV, dtype, tag, bound=bd["dV"])
+            compare("dQ", dqh[rows], rdQ[rows], dtype, tag, bound=bd["dQ"], extra=al.get("dQ"),
+                    zero_rows=one_key_rows(As[h][rows]))
+            compare("dK", got(dk[0, h]), rdK, dtype, tag, bound=bd["dK"], extra=al.get("dK"),
+                    zero_rows=zero_key_rows(As[h][rows]))
+            compare("dV", got(dv[0, h]), rdV, dtype, tag, bound=bd["dV"], extra=al.get("dV"))
 
 
 def _oracle_fwd_only(Q, K, V, c, A):

@@ -142,14 +142,15 @@ def test_empty_rows_are_defined(dtype):
             # Reference: the same problem without the empty rows (they contribute nothing).
             Q, K, V, G = (getattr(prob, x)[0, h].astype(np.float64) for x in "QKVG")
             A = prob.mask_bool[h][keep]
-            Y, m, ell, _ = dense.forward(Q[keep], K, V, prob.w.scale, A)
-            from tests.gpu_common import stored
+            Y, m, ell, Lr = dense.forward(Q[keep], K, V, prob.w.scale, A)
+            from tests.gpu_common import allowance_full, stored
             from oracle import tiled
             rdq, rdk, rdv = tiled.reverse(Q[keep], K, V, prob.w.scale, A, 500, stored(Y, dtype), m, ell, G[keep])
-            compare("O", o[0, h][keep].double().numpy(), Y, dtype, ("empty", h))
-            compare("dQ", dq[0, h][keep].double().numpy(), rdq, dtype, ("empty", h, det))
-            compare("dK", dk[0, h].double().numpy(), rdk, dtype, ("empty", h, det))
-            compare("dV", dv[0, h].double().numpy(), rdv, dtype, ("empty", h, det))
+            al = allowance_full(Q[keep], K, V, G[keep], prob.w.scale, A, stored(Y, dtype), Lr, dtype)
+            compare("O", o[0, h][keep].double().numpy(), Y, dtype, ("empty", h), extra=al.get("O"))
+            compare("dQ", dq[0, h][keep].double().numpy(), rdq, dtype, ("empty", h, det), extra=al.get("dQ"))
+            compare("dK", dk[0, h].double().numpy(), rdk, dtype, ("empty", h, det), extra=al.get("dK"))
+            compare("dV", dv[0, h].double().numpy(), rdv, dtype, ("empty", h, det), extra=al.get("dV"))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -194,9 +195,11 @@ def test_negative_and_zero_scale(scale, mask):
                 if scale == 0.0 and name in ("dQ", "dK"):
                     assert np.all(got[name][0, h] == 0) and np.all(got[name + "_det"][0, h] == 0)
                     continue
-                compare(name, got[name][0, h], ref[name], dtype, (scale, mask, dtype, name))
+                ex = ref["allow"].get(name)
+                compare(name, got[name][0, h], ref[name], dtype, (scale, mask, dtype, name), extra=ex)
                 if name in ("dQ", "dK", "dV"):
-                    compare(name, got[name + "_det"][0, h], ref[name], dtype, (scale, mask, dtype, name, "det"))
+                    compare(name, got[name + "_det"][0, h], ref[name], dtype, (scale, mask, dtype, name, "det"),
+                            extra=ex)
 
 
 def test_self_attention_aliased_inputs():
@@ -254,3 +257,64 @@ def test_mask_pad_bits_and_padded_rows_are_ignored(dtype, d, v):
     names = ["O", "L", "dQ", "dK", "dV", "map_fwd", "map_bwd", "map_dq"]
     for name, a, b in zip(names, *res):
         assert torch.equal(a, b), name
+
+
+def _count_case(dtype, d, v, n, nk, mask, off, seed):
+    rng = np.random.default_rng(seed)
+    H = 2
+    Q, K, V, G = (rng.standard_normal((1, H, r, c), dtype=np.float32) for r, c in ((n, d), (nk, d), (nk, v), (n, v)))
+    if mask == "bitmask":
+        A = rng.random((H, n, nk)) < 0.02
+        A[:, :, : nk // 3] = False  # whole empty key tiles
+        A[:, : n // 4] = False      # whole empty query tiles
+        A[0, : n // 4, -40:] = True  # and a few nonempty among them
+        allowed = [A[h] for h in range(H)]
+    elif mask == "causal":
+        allowed = [W.causal_allowed(n, nk=nk, offset=off)] * H
+    else:
+        allowed = [np.ones((n, nk), bool)] * H
+    return (Q, K, V, G), allowed, H
+
+
+@pytest.mark.parametrize("dtype,d,v", [("bf16", 128, 128), ("bf16", 64, 128), ("bf16", 80, 80), ("f32", 64, 64)])
+@pytest.mark.parametrize("mask,n,nk,off", [("none", 700, 700, 0), ("causal", 1000, 1000, 0),
+                                          ("causal", 300, 1500, 1200), ("causal", 900, 600, -250),
+                                          ("causal", 128, 4096, 3968), ("bitmask", 800, 900, 0),
+                                          ("bitmask", 128, 4096, 0)])
+def test_executed_tiles_equal_nonempty_tiles(dtype, d, v, mask, n, nk, off):
+    """Every kernel computes exactly the tiles the oracle's classification
+    calls nonempty, at its own tiling (key-range splits included), and skips
+    the rest: the debug counters against oracle/tilemap.py."""
+    import exact_tiled_attention_attn_amd as E
+
+    (Q, K, V, G), allowed, H = _count_case(dtype, d, v, n, nk, mask, off, seed=n + nk + d)
+
+    def dev(x):
+        if dtype == "bf16":
+            return torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+        return torch.from_numpy(x).to(DEV)
+
+    q, k, val, g = (dev(x) for x in (Q, K, V, G))
+    mdev = None
+    if mask == "bitmask":
+        mdev = torch.from_numpy(W.pack_bits(np.stack(allowed)).view(np.int32)).to(DEV)
+    want = []
+    for is_bwd in (0, 1, 2):
+        _, bq, bk = E.debug_tile_map(q, k, val, 0.125, mask, mdev, is_bwd=is_bwd, causal_offset=off)
+        want.append(sum(tilemap.nonempty_tiles(tilemap.tile_map(allowed[h], bq, bk)) for h in range(H)))
+    counters = torch.zeros(3, dtype=torch.int64, device=DEV)
+    E.count_tiles(counters)
+    try:
+        o, L = E.fwd(q, k, val, 0.125, mask, mdev, causal_offset=off)
+        E.bwd(q, k, val, o, g, L, 0.125, mask, mdev, deterministic=True, causal_offset=off)
+        torch.cuda.synchronize()
+        got_det = counters.cpu().tolist()
+        counters.zero_()
+        E.bwd(q, k, val, o, g, L, 0.125, mask, mdev, deterministic=False, causal_offset=off)
+        torch.cuda.synchronize()
+        got_atomic = counters.cpu().tolist()
+    finally:
+        E.count_tiles(None)
+    print(dtype, d, v, mask, n, nk, off, "nonempty", want, "executed", got_det, got_atomic, flush=True)
+    assert got_det == want, (got_det, want)
+    assert got_atomic == [0, want[1], 0], (got_atomic, want)
