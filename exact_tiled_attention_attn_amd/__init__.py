@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     AttnProblem,
     bwd,
+    bwd_noalloc,
     count_tiles,
     debug_tile_map,
     dropout_mask,

@@ -23,7 +23,8 @@ STATUS = {
     4: "ATTN_ERR_DTYPE", 5: "ATTN_ERR_MASK", 6: "ATTN_ERR_UNSUPPORTED",
     7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP",
 }
-EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask",
+EXPORTS = ["attn_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_debug_tile_map",
+           "attn_debug_dropout_mask",
            "attn_debug_count_tiles", "attn_timing_enable", "attn_timing_read", "attn_timing_reset",
            "attn_status_str", "attn_last_error", "attn_version"]
 KERNELS = ["tile_map", "fwd", "bwd_pre", "bwd", "bwd_post", "bwd_dq", "fwd_merge", "bwd_dq_merge"]
@@ -68,13 +69,14 @@ def load_library(path: str = LIB_PATH):
     lib.attn_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
     lib.attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.attn_debug_tile_map.argtypes = [P, ctypes.c_int, vp, sz, i32p, i32p, i32p, i32p, vp, sz, vp]
     lib.attn_debug_dropout_mask.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_int32, vp, sz, vp]
     lib.attn_debug_count_tiles.argtypes = [vp]
-    for f in ("attn_workspace_size", "attn_fwd", "attn_bwd", "attn_debug_tile_map", "attn_debug_dropout_mask",
-              "attn_debug_count_tiles"):
+    for f in ("attn_workspace_size", "attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_debug_tile_map",
+              "attn_debug_dropout_mask", "attn_debug_count_tiles"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -267,6 +269,34 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
     with torch.cuda.device(q.device):
         _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ctypes.c_size_t(_nbytes(ws)), _stream()))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=None, dv=None,
+                deterministic=False, causal_offset=0, dropout_p=0.0, dropout_seed=0):
+    """attn_bwd_noalloc: bwd() with the library's static scratch as the
+    workspace.  The library allocates nothing; dQ, dK, dV are the caller's
+    (allocated here only when not given)."""
+    lib = load_library()
+    _on_gpu("q", q)
+    _on_gpu("O", o, q.device, q.dtype)
+    _on_gpu("dO", do, q.device, q.dtype, o.shape)
+    if do.stride() != o.stride():
+        raise ValueError("dO must have the strides of O")
+    dq = dq if dq is not None else _like(q)
+    dk = dk if dk is not None else _like(k)
+    dv = dv if dv is not None else _like(v)
+    for name, t, ref in (("dQ", dq, q), ("dK", dk, k), ("dV", dv, v)):
+        _on_gpu(name, t, q.device, q.dtype, ref.shape)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("dQ, dK, dV must have the strides of Q, K, V")
+    _on_gpu("lse", lse, q.device, torch.float32, q.shape[:3])
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, n]")
+    p = make_problem(q, k, v, o, scale, mask_mode, mask, deterministic, causal_offset, dropout_p, dropout_seed)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _stream()))
     return dq, dk, dv
 
 

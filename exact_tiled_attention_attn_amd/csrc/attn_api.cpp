@@ -504,6 +504,25 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
                [&] { return eta::launch_bwd_post(b, bf, (int)p->d, stream); });
 }
 
+attn_status attn_bwd_noalloc(const attn_problem* p, const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* L, void* dQ, void* dK, void* dV, void* stream) {
+  attn_status st = validate_bwd(p);
+  if (st != ATTN_OK) return st;
+  if ((st = check_ptr("Q", Q)) || (st = check_ptr("K", K)) || (st = check_ptr("V", V)) ||
+      (st = check_ptr("O", O)) || (st = check_ptr("dO", dO)) || (st = check_ptr("L", L)) ||
+      (st = check_ptr("dQ", dQ)) || (st = check_ptr("dK", dK)) || (st = check_ptr("dV", dV)))
+    return st;
+  const size_t need = plan(*p, 1).total, cap = eta::scratch_capacity();
+  if (need > cap)
+    return fail(ATTN_ERR_WORKSPACE,
+                "attn_bwd_noalloc: this problem needs %zu bytes of scratch, more than the %zu-byte static "
+                "buffer; call attn_bwd with a workspace of attn_workspace_size bytes",
+                need, cap);
+  void* ws = nullptr;
+  if ((st = hip_status(eta::scratch_address(&ws), "static scratch address")) != ATTN_OK) return st;
+  return attn_bwd(p, Q, K, V, O, dO, L, dQ, dK, dV, ws, cap, stream);
+}
+
 attn_status attn_debug_tile_map(const attn_problem* p, int is_bwd, uint8_t* map_dev, size_t map_bytes,
                                 int32_t* bq, int32_t* bk, int32_t* tq, int32_t* tk, void* ws,
                                 size_t ws_bytes, void* stream) {
@@ -590,6 +609,6 @@ attn_status attn_timing_reset(void) {
   return ATTN_OK;
 }
 
-int32_t attn_version(void) { return 500; }
+int32_t attn_version(void) { return 600; }
 
 }  // extern "C"

@@ -178,6 +178,12 @@ int timing_enable(int on);
 int timing_read(double* ms, int64_t* launches);
 void timing_reset();
 
+// Static scratch of attn_bwd_noalloc (attn_scratch.hip): its size, and the
+// device address of the current GPU's copy (resolved once per device with
+// hipGetSymbolAddress; returns a hipError_t value, 0 = success).
+size_t scratch_capacity();
+int scratch_address(void** out);
+
 // True when the (d, v) pair has compiled kernels.
 inline bool supported_dims(int64_t d, int64_t v) {
   return (d == 64 && v == 64) || (d == 80 && v == 80) || (d == 128 && v == 128) ||

@@ -172,6 +172,23 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
                      void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Backward that allocates nothing: for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same operation, arguments, results and errors as
+ * attn_bwd, without the workspace arguments: the workspace is a static
+ * 64 MiB device array of the library, of which each GPU holds its own copy
+ * from the first call on that GPU until the process ends.  Problems whose
+ * attn_workspace_size (is_bwd = 1) exceeds 64 MiB are refused with
+ * ATTN_ERR_WORKSPACE before anything runs (the atomic path's fp32 dQ
+ * accumulator, 4 B H n d bytes, reaches that size first).  Every region the
+ * kernels read is written earlier in the same call, so a call never sees an
+ * earlier call's contents; but all calls on one GPU share the array, so
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and must be serialised by the caller. */
+attn_status attn_bwd_noalloc(const attn_problem* p, const void* Q, const void* K, const void* V,
+                             const void* O, const void* dO, const float* L,
+                             void* dQ, void* dK, void* dV, void* stream);
+
 /* Debug: the (query tile x key tile) classification the forward (is_bwd=0),
  * key-tile-outer backward (is_bwd=1) or query-tile-outer dQ (is_bwd=2)
  * kernels use, 0 = empty (skipped), 1 = partial
@@ -242,7 +259,7 @@ const char* attn_status_str(int status);
 const char* attn_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch (0.5.0 added
- * attn_debug_count_tiles). */
+ * attn_debug_count_tiles, 0.6.0 attn_bwd_noalloc). */
 int32_t attn_version(void);
 
 #ifdef __cplusplus

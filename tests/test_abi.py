@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(E.EXPORTS)
     for name in names:
         assert getattr(lib, name) is not None
-    assert lib.attn_version() == 500
+    assert lib.attn_version() == 600
 
 
 def problem(B=1, H=2, n=100, d=64, v=64, dtype=1, mask_mode=0, contiguous=True):
@@ -230,6 +230,21 @@ def test_workspace_checks():
     assert call_bwd(p, ws=FAKE + (20 << 30), ws_bytes=need - 1) == 7
     assert call_bwd(p, ws=FAKE + (20 << 30) + 16, ws_bytes=need) == 7  # not 256-byte aligned
     assert call_bwd(p, ws=FAKE, ws_bytes=need) == 8  # workspace overlaps Q
+
+
+def test_noalloc_backward_validation():
+    """attn_bwd_noalloc validates like attn_bwd and refuses problems whose
+    workspace exceeds its static 64 MiB buffer, before any device call."""
+    lib = E.load_library()
+    vp = ctypes.c_void_p
+    ptrs = [vp(FAKE + (i << 30)) for i in range(9)]
+    p = problem(B=2, H=32, n=4096, d=128, v=128)  # atomic path: 4 B H n d = 128 MiB of accumulator
+    assert lib.attn_bwd_noalloc(ctypes.byref(p), *ptrs, None) == 7
+    assert "static" in err() and "attn_workspace_size" in err()
+    p = problem()
+    assert lib.attn_bwd_noalloc(ctypes.byref(p), *([vp(0)] + ptrs[1:]), None) == 1 and "Q" in err()
+    p.d = 96
+    assert lib.attn_bwd_noalloc(ctypes.byref(p), *ptrs, None) == 6
 
 
 def test_tile_counter_setting():
