@@ -444,7 +444,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       const int ks = j / S::NDB, blk = j % S::NDB;
       const bf16x8 a = join_tr(tlo[j % PB], thi[j % PB]);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) mfma_aacc(dq[u][blk], a, __builtin_bit_cast(bf16x8, sk[u][ks]));
+      for (int u = 0; u < 2; ++u)  // (64, 64): the allocator moves accumulators through VGPRs
+        mfma_aacc_g<D == 64 && DV == 64>(dq[u][blk], a, __builtin_bit_cast(bf16x8, sk[u][ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
       if (j == 2) hook();
       if constexpr (decltype(dofill)::value) {  // chunk 1: the next step's first row operands

@@ -458,8 +458,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       int blk, ks;
       bmfma(j, is_v, blk, ks);
       const bf16x8 a = join_tr(tlo[j % PB], thi[j % PB]);
-      if (is_v) mfma_aacc(dv[blk], a, __builtin_bit_cast(bf16x8, pk[ks]));
-      else mfma_aacc(dk[blk], a, __builtin_bit_cast(bf16x8, sk[ks]));
+      // (64, 64): the allocator moves accumulators through VGPRs (the
+      // wait-state test of the compiled kernels checks every instance).
+      constexpr bool kGuard = D == 64 && DV == 64;
+      if (is_v) mfma_aacc_g<kGuard>(dv[blk], a, __builtin_bit_cast(bf16x8, pk[ks]));
+      else mfma_aacc_g<kGuard>(dk[blk], a, __builtin_bit_cast(bf16x8, sk[ks]));
       if (j + PB < S::NB) bread(j + PB, tlo[j % PB], thi[j % PB]);
       if constexpr (decltype(dofill)::value) {  // chunk 1: the next step's first row operands
         if (j >= S::NB - PF) afr[j - (S::NB - PF)] = arow(nst, 1, j - (S::NB - PF));

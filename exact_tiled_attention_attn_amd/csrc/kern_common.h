@@ -280,6 +280,14 @@ __device__ __forceinline__ void mfma_vacc(f32x16& d, const bf16x8& a, const bf16
 __device__ __forceinline__ void mfma_aacc(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
+// mfma_aacc behind 5 wait states (kGuard): for template instances whose
+// register allocation carries an accumulator through VGPRs and writes it
+// back to its AGPRs just before the product.
+template <bool kGuard>
+__device__ __forceinline__ void mfma_aacc_g(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  if constexpr (kGuard) asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  else mfma_aacc(d, a, b);
+}
 __device__ __forceinline__ void nops_after_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
 // After nops_after_mfma: tie the MFMA results to it, so that no read of them
 // is scheduled above the nops (the nops have no data dependence of their

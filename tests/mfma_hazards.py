@@ -6,16 +6,18 @@ This module compiles a kernel source to gfx950 assembly and walks every
 function in program order, counting wait states (one per instruction,
 N + 1 for ``s_nop N``), and reports:
 
-* RAW into an MFMA: a vector ALU write of a VGPR the MFMA reads, fewer than
-  ``SRC_AB`` (A / B operands) or ``SRC_C`` (separate accumulator input) wait
-  states before it;
+* RAW into an MFMA: a vector ALU write (``v_accvgpr_write`` included) of a
+  VGPR or AGPR the MFMA reads, fewer than
+  ``SRC_AB`` (A / B operands) or ``SRC_C`` (accumulator input, separate or
+  the result registers themselves) wait states before it;
 * RAW out of an MFMA: a non-MFMA instruction reading an MFMA result (VGPR or,
   through ``v_accvgpr_read``, AGPR) fewer than ``RESULT`` wait states after
   it; an MFMA that accumulates into the same registers is not a reader;
 * WAR on a separate accumulator input: a write to those VGPRs fewer than
   ``SRC_C_WAR`` wait states after the MFMA.
 
-The walk is linear, so a branch can only make it report more, never less.
+The walk is linear: a forward branch can only make it report more, never
+less; a loop's back edge is not followed.
 """
 
 from __future__ import annotations
@@ -130,9 +132,9 @@ def check(ins):
             if not pop.startswith("v_") or pop.startswith("v_mfma"):
                 continue
             w, _ = _writes_reads(pop, pargs)
-            if gap < SRC_AB and w & {r for r in srcab if r[0] == "v"}:
+            if gap < SRC_AB and w & srcab:
                 problems.append(f"{ins[j]} -> {t}: A/B operand {gap} wait states after a vector write")
-            if separate_c and gap < SRC_C and w & {r for r in srcc if r[0] == "v"}:
+            if gap < SRC_C and w & srcc:
                 problems.append(f"{ins[j]} -> {t}: accumulator input {gap} wait states after a vector write")
         # After the MFMA: reads of its result, writes of a separate accumulator input.
         for j in range(i + 1, len(ins)):

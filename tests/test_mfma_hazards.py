@@ -25,6 +25,19 @@ def test_checker_catches_planted_hazards():
         "v_mfma_f32_32x32x16_bf16 v[32:47], v[4:7], a[8:11], v[0:15]",
     ]
     assert any("accumulator input" in p for p in check(raw_in))
+    in_place = [
+        "v_mov_b64_e32 v[14:15], 0",
+        "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",
+    ]
+    assert any("accumulator input" in p for p in check(in_place))
+    agpr_back = [
+        "v_accvgpr_write_b32 a15, v3",
+        "s_waitcnt lgkmcnt(4)",
+        "v_mfma_f32_32x32x16_bf16 a[0:15], v[16:19], v[20:23], a[0:15]",
+    ]
+    assert any("accumulator input" in p for p in check(agpr_back))
+    guarded = ["v_accvgpr_write_b32 a15, v3", "s_nop 4", "v_mfma_f32_32x32x16_bf16 a[0:15], v[16:19], v[20:23], a[0:15]"]
+    assert check(guarded) == []
     early_read = [
         "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]",
         "s_nop 7",
