@@ -56,6 +56,10 @@ struct FwdShape {
 // the same O and L (softmax is shift-invariant); this bound keeps the
 // unnormalised weights <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
+// Bound on a lane's sum of 32 weights below which none of them exceeds
+// 2^(kRescaleSlack - 1) (the pipelined forward's test for keeping its
+// reference max without computing the row max).
+constexpr float kSpecBound = 128.0f;
 
 // DROP: dropout on the weights (kern_common.h keep decisions): the PV
 // product takes the kept weights only, the normaliser and L stay those of
@@ -593,7 +597,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     kt_end = t0 + per < kt_end ? t0 + per : kt_end;
   }
   if (MASK == kMaskBitmask && t0 < kt_end && tile_class(t0) == kTileEmpty) t0 = next_tile(t0);
-  int ntiles = 0;
   __syncthreads();  // V buffers cleared
   if (t0 < kt_end) {  // workgroup-uniform
     int t1 = next_tile(t0);
@@ -609,11 +612,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     apply_rescale();
     __syncthreads();  // K buffer 0 free for tile t2
 
-    // One pipeline step.  On entry cur holds the masked S^T of tile t0 and
-    // the running state is already referenced to t0's max; nxt receives S^T
-    // of tile t1 from knxt.  One scheduling region:
+    // One pipeline step.  On entry cur holds the masked S^T of tile t0; nxt
+    // receives S^T of tile t1 from knxt.  One scheduling region:
     //   MFMA S^T(t1)             || VALU exp / pack / sums of t0
-    //   MFMA O^T += V^T P^T(t0)  || VALU row max of t1
+    //   MFMA O^T += V^T P^T(t0)
+    // The weights of t0 are formed against the running reference max before
+    // that max is brought up to date (no row max on the common path): a
+    // lane whose 32 weights sum to at most 2^(slack - 1) has every score
+    // below the reference plus slack - 1, where the lazy-rescale rule keeps
+    // the reference.  Otherwise (or for a row that had no allowed key yet)
+    // the wave takes the rule's exact path: row max of t0, rescale, and the
+    // weights again.  The reference max therefore follows the same rule as
+    // with the max computed first.
     auto step = [&](f32x16 (&cur)[S::NKB], f32x16 (&nxt)[S::NKB], char* kcur, char* knxt, char* vcur,
                     char* vnxt) {
       const int t2 = t1 < kt_end ? next_tile(t1) : kt_end;
@@ -652,19 +662,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // Two waves share each SIMD (one from each workgroup on the CU).  The
       // wave in this phase (MFMAs plus the weights' vector work) takes issue
       // priority over a wave in phase B (MFMAs only), so that the vector work
-      // runs beside the other wave's MFMAs: 4% fewer cycles than equal priority.
+      // runs beside the other wave's MFMAs.
       __builtin_amdgcn_s_setprio(1);
-      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       u32x4 pk[S::NKB][2];
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-      auto weights = [&](int pr) {  // pair pr: registers 2 (pr % 8), +1 of block pr / 8
+      float ls[4];
+      auto weights = [&](int pr, float neg_m) {  // pair pr: registers 2 (pr % 8), +1 of block pr / 8
         const int kb = pr / 8, r = 2 * (pr % 8);
         const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], scale2, neg_m));
         const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], scale2, neg_m));
-        ls[pr % 4] += p0 + p1;
-        const uint32_t u = pack_bf16x2(p0, p1);
-        pk[kb][r / 8][(r / 2) % 4] = u;
+        ls[pr % 4] = pr < 4 ? p0 + p1 : ls[pr % 4] + (p0 + p1);
+        pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(p0, p1);
       };
+      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       bf16x8 kfr[PF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) kfr[i] = kread(i);
@@ -684,68 +693,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           vfr[3] = vread(1, 1);
         }
 #pragma unroll
-        for (int pr = i * NPAIR / NS; pr < (i + 1) * NPAIR / NS; ++pr) weights(pr);
+        for (int pr = i * NPAIR / NS; pr < (i + 1) * NPAIR / NS; ++pr) weights(pr, neg_m);
       }
       __builtin_amdgcn_sched_barrier(0);
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      float lt = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if (__ballot(lt > kSpecBound || (m_run == -INFINITY && lt > 0.f)) != 0) {  // wave-uniform, rare
+        row_max(cur);
+        if (__ballot(raise) != 0) {
+          apply_rescale();
+          const float neg_m2 = (m_run == -INFINITY) ? 0.f : -m_run;
+#pragma unroll
+          for (int pr = 0; pr < NPAIR; ++pr) weights(pr, neg_m2);
+          lt = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        }
+      }
+      l_run += lt;
 
       __builtin_amdgcn_s_setprio(0);
-      // ---- phase B: O^T += V^T P^T(t0) on the MFMA pipe, row max of t1 ----
-      // Max over the 32 scores of t1 in three-input steps (v_max3): node
-      // 32 + k = max(node 3k, 3k + 1, 3k + 2) for k = 0..14 covers every
-      // score by node 45 or 46, so the row max is max(node 45, node 46).
-      float tree[47];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        tree[r] = nxt[0][r];
-        tree[16 + r] = nxt[1][r];
-      }
+      // ---- phase B: O^T += V^T P^T(t0) on the MFMA pipe ----
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[(i / S::NVB) / 2][(i / S::NVB) % 2]);
         o[i % S::NVB] = mfma_bf16(join_tr(vfr[2 * (i % 2)], vfr[2 * (i % 2) + 1]), pb, o[i % S::NVB]);
         if (i + 2 < NP) {
           vfr[2 * (i % 2)] = vread(i + 2, 0);
           vfr[2 * (i % 2) + 1] = vread(i + 2, 1);
         }
-#pragma unroll
-        for (int k = i * 15 / NP; k < (i + 1) * 15 / NP; ++k)
-          tree[32 + k] = fmaxf(fmaxf(tree[3 * k], tree[3 * k + 1]), tree[3 * k + 2]);
-      }
-      // One MFMA, its reads two MFMAs ahead, one max step per group.
-#pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (i + 2 < NP) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (t1 < kt_end) {  // else nxt holds scores of stale LDS contents: unused
-        const float mx = max_halves(fmaxf(tree[45], tree[46])) * scale2;
-        raise = mx > m_run + kRescaleSlack;
-        m_new = raise ? fmaxf(m_run, mx) : m_run;
-        alpha = (!raise || m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-        if (tile_class(t1) == kTilePartial) {
-          mask_tile(nxt, t1);
-          row_max(nxt);
-        }
-        apply_rescale();
-      }
+      // else nxt holds scores of stale LDS contents: unused
+      if (t1 < kt_end && tile_class(t1) == kTilePartial) mask_tile(nxt, t1);
       wait_vm();
       __syncthreads();
       t0 = t1;
       t1 = t2;
     };
+    // Tiles are counted one per step (an atomic only while counting): a
+    // loop-carried count costs this kernel 40 registers and spills.
     while (true) {
       step(sa, sb, kbuf0, kbuf1, vbuf0, vbuf1);
-      ++ntiles;
+      count_tiles(p.tile_count, 1);
       if (t0 >= kt_end) break;
       step(sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
-      ++ntiles;
+      count_tiles(p.tile_count, 1);
       if (t0 >= kt_end) break;
     }
   }
-  count_tiles(p.tile_count, ntiles);
 
   const float l_tot = sum_halves(l_run);
   const float l_norm = l_tot;

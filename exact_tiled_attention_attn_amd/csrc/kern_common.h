@@ -410,8 +410,9 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, G | (G << 2) | (G << 4) | (G << 6), 0xF, 0xF, false);
 }
 
-// Debug tile counter: one 64-bit atomic add per workgroup, by its first lane,
-// of the tiles the workgroup computed (ntiles is workgroup-uniform).
+// Debug tile counter: a 64-bit atomic add, by the workgroup's first lane, of
+// tiles the workgroup computed (ntiles is workgroup-uniform); nothing while
+// the counter pointer is null.
 __device__ __forceinline__ void count_tiles(unsigned long long* counter, int ntiles) {
   if (counter != nullptr && threadIdx.x == 0 && ntiles > 0) atomicAdd(counter, (unsigned long long)ntiles);
 }
