@@ -7,6 +7,7 @@
 * causal row 0 reproduces V_0 bitwise; empty rows are defined;
 * strided layouts give bitwise the same results as contiguous ones;
 * negative and zero scale, and Q = K = V aliasing, against the oracle;
+* score ranges that grow by far more than the rescale slack per key tile;
 * bitmask pad bits past nk and padding words of padded mask rows are ignored.
 """
 
@@ -200,6 +201,36 @@ def test_negative_and_zero_scale(scale, mask):
                 if name in ("dQ", "dK", "dV"):
                     compare(name, got[name + "_det"][0, h], ref[name], dtype, (scale, mask, dtype, name, "det"),
                             extra=ex)
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "bitmask"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_reference_max_raised_between_tiles(mask, d):
+    """Scores whose range grows from one 64-key tile to the next by far more
+    than the lazy-rescale slack, so that the running reference max is raised
+    in the middle of the key sequence (the pipelined forward's exact path);
+    with the bitmask, even rows have no allowed key before key 300 (their
+    reference is still -inf when their first weights arrive)."""
+    rng = np.random.default_rng(21 + d)
+    n = nk = 640
+    Q = rng.standard_normal((1, 2, n, d), dtype=np.float32)
+    K = rng.standard_normal((1, 2, nk, d), dtype=np.float32)
+    K *= (1.0 + 4.0 * (np.arange(nk) // 64))[None, None, :, None].astype(np.float32)
+    V = rng.standard_normal((1, 2, nk, 128), dtype=np.float32)
+    G = rng.standard_normal((1, 2, n, 128), dtype=np.float32)
+    allowed = None
+    if mask == "bitmask":
+        allowed = np.ones((2, n, nk), bool)
+        allowed[:, 0::2, :300] = False
+    prob = W.custom(Q, K, V, G, scale=1 / np.sqrt(d), mask=mask, allowed=allowed, dtype="bf16")
+    got = run_gpu(prob)
+    for h in range(2):
+        ref = oracle_unit(prob, 0, h)
+        for name in ("O", "L", "dQ", "dK", "dV"):
+            ex = ref["allow"].get(name)
+            compare(name, got[name][0, h], ref[name], "bf16", (mask, d, name), extra=ex)
+            if name in ("dQ", "dK", "dV"):
+                compare(name, got[name + "_det"][0, h], ref[name], "bf16", (mask, d, name, "det"), extra=ex)
 
 
 def test_self_attention_aliased_inputs():
