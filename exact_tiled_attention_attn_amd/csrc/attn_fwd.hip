@@ -491,16 +491,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int i = 0; i < S::VWIN; ++i) voff[i] = S::VT::fill_src((w + S::NW * i) * 1024 + 16 * lane, vrow);
   const __amdgpu_buffer_rsrc_t rnone = make_rsrc(Kb, 0);
+  const int kmax_rows = 0x7FFFFFFF / krow, vmax_rows = 0x7FFFFFFF / vrow;
   auto fill_k = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kb + (int64_t)k0 * krow, (int64_t)(nk - k0) * krow);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc_rows(Kb + (int64_t)k0 * krow, nk - k0, krow, kmax_rows);
 #pragma unroll
     for (int i = 0; i < S::KWIN; ++i)
       if (S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS) dma16(r, buf + (w + S::NW * i) * 1024, koff[i]);
   };
   auto fill_v = [&](int kt, char* buf) {
     const int k0 = kt * S::BK;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vb + (int64_t)k0 * vrow, (int64_t)(nk - k0) * vrow);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc_rows(Vb + (int64_t)k0 * vrow, nk - k0, vrow, vmax_rows);
 #pragma unroll
     for (int i = 0; i < S::VWIN; ++i)
       if (S::VWINS % S::NW == 0 || w + S::NW * i < S::VWINS) dma16(r, buf + (w + S::NW * i) * 1024, voff[i]);
@@ -630,8 +631,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // This step's copies (K of t2 into kcur, V of t1 into vnxt) issue one per
       // first-phase MFMA; past the last tile they copy empty ranges.
       const int k2 = t2 < kt_end ? t2 * S::BK : nk, k1 = t1 < kt_end ? t1 * S::BK : nk;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb + (int64_t)k2 * krow, (int64_t)(nk - k2) * krow);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb + (int64_t)k1 * vrow, (int64_t)(nk - k1) * vrow);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc_rows(Kb + (int64_t)k2 * krow, nk - k2, krow, kmax_rows);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc_rows(Vb + (int64_t)k1 * vrow, nk - k1, vrow, vmax_rows);
       auto copy_item = [&](int i) {
         if (i < S::KWIN) {
           const bool real = S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS;

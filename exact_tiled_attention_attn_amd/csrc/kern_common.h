@@ -128,6 +128,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, 0x00020000);
 }
 
+// The same for `rows` rows of `row_bytes` each, in 32-bit scalar arithmetic:
+// max_rows = 0x7FFFFFFF / row_bytes, computed once by the caller.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_rows(const void* base, int rows, int row_bytes,
+                                                                 int max_rows) {
+  const int nb = rows <= 0 ? 0 : (rows >= max_rows ? 0x7FFFFFFF : rows * row_bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nb, 0x00020000);
+}
+
 // Swizzled LDS tile layout.  A tile row holds CPR 16-byte chunks.  LDS has
 // 64 four-byte banks, so a wave's 16-lane b128 row reads (16 rows, one chunk
 // each) and 32-lane transposed b64 reads (4 rows x an aligned quad of chunks)
