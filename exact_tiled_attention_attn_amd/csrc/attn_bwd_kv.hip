@@ -35,6 +35,17 @@
 // u + 4 v) by the score products, so the transposed reads of dO^T and Q^T
 // cover rows 4 apart: both kinds of read are then free of bank conflicts
 // and every LDS read address is one per-lane register plus a constant.
+//
+// Dropout (DROP; alphabetamath page, reverse procedure, closing remark: the
+// reverse pass replays the forward's realised mask): with keep decisions Z
+// and keep = P(kept), dV^T += dO^T (P o Z) (times 1 / keep at the end) and
+// dS = P (Z dP / keep - D); the dP accumulators then start from zero.  The
+// decisions are the counter-based draws of kern_common.h, regenerated: the
+// chunk's 32 rows form 8 row blocks of 4, a lane's key one key block of 4
+// with its quad, so the 8 lanes sharing a key block (a quad in each half)
+// draw the chunk's 8 calls, one each, in the previous step's second phase
+// (where the vector ALUs are idle), and exchange them by one half swap and
+// quad broadcasts.
 #include "attn_internal.h"
 #include "kern_common.h"
 
@@ -76,7 +87,7 @@ struct KvShape {
   static_assert(BQ == 64 && BK == 128, "two chunks of 32 queries, 32 keys per wave");
 };
 
-template <int D, int DV, int MASK>
+template <int D, int DV, int MASK, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   using S = KvShape<D, DV>;
   __shared__ __attribute__((aligned(1024))) char qs[S::NSTAGE * S::QTILE];
@@ -306,8 +317,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < S::NVF; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + orb + 32 * s);
-      if (s == 0) mfma_vc(dp, a, vf[s], dn);
-      else mfma_vacc(dp, a, vf[s]);
+      if (s == 0) {
+        if constexpr (DROP) mfma_vz(dp, a, vf[s]);
+        else mfma_vc(dp, a, vf[s], dn);
+      } else {
+        mfma_vacc(dp, a, vf[s]);
+      }
     }
     nops_after_mfma();
     after_nops_v(sc, dp);
@@ -347,6 +362,51 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     }
   };
 
+  // Dropout draws.  Lane (hh, quad position e) draws row block 4 hh + e of a
+  // chunk for its quad's key block: counter (key / 4, row / 4, unit, 0).  The
+  // call's 16 keep bits are packed as bit 4 (key % 4) + row % 4.  Register r
+  // = 4 g + e' of a chunk holds row 16 (g / 2) + 2 (g % 2) + hh + 4 e' (the
+  // perm() order), i.e. row block 4 (g / 2) + e', row 2 (g % 2) + hh in it:
+  // the call of the lane in half g / 2 at quad position e', bit dsh + 2 (g % 2).
+  const uint32_t dsh = 4u * (uint32_t)(lane & 3) + (uint32_t)hh;
+  uint32_t dc[4] = {0u, 0u, 0u, 0u};  // call in flight (the next chunk's)
+  uint32_t dm = 0u;                   // ... packed
+  uint32_t dM[2][4] = {};             // the current chunk's 8 calls, seen from this lane
+  auto draw_init = [&](int row0) {    // first row of the chunk (a multiple of 32)
+    dc[0] = (uint32_t)key >> 2;
+    dc[1] = ((uint32_t)row0 >> 2) + 4u * (uint32_t)hh + (uint32_t)(lane & 3);
+    dc[2] = (uint32_t)unit;
+    dc[3] = 0u;
+    dm = 0u;
+  };
+  // Item t of a call: rounds 0..9, then the keep bits of output word t - 10.
+  auto draw_item = [&](int t) {
+    if (t < 10) {
+      philox_round(dc[0], dc[1], dc[2], dc[3], p.drop.seed_lo, p.drop.seed_hi, t);
+    } else {
+      const uint32_t kb = keep_bits4(dc[t - 10], p.drop.p8);  // bit b: key b of the block, row t - 10
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dm |= ((kb >> b) & 1u) << (4 * b + (t - 10));
+    }
+  };
+  auto draw_share = [&]() {  // every lane's view of its 8-lane group's calls
+    auto sw = __builtin_amdgcn_permlane32_swap(dm, dm, false, false);  // [0]: the half-0 lane's, [1]: the half-1 lane's
+    dM[0][0] = quad_bcast<0>(sw[0]);
+    dM[0][1] = quad_bcast<1>(sw[0]);
+    dM[0][2] = quad_bcast<2>(sw[0]);
+    dM[0][3] = quad_bcast<3>(sw[0]);
+    dM[1][0] = quad_bcast<0>(sw[1]);
+    dM[1][1] = quad_bcast<1>(sw[1]);
+    dM[1][2] = quad_bcast<2>(sw[1]);
+    dM[1][3] = quad_bcast<3>(sw[1]);
+  };
+  // Keep mask (all ones or zero) of register r of the current chunk.
+  auto keep_mask = [&](int r) -> uint32_t {
+    const int g = r >> 2, e = r & 3;
+    return (uint32_t)__builtin_amdgcn_sbfe((int)dM[g >> 1][e], dsh + 2u * (uint32_t)(g & 1), 1u);
+  };
+  const float keep_inv = p.drop.keep_inv;
+
   // One pipeline step for chunk (st, c): cur holds its S and dP (masked);
   // nxt receives S and dP of the next chunk (stage nst, chunk nc), computed
   // from whatever that stage holds (unused after the last chunk).
@@ -368,8 +428,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // first kPrefetchA operands of the following step (its stage is already
   // visible), which then starts without waiting for them.
   bf16x8 afr[kPrefetchA];
+  // With DROP, dcur is -D of this chunk and nrow0 the first row of the next.
   auto step = [&](auto dofill, f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc,
-                  const f32x16& dni, auto dload, f32x16& dnx, auto hook, auto pre_a) {
+                  const f32x16& dni, auto dload, f32x16& dnx, auto hook, auto pre_a, const f32x16& dcur, int nrow0) {
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS + qtb;
     const char* ob = os + st * S::OTILE + 32 * c * S::OS + otb;
     const float* nls = reinterpret_cast<const float*>(lds_ld + nst * S::LDB + S::LD_L) + 32 * nc + 4 * hh;
@@ -416,10 +477,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     };
     auto weights_f = [&](int pr) {
       const int r = 2 * pr;
-      const float d0 = pe[pr][0] * dp[r];
-      const float d1 = pe[pr][1] * dp[r + 1];
-      pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0], pe[pr][1]);
-      sk[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
+      if constexpr (DROP) {  // dp = dP: dS = P Z dP / keep + P (-D)
+        const float z0 = __uint_as_float(__float_as_uint(pe[pr][0]) & keep_mask(r));
+        const float z1 = __uint_as_float(__float_as_uint(pe[pr][1]) & keep_mask(r + 1));
+        const float d0 = __builtin_fmaf(z0, keep_inv * dp[r], pe[pr][0] * dcur[r]);
+        const float d1 = __builtin_fmaf(z1, keep_inv * dp[r + 1], pe[pr][1] * dcur[r + 1]);
+        pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(z0, z1);
+        sk[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
+      } else {
+        const float d0 = pe[pr][0] * dp[r];
+        const float d1 = pe[pr][1] * dp[r + 1];
+        pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0], pe[pr][1]);
+        sk[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
+      }
     };
     // Slices 0..8 over the NA MFMAs: slice k issues e(k) and f(k - 1).
 #pragma unroll
@@ -430,8 +500,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         if (si == 0) mfma_vz(nsc, afr[i % PF], kf[si]);
         else mfma_vacc(nsc, afr[i % PF], kf[si]);
       } else {
-        if (i - si == 0) mfma_vc(ndp, afr[i % PF], vf[i - si], dni);
-        else mfma_vacc(ndp, afr[i % PF], vf[i - si]);
+        if (i - si == 0) {
+          if constexpr (DROP) mfma_vz(ndp, afr[i % PF], vf[0]);
+          else mfma_vc(ndp, afr[i % PF], vf[i - si], dni);
+        } else {
+          mfma_vacc(ndp, afr[i % PF], vf[i - si]);
+        }
       }
       if (i + PF < S::NA) afr[i % PF] = aread(i + PF);
       if (i >= S::NA - PB) bread(i - (S::NA - PB), tlo[i - (S::NA - PB)], thi[i - (S::NA - PB)]);
@@ -448,6 +522,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     asm volatile("" ::"v"(dni));  // keep the init registers until its product is done
 
     // ---- phase B ----
+    if constexpr (DROP) draw_init(nrow0);
     asm volatile("s_nop 1");  // the last packed P / dS operands were just written
     // Slice j: one MFMA, the reads PB MFMAs ahead and, for j < 8, one of the
     // next chunk's L log2(e) / D reads.
@@ -469,6 +544,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       }
       if (j < 4) lv[j] = *reinterpret_cast<const f32x4*>(nls + 8 * j);
       if (j == 2) hook();
+      if constexpr (DROP) {  // the next chunk's call: 14 items over the NB slices
+#pragma unroll
+        for (int t = j * 14 / S::NB; t < (j + 1) * 14 / S::NB; ++t) draw_item(t);
+      }
       if constexpr (decltype(dload)::value) {
         if (j >= 4 && j < 8) {
           const f32x4 x = *reinterpret_cast<const f32x4*>(nds + 8 * (j - 4));
@@ -478,6 +557,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DROP) draw_share();
   };
 
   // ---- main loop -------------------------------------------------------------
@@ -497,12 +577,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     wait_vm_n<2 * kF>();
     __syncthreads();
     f32x16 sa, pa, sb, pb;
-    score_products(sa, pa, 0, 0, load_dn(0, 0));
+    // -D of chunk 0 of the current tile (used by the dropout path's dS).
+    f32x16 dnB = load_dn(0, 0);
+    score_products(sa, pa, 0, 0, dnB);
+    if constexpr (DROP) {  // the first chunk's calls
+      draw_init(t0 * S::BQ);
+#pragma unroll
+      for (int t = 0; t < 14; ++t) draw_item(t);
+      draw_share();
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       lv[g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds_ld + S::LD_L) + 8 * g + 4 * hh);
     // -D starts of chunk 1 of the current tile (dnA) and chunk 0 of the next (dnB).
-    f32x16 dnA = load_dn(0, 1), dnB;
+    f32x16 dnA = load_dn(0, 1);
 #pragma unroll
     for (int i = 0; i < kPrefetchA; ++i) afr[i] = arow(0, 1, i);  // the first step's first operands
     unsigned j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
@@ -513,7 +601,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, q0);
       step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, dnA, std::false_type{}, dnA,
-           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); }, std::true_type{});
+           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); }, std::true_type{}, dnB, q0 + 32);
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3.
@@ -523,7 +611,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       fill_begin();
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, q0);
-      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA, [] {}, std::false_type{});
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, dnB, std::true_type{}, dnA, [] {}, std::false_type{}, dnA,
+           t1 < 0 ? 0 : t1 * S::BQ);
       ++ntiles;
       if (t1 < 0) break;
       t0 = t1;
@@ -559,15 +648,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c0 = vb * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<u32x2*>(dVp + c0 * 2) =
-            u32x2{pack_bf16x2(dv[vb][4 * g], dv[vb][4 * g + 1]), pack_bf16x2(dv[vb][4 * g + 2], dv[vb][4 * g + 3])};
+        const float ks = DROP ? p.drop.keep_inv : 1.f;
+        *reinterpret_cast<u32x2*>(dVp + c0 * 2) = u32x2{pack_bf16x2(dv[vb][4 * g] * ks, dv[vb][4 * g + 1] * ks),
+                                                        pack_bf16x2(dv[vb][4 * g + 2] * ks, dv[vb][4 * g + 3] * ks)};
       }
   }
 }
 
 template <int D, int DV, int MASK>
 static int launch_kv(const BwdParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_kv_kernel<D, DV, MASK>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
+  if (p.drop.p8 != 0)
+    hipLaunchKernelGGL((bwd_kv_kernel<D, DV, MASK, true>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<D, DV, MASK, false>), dim3((unsigned)p.grid_pad), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 

@@ -351,20 +351,29 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t bid, int64_t grid_pad, in
 // (seed_lo, seed_hi).  Its four words cover the 4 x 4 block of pairs with
 // i / 4, j / 4: pair (i, j) takes byte j % 4 (least significant first) of
 // word i % 4 as its 8-bit draw and is kept iff draw >= p8.
+// Round r (0..9) of Philox4x32-10 on the counter (c0..c3), key (k0, k1):
+// the round key is the key plus r times the Weyl increments.
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
+                                             uint32_t k1, int r) {
+  const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+  const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+  const uint32_t n0 = hi1 ^ c1 ^ (k0 + (uint32_t)r * 0x9E3779B9u), n2 = hi0 ^ c3 ^ (k1 + (uint32_t)r * 0xBB67AE85u);
+  c0 = n0;
+  c1 = lo1;
+  c2 = n2;
+  c3 = lo0;
+}
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
                                               uint32_t k0, uint32_t k1) {
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0;
-    c1 = lo1;
-    c2 = n2;
-    c3 = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
+  for (int r = 0; r < 10; ++r) philox_round(c0, c1, c2, c3, k0, k1, r);
+}
+// Keep bits of one output word of a call: bit b set iff byte b >= p8.
+__device__ __forceinline__ uint32_t keep_bits4(uint32_t w, uint32_t p8) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m |= (((w >> (8 * b)) & 0xFFu) >= p8 ? 1u : 0u) << b;
+  return m;
 }
 
 // Keep bits of the pairs (i, j0 + e), e = 0..3, for j0 % 4 == 0: bit e set
