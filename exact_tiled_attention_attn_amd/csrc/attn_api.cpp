@@ -71,7 +71,7 @@ int64_t mask_units(const attn_problem& p) { return p.mask_sb == 0 ? p.H : p.B * 
 
 Tiles dq_tiles(const attn_problem& p) {
   const int64_t nk = nkeys(p);
-  if (drop_p8(p) == 0 && eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nk))
+  if (eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nk))
     return Tiles{eta::kDqPipeBq, eta::kDqPipeBk, cdiv(p.n, eta::kDqPipeBq), cdiv(nk, eta::kDqPipeBk)};
   return Tiles{eta::kDqBq, eta::kDqBk, cdiv(p.n, eta::kDqBq), cdiv(nk, eta::kDqBk)};
 }
@@ -93,8 +93,7 @@ int fwd_split_count(const attn_problem& p) {
 
 // Pipelined dQ kernel's key-range splits (deterministic path only).
 int dq_split_count(const attn_problem& p) {
-  if (!p.deterministic || drop_p8(p) != 0 ||
-      !eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nkeys(p)))
+  if (!p.deterministic || !eta::bwd_dq_pipe_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, nkeys(p)))
     return 1;
   const Tiles t = dq_tiles(p);
   return eta::dq_splits(p.B * p.H, t.tq, t.tk);

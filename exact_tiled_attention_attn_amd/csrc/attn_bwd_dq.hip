@@ -358,7 +358,7 @@ static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, hipStrea
 }
 
 int launch_bwd_dq(const BwdParams& p, int bf16, int d, int v, int mask_mode, void* stream) {
-  if (p.drop.p8 == 0 && bwd_dq_pipe_supported(bf16, d, v, mask_mode, p.nk))
+  if (bwd_dq_pipe_supported(bf16, d, v, mask_mode, p.nk))
     return launch_bwd_dq_pipe(p, d, v, mask_mode, stream);
   hipStream_t st = (hipStream_t)stream;
   return bf16 ? launch_dims<true>(p, d, v, mask_mode, st) : launch_dims<false>(p, d, v, mask_mode, st);

@@ -86,7 +86,7 @@ struct DqPipeShape {
   static_assert(MTILE == NW * 2 * 256, "two 256-byte mask-word copies per wave");
 };
 
-template <int D, int DV, int MASK>
+template <int D, int DV, int MASK, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   using S = DqPipeShape<D, DV>;
   __shared__ __attribute__((aligned(1024))) char kts[S::NSTAGE * S::KTILE];
@@ -182,6 +182,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dinit[u][r] = dn[u];
   }
+  // Dropout (DROP): dS = P (Z dP / keep - D), the dP accumulators starting
+  // from zero, with the keep decisions Z of kern_common.h regenerated per
+  // 32-key chunk.  Per half u, lane (hh, quad position e) draws key block
+  // 4 hh + e of the chunk for its quad's query block (counter (key / 4,
+  // query / 4, unit, 0)); the call's 16 keep bits are packed as bit
+  // 4 (query % 4) + key % 4.  Register r = 4 g + e' of a half holds key
+  // 16 (g / 2) + 2 (g % 2) + hh + 4 e' of the chunk (the perm() order), i.e.
+  // key block 4 (g / 2) + e', key 2 (g % 2) + hh in it: the call of the lane
+  // in half g / 2 at quad position e', bit dsh + 2 (g % 2).  The next chunk's
+  // calls are drawn during a step's second phase (where the vector ALUs are
+  // idle) and shared by one half swap and quad broadcasts.
+  const uint32_t dsh = 4u * (uint32_t)(lane & 3) + (uint32_t)hh;
+  uint32_t dc[2][4] = {}, dm[2] = {0u, 0u}, dM[2][2][4] = {};
+  auto draw_init = [&](int key0) {  // first key of the chunk (a multiple of 32)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      dc[u][0] = ((uint32_t)key0 >> 2) + 4u * (uint32_t)hh + (uint32_t)(lane & 3);
+      dc[u][1] = (uint32_t)(qa + 32 * u) >> 2;
+      dc[u][2] = (uint32_t)unit;
+      dc[u][3] = 0u;
+      dm[u] = 0u;
+    }
+  };
+  auto draw_item = [&](int t) {  // call t / 14: rounds 0..9, then the keep bits of its four words
+    const int u = t / 14, k = t % 14;
+    if (k < 10) philox_round(dc[u][0], dc[u][1], dc[u][2], dc[u][3], p.drop.seed_lo, p.drop.seed_hi, k);
+    else dm[u] |= keep_bits4(dc[u][k - 10], p.drop.p8) << (4 * (k - 10));
+  };
+  auto draw_share = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      auto sw = __builtin_amdgcn_permlane32_swap(dm[u], dm[u], false, false);  // [0]: half 0's call, [1]: half 1's
+      dM[u][0][0] = quad_bcast<0>(sw[0]);
+      dM[u][0][1] = quad_bcast<1>(sw[0]);
+      dM[u][0][2] = quad_bcast<2>(sw[0]);
+      dM[u][0][3] = quad_bcast<3>(sw[0]);
+      dM[u][1][0] = quad_bcast<0>(sw[1]);
+      dM[u][1][1] = quad_bcast<1>(sw[1]);
+      dM[u][1][2] = quad_bcast<2>(sw[1]);
+      dM[u][1][3] = quad_bcast<3>(sw[1]);
+    }
+  };
+  auto keep_mask = [&](int u, int r) -> uint32_t {  // all ones iff register r of half u is kept
+    const int g = r >> 2, e = r & 3;
+    return (uint32_t)__builtin_amdgcn_sbfe((int)dM[u][g >> 1][e], dsh + 2u * (uint32_t)(g & 1), 1u);
+  };
+  const float keep_inv = p.drop.keep_inv;
 
   // ---- tile fills ----------------------------------------------------------
   // Wave w copies a contiguous run of 1 KB windows of each tile: KB = KWINS /
@@ -338,8 +385,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + 32 * s);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        if (s == 0) mfma_vc(dp[u], a, of[u][s], dinit[u]);
-        else mfma_vacc(dp[u], a, of[u][s]);
+        if (s == 0) {
+          if constexpr (DROP) mfma_vz(dp[u], a, of[u][s]);
+          else mfma_vc(dp[u], a, of[u][s], dinit[u]);
+        } else {
+          mfma_vacc(dp[u], a, of[u][s]);
+        }
       }
     }
     nops_after_mfma();
@@ -363,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // visible), which then starts without waiting for them.
   bf16x8 afr[kDqPrefetchA];
   auto step = [&](auto dofill, f32x16 (&sc)[2], f32x16 (&dp)[2], f32x16 (&nsc)[2], f32x16 (&ndp)[2], int st, int c,
-                  int nst, int nc, auto hook, auto pre_a) {
+                  int nst, int nc, auto hook, auto pre_a, int nkey0) {
     const char* kb = kts + st * S::KTILE + 32 * c * S::KS + ktb;
     // Phase B's transposed K operands; the first PB are read in phase A's last sub-slices.
     auto bread = [&](int j, i16x4& lo, i16x4& hi) {
@@ -395,7 +446,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     auto w2 = [&](int pr) { pe[pr][1] = fast_exp2(pt[pr]); };
     auto w3 = [&](int pr) {
       const int u = pr >> 3, r = 2 * (pr & 7);
-      sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0] * dp[u][r], pe[pr][1] * dp[u][r + 1]);
+      if constexpr (DROP) {  // dp = dP: dS = P Z dP / keep + P (-D)
+        const float z0 = __uint_as_float(__float_as_uint(pe[pr][0]) & keep_mask(u, r));
+        const float z1 = __uint_as_float(__float_as_uint(pe[pr][1]) & keep_mask(u, r + 1));
+        sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(__builtin_fmaf(z0, keep_inv * dp[u][r], pe[pr][0] * dn[u]),
+                                                  __builtin_fmaf(z1, keep_inv * dp[u][r + 1], pe[pr][1] * dn[u]));
+      } else {
+        sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0] * dp[u][r], pe[pr][1] * dp[u][r + 1]);
+      }
     };
     // Work items in issue order: w1(k), w2(k), w3(k - 1) for k = 0..15, then
     // w3(15); item t goes to sub-slice t * NSUB / NITEM.
@@ -419,8 +477,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
         else mfma_vacc(nsc[u], afr[i % PF], qf[u][si]);
       } else {
         const int vi = i - si;
-        if (vi == 0) mfma_vc(ndp[u], afr[i % PF], of[u][vi], dinit[u]);
-        else mfma_vacc(ndp[u], afr[i % PF], of[u][vi]);
+        if (vi == 0) {
+          if constexpr (DROP) mfma_vz(ndp[u], afr[i % PF], of[u][0]);
+          else mfma_vc(ndp[u], afr[i % PF], of[u][vi], dinit[u]);
+        } else {
+          mfma_vacc(ndp[u], afr[i % PF], of[u][vi]);
+        }
       }
       if (u == 1 && i + PF < S::NR) afr[i % PF] = aread(i + PF);
       if (u == 1 && i >= S::NR - PB) bread(i - (S::NR - PB), tlo[i - (S::NR - PB)], thi[i - (S::NR - PB)]);
@@ -436,6 +498,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 
     // ---- phase B ----
     // Operand j: key step j / NDB, column block j % NDB; two MFMAs (halves).
+    if constexpr (DROP) draw_init(nkey0);
     asm volatile("s_nop 1");  // the last packed dS operands were just written
     // Slice j: two MFMAs (halves) and the reads PB operands ahead.
 #pragma unroll
@@ -451,8 +514,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       if constexpr (decltype(dofill)::value) {  // chunk 1: the next step's first row operands
         if (j >= S::NB - PF) afr[j - (S::NB - PF)] = arow(nst, 1, j - (S::NB - PF));
       }
+      if constexpr (DROP) {  // the next chunk's two calls: 28 items over the NB slices
+#pragma unroll
+        for (int t = j * 28 / S::NB; t < (j + 1) * 28 / S::NB; ++t) draw_item(t);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DROP) draw_share();
   };
 
   // ---- main loop -------------------------------------------------------------
@@ -478,6 +546,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     __syncthreads();
     f32x16 sa[2], pa[2], sb[2], pb[2];
     score_products(sa, pa, 0, 0);
+    if constexpr (DROP) {  // the first chunk's calls
+      draw_init(t0 * S::BK);
+#pragma unroll
+      for (int t = 0; t < 28; ++t) draw_item(t);
+      draw_share();
+    }
 #pragma unroll
     for (int i = 0; i < kDqPrefetchA; ++i) afr[i] = arow(0, 1, i);  // the first step's first operands
     unsigned j = 0;  // position of t0 in the sequence; its stage is j % NSTAGE
@@ -488,7 +562,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, k0);
       step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1,
-           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); }, std::true_type{});
+           [&] { plan_fill(t3, (int)((j + 3) & (S::NSTAGE - 1))); }, std::true_type{}, k0 + 32);
       // The next tile's stage must be complete and visible before chunk 1's
       // phase A reads it; after this barrier every wave is past tile j-1, so
       // its stage takes the fill of position j+3 (empty past the last tile),
@@ -498,7 +572,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       fill_begin();
       // chunk 1 of t0
       if (partial) mask_chunk(sb, st, 1, k0);
-      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, [] {}, std::false_type{});
+      step(std::true_type{}, sb, pb, sa, pa, st, 1, nst, 0, [] {}, std::false_type{}, t1 < 0 ? 0 : t1 * S::BK);
       ++ntiles;
       if (t1 < 0) break;
       t0 = t1;
@@ -555,7 +629,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 
 template <int D, int DV, int MASK>
 static int launch_dq_pipe(const BwdParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, DV, MASK>), dim3((unsigned)p.grid_pad_dq), dim3(256), 0, st, p);
+  if (p.drop.p8 != 0)
+    hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, DV, MASK, true>), dim3((unsigned)p.grid_pad_dq), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, DV, MASK, false>), dim3((unsigned)p.grid_pad_dq), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ def test_keep_decisions_match_the_oracle(seed, p, unit_bh, i0, j0, rows, cols):
     assert np.array_equal(got.cpu().numpy().astype(bool), full[i0:, j0:])
 
 
-DIMS = [("f32", 64, 64), ("f32", 80, 80), ("bf16", 128, 128), ("bf16", 64, 128)]
+DIMS = [("f32", 64, 64), ("f32", 80, 80), ("bf16", 128, 128), ("bf16", 64, 128), ("bf16", 64, 64)]
 
 
 @pytest.mark.parametrize("mask", ["none", "causal", "bitmask"])
