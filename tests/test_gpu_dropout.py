@@ -8,6 +8,8 @@ page, reverse procedure): the kernels regenerate each keep decision from
 * O, L and dQ, dK, dV (both dQ paths) equal the oracle's dropout forward
   and VJP taken with the oracle's own mask, within the dtype tolerance;
 * the same seed gives bitwise the same results, another seed other ones;
+* with few query rows against many keys the dQ kernel's key-range splits
+  carry the replayed mask too;
 * the autograd wrapper passes the dropout through to the backward.
 """
 
@@ -93,6 +95,46 @@ def test_dropout_parity(dtype, d, v, mask):
             compare("dQ", got(dq[0, h]), rdQ, dtype, (tag, path), extra=al.get("dQ"))
             compare("dK", got(dk[0, h]), rdK, dtype, (tag, path), extra=al.get("dK"))
             compare("dV", got(dv[0, h]), rdV, dtype, (tag, path), extra=al.get("dV"))
+
+
+@pytest.mark.parametrize("d,v", [(128, 128), (64, 128)])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_dropout_with_key_range_splits(d, v, mask):
+    """Few query rows against many keys (the dQ kernel splits its key
+    range): the replayed mask through the split dQ partials and their merge,
+    bitwise reproducible, against the oracle."""
+    import exact_tiled_attention_attn_amd as E
+
+    H, n, nk, p, seed = 2, 70, 3000, 0.25, 99
+    off = nk - n if mask == "causal" else 0
+    rng = np.random.default_rng(d + v + nk)
+    Q, K, V, G = (W.round_bf16(rng.standard_normal((1, H, r, x), dtype=np.float32))
+                  for r, x in ((n, d), (nk, d), (nk, v), (n, v)))
+    A = W.causal_allowed(n, nk=nk, offset=off) if mask == "causal" else None
+    q, k, val, g = (_dev(x, "bf16") for x in (Q, K, V, G))
+    c = 1 / np.sqrt(d)
+    kw = dict(dropout_p=p, dropout_seed=seed, causal_offset=off)
+    o, L = E.fwd(q, k, val, c, mask, None, **kw)
+    pb = E.make_problem(q, k, val, o, c, mask, None, True, off, p, seed)
+    assert E.workspace_size(pb, True) >= 2 * 4 * H * 128 + 2 * 4 * H * n * d, "dQ key-range splits expected"
+    det = E.bwd(q, k, val, o, g, L, c, mask, None, deterministic=True, **kw)
+    det2 = E.bwd(q, k, val, o, g, L, c, mask, None, deterministic=True, **kw)
+    torch.cuda.synchronize()
+    for x, y in zip(det, det2):
+        assert torch.equal(x, y)
+    p8 = dropout.p8_of(p)
+    got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    for h in range(H):
+        Z = dropout.keep_mask(seed, h, n, nk, p8)
+        Qh, Kh, Vh, Gh = (x[0, h].astype(np.float64) for x in (Q, K, V, G))
+        Y, Lr = dropout.forward(Qh, Kh, Vh, c, A, Z, p8)
+        rdQ, rdK, rdV = dropout.vjp(Qh, Kh, Vh, c, A, Z, p8, Gh, stored(Y, "bf16"))
+        al = allowance_full(Qh, Kh, Vh, Gh, c, A, stored(Y, "bf16"), Lr, "bf16", Z, p8)
+        tag = (d, v, mask, h)
+        compare("O", got(o[0, h]), Y, "bf16", tag, extra=al.get("O"))
+        compare("dQ", got(det[0][0, h]), rdQ, "bf16", tag, extra=al.get("dQ"))
+        compare("dK", got(det[1][0, h]), rdK, "bf16", tag, extra=al.get("dK"))
+        compare("dV", got(det[2][0, h]), rdV, "bf16", tag, extra=al.get("dV"))
 
 
 def test_autograd_passes_dropout_through():
