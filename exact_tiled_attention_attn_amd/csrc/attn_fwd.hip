@@ -541,6 +541,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Masking of a partially allowed tile's scores (keys past nk, causal, bitmask).
   auto mask_tile = [&](f32x16 (&sc)[S::NKB], int kt) {
     const int k0 = kt * S::BK;
+    if constexpr (MASK == kMaskBitmask) {
+      if (k0 + S::BK <= nk) {  // every key of the tile exists: the word's bit alone decides
+#pragma unroll
+        for (int kb = 0; kb < S::NKB; ++kb) {
+          const uint32_t word = qvalid ? mrow[(k0 + 32 * kb) >> 5] : 0xFFFFFFFFu;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r >> 2) + 4 * hh + (r & 3);
+            // All ones iff allowed; disallowed scores become -inf (bit select).
+            const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)word, (uint32_t)kk, 1u);
+            sc[kb][r] = __uint_as_float((__float_as_uint(sc[kb][r]) & keep) | (0xFF800000u & ~keep));
+          }
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) {
       uint32_t word = 0xFFFFFFFFu;
