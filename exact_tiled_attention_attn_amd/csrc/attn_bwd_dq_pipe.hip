@@ -350,6 +350,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // row 32 c + perm(m) of the tile, for query qa + 32 u.
   auto mask_chunk = [&](f32x16 (&sc)[2], int st, int c, int k0) {
     const uint32_t* ms = reinterpret_cast<const uint32_t*>(mws + st * S::MTILE);
+    if constexpr (MASK == kMaskBitmask) {
+      if (k0 + S::BK <= nk) {  // every key of the tile exists: the word's bit alone decides
+        const uint32_t sentinel = __float_as_uint(masked_score);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t word = ms[(64 * w + 32 * u + (lane & 31)) * S::MWORDS + c];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = perm(8 * (r >> 2) + 4 * hh + (r & 3));
+            const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)word, (uint32_t)kk, 1u);
+            sc[u][r] = __uint_as_float((__float_as_uint(sc[u][r]) & keep) | (sentinel & ~keep));
+          }
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = qa + 32 * u;

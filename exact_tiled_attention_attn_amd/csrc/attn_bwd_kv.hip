@@ -349,6 +349,18 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // query row 32 c + perm(m) of the tile.
   auto mask_chunk = [&](f32x16& sc, int st, int c, int q0) {
     const uint32_t* ms = reinterpret_cast<const uint32_t*>(lds_ld + st * S::LDB + S::LD_M);
+    if constexpr (MASK == kMaskBitmask) {
+      if (k0 + S::BK <= nk) {  // every key of the tile exists: the word's bit alone decides
+        const uint32_t sentinel = __float_as_uint(masked_score);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * c + perm(8 * (r >> 2) + 4 * hh + (r & 3));
+          const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)ms[ql * S::MWORDS + w], (uint32_t)(lane & 31), 1u);
+          sc[r] = __uint_as_float((__float_as_uint(sc[r]) & keep) | (sentinel & ~keep));
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ql = 32 * c + perm(8 * (r >> 2) + 4 * hh + (r & 3));
