@@ -127,7 +127,9 @@ typedef struct {
    * (j / 4, i / 4, u, 0) and key (dropout_seed mod 2^32, dropout_seed div
    * 2^32).  O_i = sum_j P_ij Z_ij V_j * 256 / (256 - p8), with P the
    * undropped softmax, whose L is returned; attn_bwd with the same seed and
-   * dropout_p regenerates Z.  Runs on the register-staged kernels. */
+   * dropout_p regenerates Z.  The forward runs on the register-staged
+   * kernel; the backward's key-tile-outer and deterministic dQ kernels
+   * replay Z in their pipelined bf16 forms where those apply. */
   double dropout_p;
   uint64_t dropout_seed;
 } attn_problem;
@@ -140,8 +142,8 @@ typedef struct {
  * L log2(e) (4 B H n_pad bytes each, n_pad = n rounded up to 128), plus the
  * fp32 dQ accumulator (4 B H n d bytes) when deterministic = 0, plus the
  * bitmask tile map(s), plus, when deterministic = 1 and few query tiles face
- * many key tiles (bf16 with (d, v) in {(128,128), (64,128), (64,64)}, no
- * dropout), the dQ kernel's key-range partials, S B H n d * 4 bytes for
+ * many key tiles (bf16 with (d, v) in {(128,128), (64,128), (64,64)}), the
+ * dQ kernel's key-range partials, S B H n d * 4 bytes for
  * S <= 16 splits; every region 256-byte aligned.  Validates the problem like
  * the compute calls. */
 attn_status attn_workspace_size(const attn_problem* p, int is_bwd, size_t* bytes);

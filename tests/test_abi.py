@@ -204,6 +204,26 @@ def test_forward_split_workspace():
     assert wsize(p, 0) == (0, 0)
 
 
+def test_dq_split_workspace_with_and_without_dropout():
+    """Deterministic backward, few query tiles against many key tiles (bf16,
+    (d, v) = (128, 128)): the workspace holds D, L log2(e) and the dQ
+    kernel's S key-range partials, with dropout as without (the pipelined
+    dQ kernel replays the mask)."""
+    p = problem(B=1, H=2, n=100, d=128, v=128)
+    p.nk, p.deterministic = 8192, 1
+    for name, w in (("sk", 128), ("sv", 128)):
+        arr = getattr(p, name)
+        arr[0], arr[1], arr[2] = 2 * 8192 * w, 8192 * w, w
+    align = lambda x: -(-x // 256) * 256  # noqa: E731
+    S = 16  # 2 workgroups of 256 queries: min(16, ceil(512 / 2), 128 key tiles / 4)
+    expected = 2 * align(4 * 2 * 128) + align(S * 2 * 100 * 128 * 4)
+    assert wsize(p, 1) == (0, expected)
+    p.dropout_p = 0.2
+    assert wsize(p, 1) == (0, expected)
+    p.deterministic = 0  # atomic path: the fp32 dQ accumulator, no splits
+    assert wsize(p, 1) == (0, 2 * align(4 * 2 * 128) + align(4 * 2 * 100 * 128))
+
+
 def test_null_and_misaligned_pointers():
     p = problem()
     assert call_fwd(p, Q=0) == 1 and "Q" in err()
