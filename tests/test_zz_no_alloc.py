@@ -60,6 +60,24 @@ def test_noalloc_backward_equals_workspace_backward(deterministic):
                 compare(name, x.reshape(-1, x.shape[-1]), r.reshape(-1, r.shape[-1]), "bf16", (H, n, mask, name))
 
 
+def test_noalloc_backward_with_dropout():
+    """The same with dropout (the pipelined backward kernels replay the mask;
+    both calls, the second smaller, also run the dQ key-range splits)."""
+    import exact_tiled_attention_attn_amd as E
+
+    for H, n, d, v, mask, seed in [(4, 2048, 128, 128, "causal", 4), (2, 512, 64, 128, "none", 5)]:
+        q, k, val, do, mdev = _case(H, n, d, v, mask, seed)
+        c, kw = d ** -0.5, dict(dropout_p=0.15, dropout_seed=seed)
+        o, L = E.fwd(q, k, val, c, mask, mdev, **kw)
+        ref = E.bwd(q, k, val, o, do, L, c, mask, mdev, deterministic=True, **kw)
+        outs = [torch.full_like(t, float("nan")) for t in ref]
+        E.bwd_noalloc(q, k, val, o, do, L, c, mask, mdev, dq=outs[0], dk=outs[1], dv=outs[2], deterministic=True,
+                      **kw)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dQ", "dK", "dV"), outs, ref):
+            assert torch.equal(a, b), (H, n, mask, name)
+
+
 def test_noalloc_refuses_problems_beyond_the_scratch():
     import exact_tiled_attention_attn_amd as E
 
