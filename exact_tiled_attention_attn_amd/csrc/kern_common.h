@@ -274,11 +274,13 @@ __device__ __forceinline__ void mfma_vz(f32x16& d, const bf16x8& a, const bf16x8
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
 // mfma_vc may receive c in registers the compiler copied (from AGPRs) just
-// before the statement and treats as free right after it: the statement
-// itself waits for such a copy and keeps the wave from overwriting those
-// registers while the MFMA still reads them.
+// before the statement: the statement itself waits for such a copy.  Its
+// callers keep c live well past the product, so nothing overwrites c while
+// the MFMA still reads it; the wait-state test of the compiled kernels checks
+// this (a write of a separate accumulator input within 18 wait states) for
+// every instance.
 __device__ __forceinline__ void mfma_vc(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
                : "=&v"(d)
                : "v"(a), "a"(b), "v"(c));
 }

@@ -38,6 +38,12 @@ def test_checker_catches_planted_hazards():
     assert any("accumulator input" in p for p in check(agpr_back))
     guarded = ["v_accvgpr_write_b32 a15, v3", "s_nop 4", "v_mfma_f32_32x32x16_bf16 a[0:15], v[16:19], v[20:23], a[0:15]"]
     assert check(guarded) == []
+    war_c = [
+        "v_mfma_f32_32x32x16_bf16 v[32:47], v[4:7], a[8:11], v[0:15]",
+        "s_nop 7",
+        "v_mov_b32_e32 v3, 0",
+    ]
+    assert any("accumulator input overwritten" in p for p in check(war_c))
     early_read = [
         "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]",
         "s_nop 7",
