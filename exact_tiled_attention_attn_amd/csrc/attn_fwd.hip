@@ -683,12 +683,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __builtin_amdgcn_s_setprio(1);
       u32x4 pk[S::NKB][2];
       float ls[4];
-      auto weights = [&](int pr, float neg_m) {  // pair pr: registers 2 (pr % 8), +1 of block pr / 8
+      // Pair pr (registers 2 (pr % 8), +1 of block pr / 8) in two halves,
+      // issued one slice apart so that the exponentials' latency is covered:
+      // weights_e = the exponentials, weights_f = the sum and the packing.
+      float pe[S::NKB * 8][2];
+      auto weights_e = [&](int pr, float neg_m) {
         const int kb = pr / 8, r = 2 * (pr % 8);
-        const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], scale2, neg_m));
-        const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], scale2, neg_m));
-        ls[pr % 4] = pr < 4 ? p0 + p1 : ls[pr % 4] + (p0 + p1);
-        pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(p0, p1);
+        pe[pr][0] = fast_exp2(__builtin_fmaf(cur[kb][r], scale2, neg_m));
+        pe[pr][1] = fast_exp2(__builtin_fmaf(cur[kb][r + 1], scale2, neg_m));
+      };
+      auto weights_f = [&](int pr) {
+        const int kb = pr / 8, r = 2 * (pr % 8);
+        ls[pr % 4] = pr < 4 ? pe[pr][0] + pe[pr][1] : ls[pr % 4] + (pe[pr][0] + pe[pr][1]);
+        pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(pe[pr][0], pe[pr][1]);
+      };
+      auto weights = [&](int pr, float neg_m) {
+        weights_e(pr, neg_m);
+        weights_f(pr);
       };
       const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       bf16x8 kfr[PF];
@@ -709,8 +720,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           vfr[2] = vread(1, 0);
           vfr[3] = vread(1, 1);
         }
+        // Slice i: the exponentials of its pairs and the rest of the previous slice's.
 #pragma unroll
-        for (int pr = i * NPAIR / NS; pr < (i + 1) * NPAIR / NS; ++pr) weights(pr, neg_m);
+        for (int k = i * (NPAIR + 1) / NS; k < (i + 1) * (NPAIR + 1) / NS; ++k) {
+          if (k < NPAIR) weights_e(k, neg_m);
+          if (k > 0) weights_f(k - 1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       float lt = (ls[0] + ls[1]) + (ls[2] + ls[3]);
