@@ -219,6 +219,32 @@ def test_split_key_forward(d, v, n, nk, mask, off):
         compare("L", Lh, rL, dtype, tag)
 
 
+@pytest.mark.parametrize("d,v", [(128, 128), (64, 128)])
+def test_split_key_forward_growing_scores(d, v):
+    """Key-range splits whose scores grow from one 64-key tile to the next by
+    far more than the rescale slack: every split raises its reference max
+    mid-range (the forward's exact path) before the splits are merged."""
+    import exact_tiled_attention_attn_amd as E
+
+    H, n, nk, c, dtype = 2, 100, 4096, 1.0 / np.sqrt(d), "bf16"
+    Q, K, V, G, rng = _inputs(H, n, nk, d, v, "f32", seed=d + v + 7)
+    K = K * ((1.0 + 4.0 * (np.arange(nk) % 512 // 64)) * (1.0 + np.arange(nk) / nk))[None, None, :, None]
+    Q, K, V = (W.round_bf16(x.astype(np.float32)) for x in (Q, K, V))
+    q, k, val = (_dev(x, dtype) for x in (Q, K, V))
+    o_like = torch.empty((1, H, n, v), dtype=torch.bfloat16, device=DEV)
+    assert E.workspace_size(E.make_problem(q, k, val, o_like, c, "none"), False) > 0, "key-range splits expected"
+    o, L = E.fwd(q, k, val, c, "none")
+    torch.cuda.synchronize()
+    got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    A = np.ones((n, nk), bool)
+    for h in range(H):
+        Qh, Kh, Vh = (x[0, h].astype(np.float64) for x in (Q, K, V))
+        rO, rL, _, _, _, rows = _oracle_fwd_only(Qh, Kh, Vh, c, A)
+        orb = output_rounding_bound(Qh, Kh, Vh, rL, c, lambda r: A[r], dtype)
+        compare("O", got(o[0, h]), rO, dtype, (d, v, h), extra=orb)
+        compare("L", got(L[0, h]), rL, dtype, (d, v, h))
+
+
 @pytest.mark.parametrize("n,nk,mask,off", SPLIT_SHAPES)
 @pytest.mark.parametrize("d,v", [(128, 128), (64, 128), (64, 64)])
 def test_split_key_backward(d, v, n, nk, mask, off):
