@@ -88,7 +88,7 @@ struct Layout {
 
 int fwd_split_count(const attn_problem& p) {
   const Tiles t = fwd_tiles(p);
-  return eta::fwd_splits(p.dtype == ATTN_BF16, p.d, p.v, p.B * p.H, t.tq, t.tk, drop_p8(p));
+  return eta::fwd_splits(p.dtype == ATTN_BF16, p.d, p.v, p.B * p.H, t.tq, t.tk);
 }
 
 // Pipelined dQ kernel's key-range splits (deterministic path only).

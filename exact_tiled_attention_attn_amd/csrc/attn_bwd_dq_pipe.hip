@@ -187,13 +187,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // 32-key chunk.  Per half u, lane (hh, quad position e) draws key block
   // 4 hh + e of the chunk for its quad's query block (counter (key / 4,
   // query / 4, unit, 0)); the call's 16 keep bits are packed as bit
-  // 4 (query % 4) + key % 4.  Register r = 4 g + e' of a half holds key
+  // 8 (key % 4) + 4 + query % 4.  Register r = 4 g + e' of a half holds key
   // 16 (g / 2) + 2 (g % 2) + hh + 4 e' of the chunk (the perm() order), i.e.
   // key block 4 (g / 2) + e', key 2 (g % 2) + hh in it: the call of the lane
-  // in half g / 2 at quad position e', bit dsh + 2 (g % 2).  The next chunk's
+  // in half g / 2 at quad position e', bit dsh + 16 (g % 2).  The next chunk's
   // calls are drawn during a step's second phase (where the vector ALUs are
   // idle) and shared by one half swap and quad broadcasts.
-  const uint32_t dsh = 4u * (uint32_t)(lane & 3) + (uint32_t)hh;
+  const uint32_t dsh = 4u + (uint32_t)(lane & 3) + 8u * (uint32_t)hh;
+  const KeepConsts kq = keep_consts(p.drop.p8);
   uint32_t dc[2][4] = {}, dm[2] = {0u, 0u}, dM[2][2][4] = {};
   auto draw_init = [&](int key0) {  // first key of the chunk (a multiple of 32)
 #pragma unroll
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   auto draw_item = [&](int t) {  // call t / 14: rounds 0..9, then the keep bits of its four words
     const int u = t / 14, k = t % 14;
     if (k < 10) philox_round(dc[u][0], dc[u][1], dc[u][2], dc[u][3], p.drop.seed_lo, p.drop.seed_hi, k);
-    else dm[u] |= keep_bits4(dc[u][k - 10], p.drop.p8) << (4 * (k - 10));
+    else dm[u] = pack_keep(dm[u], keep_flags(dc[u][k - 10], kq), k - 10);
   };
   auto draw_share = [&]() {
 #pragma unroll
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   };
   auto keep_mask = [&](int u, int r) -> uint32_t {  // all ones iff register r of half u is kept
     const int g = r >> 2, e = r & 3;
-    return (uint32_t)__builtin_amdgcn_sbfe((int)dM[u][g >> 1][e], dsh + 2u * (uint32_t)(g & 1), 1u);
+    return (uint32_t)__builtin_amdgcn_sbfe((int)dM[u][g >> 1][e], dsh + 16u * (uint32_t)(g & 1), 1u);
   };
   const float keep_inv = p.drop.keep_inv;
 

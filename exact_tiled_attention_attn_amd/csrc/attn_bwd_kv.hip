@@ -376,11 +376,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 
   // Dropout draws.  Lane (hh, quad position e) draws row block 4 hh + e of a
   // chunk for its quad's key block: counter (key / 4, row / 4, unit, 0).  The
-  // call's 16 keep bits are packed as bit 4 (key % 4) + row % 4.  Register r
+  // call's 16 keep bits are packed as bit 8 (key % 4) + 4 + row % 4.  Register r
   // = 4 g + e' of a chunk holds row 16 (g / 2) + 2 (g % 2) + hh + 4 e' (the
   // perm() order), i.e. row block 4 (g / 2) + e', row 2 (g % 2) + hh in it:
   // the call of the lane in half g / 2 at quad position e', bit dsh + 2 (g % 2).
-  const uint32_t dsh = 4u * (uint32_t)(lane & 3) + (uint32_t)hh;
+  const uint32_t dsh = 8u * (uint32_t)(lane & 3) + 4u + (uint32_t)hh;
+  const KeepConsts kq = keep_consts(p.drop.p8);
   uint32_t dc[4] = {0u, 0u, 0u, 0u};  // call in flight (the next chunk's)
   uint32_t dm = 0u;                   // ... packed
   uint32_t dM[2][4] = {};             // the current chunk's 8 calls, seen from this lane
@@ -396,9 +397,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     if (t < 10) {
       philox_round(dc[0], dc[1], dc[2], dc[3], p.drop.seed_lo, p.drop.seed_hi, t);
     } else {
-      const uint32_t kb = keep_bits4(dc[t - 10], p.drop.p8);  // bit b: key b of the block, row t - 10
-#pragma unroll
-      for (int b = 0; b < 4; ++b) dm |= ((kb >> b) & 1u) << (4 * b + (t - 10));
+      dm = pack_keep(dm, keep_flags(dc[t - 10], kq), t - 10);  // row t - 10 of the block
     }
   };
   auto draw_share = [&]() {  // every lane's view of its 8-lane group's calls

@@ -394,6 +394,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // constant; K and V have two buffers each: K_{j+2} and V_{j+1} stream in
 // while tile j is consumed.  O is normalised by the fp32 sum of the weights
 // (the one L is taken from); the PV product uses their bf16 roundings.
+// Dropout (DROP): the PV product takes P o Z and O is scaled by 1 / P(keep),
+// with the keep decisions Z of kern_common.h regenerated per tile.
 // ---------------------------------------------------------------------------
 template <int D, int DV>
 struct FwdPipeShape {
@@ -411,7 +413,7 @@ struct FwdPipeShape {
   static_assert(KWIN + VWIN <= (D / 16) * (BK / 32), "one copy per first-phase MFMA at most");
 };
 
-template <int D, int DV, int MASK>
+template <int D, int DV, int MASK, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pipe_kernel(FwdParams p) {
   using S = FwdPipeShape<D, DV>;
   // Four distinct LDS objects, so that the compiler can tell reads of one
@@ -606,6 +608,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     m_run = m_new;
   };
 
+  // Dropout draws.  Register r of block kb holds key 32 kb + 8 g + 4 hh + e
+  // (g = r / 4, e = r % 4) of the tile for this lane's query: key block
+  // k0 / 4 + 8 kb + 2 g + hh, key e in it.  The quad's lanes hold the four
+  // queries of one query block, so the quad needs the 8 calls (kb, g) of its
+  // half; quad position e' draws calls 2 e' and 2 e' + 1 (counter (key / 4,
+  // query / 4, unit, 0)), packed as bit 8 (key % 4) + 4 + query % 4, in the
+  // previous step's second phase, where the vector ALUs are otherwise idle.
+  // The weights read them across the quad where they are applied.
+  uint32_t dc[2][4] = {}, dm[2] = {0u, 0u};
+  const uint32_t dsh = 4u + (uint32_t)(lane & 3);
+  const KeepConsts kq = keep_consts(p.drop.p8);
+  auto draw_init = [&](int key0) {  // first key of the tile
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = 2 * (lane & 3) + j, kb = c >> 2, g = c & 3;  // call (kb, g) of this lane
+      dc[j][0] = ((uint32_t)key0 >> 2) + 8u * (uint32_t)kb + 2u * (uint32_t)g + (uint32_t)hh;
+      dc[j][1] = (uint32_t)q >> 2;
+      dc[j][2] = (uint32_t)unit;
+      dc[j][3] = 0u;
+      dm[j] = 0u;
+    }
+  };
+  auto draw_item = [&](int t) {  // call t / 14: rounds 0..9, then the keep bits of its four words
+    const int j = t / 14, k = t % 14;
+    if (k < 10) philox_round(dc[j][0], dc[j][1], dc[j][2], dc[j][3], p.drop.seed_lo, p.drop.seed_hi, k);
+    else dm[j] = pack_keep(dm[j], keep_flags(dc[j][k - 10], kq), k - 10);
+  };
+  auto call_bits = [&](int c) -> uint32_t {  // the keep bits of call c = 4 kb + g of the quad
+    const uint32_t x = dm[c & 1];
+    switch (c >> 1) {
+      case 0: return quad_bcast<0>(x);
+      case 1: return quad_bcast<1>(x);
+      case 2: return quad_bcast<2>(x);
+      default: return quad_bcast<3>(x);
+    }
+  };
+  auto keep_mask = [&](uint32_t bits, int r) -> uint32_t {  // all ones iff register r is kept
+    return (uint32_t)__builtin_amdgcn_sbfe((int)bits, dsh + 8u * (uint32_t)(r & 3), 1u);
+  };
+
   // This split's share of the key tiles [0, kt_end): [t0, kt_end).
   int t0 = 0;
   if (p.splits > 1) {
@@ -623,6 +665,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vm();
     __syncthreads();
     f32x16 sa[S::NKB], sb[S::NKB];
+    if constexpr (DROP) {  // the first tile's calls
+      draw_init(t0 * S::BK);
+#pragma unroll
+      for (int tt = 0; tt < 28; ++tt) draw_item(tt);
+    }
     scores(sa, kbuf0);
     if (tile_class(t0) == kTilePartial) mask_tile(sa, t0);
     row_max(sa);
@@ -695,7 +742,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       auto weights_f = [&](int pr) {
         const int kb = pr / 8, r = 2 * (pr % 8);
         ls[pr % 4] = pr < 4 ? pe[pr][0] + pe[pr][1] : ls[pr % 4] + (pe[pr][0] + pe[pr][1]);
-        pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(pe[pr][0], pe[pr][1]);
+        if constexpr (DROP) {  // the PV product takes the kept weights; L the sum of all
+          const uint32_t bits = call_bits(4 * kb + r / 4);
+          const float z0 = __uint_as_float(__float_as_uint(pe[pr][0]) & keep_mask(bits, r));
+          const float z1 = __uint_as_float(__float_as_uint(pe[pr][1]) & keep_mask(bits, r + 1));
+          pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(z0, z1);
+        } else {
+          pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(pe[pr][0], pe[pr][1]);
+        }
       };
       auto weights = [&](int pr, float neg_m) {
         weights_e(pr, neg_m);
@@ -742,7 +796,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       l_run += lt;
 
       __builtin_amdgcn_s_setprio(0);
-      // ---- phase B: O^T += V^T P^T(t0) on the MFMA pipe ----
+      // ---- phase B: O^T += V^T P^T(t0) on the MFMA pipe (and t1's draws) ----
+      if constexpr (DROP) draw_init(k1);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -751,6 +806,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (i + 2 < NP) {
           vfr[2 * (i % 2)] = vread(i + 2, 0);
           vfr[2 * (i % 2) + 1] = vread(i + 2, 1);
+        }
+        if constexpr (DROP) {  // t1's two calls: 28 items over the NP slices
+#pragma unroll
+          for (int tt = i * 28 / NP; tt < (i + 1) * 28 / NP; ++tt) draw_item(tt);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -775,7 +834,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const float l_tot = sum_halves(l_run);
   const float l_norm = l_tot;
-  const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
+  const float inv = l_norm > 0.f ? (DROP ? p.drop.keep_inv : 1.f) / l_norm : 0.f;
   if (p.splits > 1) {  // this split's normalised output and L, for fwd_merge_kernel
     if (qvalid) {
       const int64_t row = ((int64_t)split * p.B * p.H + unit) * n + q;
@@ -814,12 +873,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <bool BF16, int D, int DV, int MASK>
 static int launch_one(const FwdParams& p, hipStream_t st) {
   dim3 grid((unsigned)p.grid_pad), block(256);
-  if (p.drop.p8 != 0)
+  if constexpr (BF16 && (D == 64 || D == 128) && (DV == 64 || DV == 128)) {
+    if (p.drop.p8 != 0) hipLaunchKernelGGL((fwd_pipe_kernel<D, DV, MASK, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((fwd_pipe_kernel<D, DV, MASK, false>), grid, block, 0, st, p);
+  } else if (p.drop.p8 != 0) {
     hipLaunchKernelGGL((fwd_kernel<BF16, D, DV, MASK, true>), grid, block, 0, st, p);
-  else if constexpr (BF16 && (D == 64 || D == 128) && (DV == 64 || DV == 128))
-    hipLaunchKernelGGL((fwd_pipe_kernel<D, DV, MASK>), grid, block, 0, st, p);
-  else
+  } else {
     hipLaunchKernelGGL((fwd_kernel<BF16, D, DV, MASK>), grid, block, 0, st, p);
+  }
   return (int)hipGetLastError();
 }
 

@@ -126,9 +126,10 @@ struct MapParams {
 // Launchers return a hipError_t value as int (0 = success).
 int launch_fwd(const FwdParams& p, int bf16, int d, int v, int mask_mode, void* stream);
 // Key-range splits the forward uses for this problem (1 = none; > 1 only
-// with the pipelined bf16 kernel, for few query tiles against many key tiles).
-inline int fwd_splits(int bf16, int64_t d, int64_t v, int64_t units, int64_t tq, int64_t tk, uint32_t p8) {
-  if (!bf16 || p8 != 0 || !((d == 64 || d == 128) && (v == 64 || v == 128))) return 1;
+// with the pipelined bf16 kernel, for few query tiles against many key tiles;
+// with dropout too, since every split replays its keys' decisions).
+inline int fwd_splits(int bf16, int64_t d, int64_t v, int64_t units, int64_t tq, int64_t tk) {
+  if (!bf16 || !((d == 64 || d == 128) && (v == 64 || v == 128))) return 1;
   const int64_t wgs = units * tq;
   if (wgs >= 256) return 1;
   int64_t s = (512 + wgs - 1) / wgs;

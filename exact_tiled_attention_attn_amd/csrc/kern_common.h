@@ -357,25 +357,44 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t bid, int64_t grid_pad, in
 // the round key is the key plus r times the Weyl increments.
 __device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
                                              uint32_t k1, int r) {
-  const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-  const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-  const uint32_t n0 = hi1 ^ c1 ^ (k0 + (uint32_t)r * 0x9E3779B9u), n2 = hi0 ^ c3 ^ (k1 + (uint32_t)r * 0xBB67AE85u);
+  // Each 64-bit product is one v_mad_u64_u32 (about 1.5x the round rate of
+  // separate high and low multiplies), each three-way XOR one v_bitop3_b32
+  // (truth table 0x96).
+  const uint64_t m0 = (uint64_t)0xD2511F53u * c0, m1 = (uint64_t)0xCD9E8D57u * c2;
+  const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(m1 >> 32), c1, k0 + (uint32_t)r * 0x9E3779B9u, 0x96);
+  const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(m0 >> 32), c3, k1 + (uint32_t)r * 0xBB67AE85u, 0x96);
   c0 = n0;
-  c1 = lo1;
+  c1 = (uint32_t)m1;
   c2 = n2;
-  c3 = lo0;
+  c3 = (uint32_t)m0;
 }
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
                                               uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) philox_round(c0, c1, c2, c3, k0, k1, r);
 }
-// Keep bits of one output word of a call: bit b set iff byte b >= p8.
-__device__ __forceinline__ uint32_t keep_bits4(uint32_t w, uint32_t p8) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) m |= (((w >> (8 * b)) & 0xFFu) >= p8 ? 1u : 0u) << b;
-  return m;
+// Keep flags of the four bytes of one output word of a call, all at once.
+// With q = 256 - p8 (p8 in [1, 255]), byte x >= p8 iff x + q carries out of
+// 8 bits, and that carry is the majority of bit 7 of x, bit 7 of q and the
+// carry out of the low 7 bits, which one add forms for all four bytes
+// (their low 7-bit sums stay below 256).  keep_flags sets bit 8 b + 7 iff
+// byte b is kept; its other bits are unspecified.
+struct KeepConsts {
+  uint32_t lo;  // the low 7 bits of q in every byte
+  uint32_t hi;  // bit 7 of q in every byte
+};
+__device__ __forceinline__ KeepConsts keep_consts(uint32_t p8) {
+  const uint32_t q = 256u - p8;
+  return KeepConsts{(q & 0x7Fu) * 0x01010101u, (q & 0x80u) ? 0x80808080u : 0u};
+}
+__device__ __forceinline__ uint32_t keep_flags(uint32_t w, KeepConsts k) {
+  const uint32_t s = (w & 0x7F7F7F7Fu) + k.lo;
+  return __builtin_amdgcn_bitop3_b32(w, s, k.hi, 0xE8);  // bitwise majority
+}
+// Adds word r's flags f to the packed keep bits m of a call: bit
+// 8 (j % 4) + 4 + i % 4 is set iff pair (i, j) is kept (word r = i % 4).
+__device__ __forceinline__ uint32_t pack_keep(uint32_t m, uint32_t f, int r) {
+  return m | ((f >> (3 - r)) & (0x10101010u << r));
 }
 
 // Keep bits of the pairs (i, j0 + e), e = 0..3, for j0 % 4 == 0: bit e set

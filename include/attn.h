@@ -127,9 +127,9 @@ typedef struct {
    * (j / 4, i / 4, u, 0) and key (dropout_seed mod 2^32, dropout_seed div
    * 2^32).  O_i = sum_j P_ij Z_ij V_j * 256 / (256 - p8), with P the
    * undropped softmax, whose L is returned; attn_bwd with the same seed and
-   * dropout_p regenerates Z.  The forward runs on the register-staged
-   * kernel; the backward's key-tile-outer and deterministic dQ kernels
-   * replay Z in their pipelined bf16 forms where those apply. */
+   * dropout_p regenerates Z.  Every forward and backward kernel draws Z
+   * itself, the pipelined bf16 ones included, so dropout changes neither
+   * the kernels chosen nor the key-range splits. */
   double dropout_p;
   uint64_t dropout_seed;
 } attn_problem;

@@ -192,8 +192,8 @@ def test_forward_split_workspace():
     rows = S * 2 * 100
     align = lambda x: -(-x // 256) * 256  # noqa: E731
     assert wsize(p, 0) == (0, align(rows * 128 * 4) + align(rows * 4))
-    p.dropout_p = 0.2  # dropout runs on the register-staged kernel: no splits
-    assert wsize(p, 0) == (0, 0)
+    p.dropout_p = 0.2  # dropout splits the same way (each split replays its keys' decisions)
+    assert wsize(p, 0) == (0, align(rows * 128 * 4) + align(rows * 4))
     p.dropout_p, p.nk = 0.0, 1000  # 16 key tiles: four per split at most
     for name, w in (("sk", 128), ("sv", 128)):
         arr = getattr(p, name)

@@ -8,8 +8,8 @@ page, reverse procedure): the kernels regenerate each keep decision from
 * O, L and dQ, dK, dV (both dQ paths) equal the oracle's dropout forward
   and VJP taken with the oracle's own mask, within the dtype tolerance;
 * the same seed gives bitwise the same results, another seed other ones;
-* with few query rows against many keys the dQ kernel's key-range splits
-  carry the replayed mask too;
+* with few query rows against many keys the forward's and the dQ
+  kernel's key-range splits carry the mask too;
 * the autograd wrapper passes the dropout through to the backward.
 """
 
@@ -100,9 +100,9 @@ def test_dropout_parity(dtype, d, v, mask):
 @pytest.mark.parametrize("d,v", [(128, 128), (64, 128)])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_dropout_with_key_range_splits(d, v, mask):
-    """Few query rows against many keys (the dQ kernel splits its key
-    range): the replayed mask through the split dQ partials and their merge,
-    bitwise reproducible, against the oracle."""
+    """Few query rows against many keys (the forward and the dQ kernel split
+    their key range): the mask through the split O and dQ partials and their
+    merges, bitwise reproducible, against the oracle."""
     import exact_tiled_attention_attn_amd as E
 
     H, n, nk, p, seed = 2, 70, 3000, 0.25, 99
@@ -117,6 +117,7 @@ def test_dropout_with_key_range_splits(d, v, mask):
     o, L = E.fwd(q, k, val, c, mask, None, **kw)
     pb = E.make_problem(q, k, val, o, c, mask, None, True, off, p, seed)
     assert E.workspace_size(pb, True) >= 2 * 4 * H * 128 + 2 * 4 * H * n * d, "dQ key-range splits expected"
+    assert E.workspace_size(pb, False) >= 2 * 4 * H * n * (v + 1), "forward key-range splits expected"
     det = E.bwd(q, k, val, o, g, L, c, mask, None, deterministic=True, **kw)
     det2 = E.bwd(q, k, val, o, g, L, c, mask, None, deterministic=True, **kw)
     torch.cuda.synchronize()
