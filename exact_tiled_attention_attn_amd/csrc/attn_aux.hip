@@ -122,7 +122,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_
       const float Lv = p.L[unit * p.n + i];
       l2 = Lv == -INFINITY ? INFINITY : Lv * kLog2e;
     }
-    p.Dn[row] = -acc;
+    // With dropout -D P(keep): the dropout kernels start dP from it and
+    // apply 1 / P(keep) at the end (P(keep) = 1 - p8 / 256, exact in fp32).
+    p.Dn[row] = -acc * ((float)(256u - p.drop.p8) * (1.f / 256.f));
     p.L2[row] = l2;
   }
   // Clear the dQ accumulator (grid-stride over float4s).

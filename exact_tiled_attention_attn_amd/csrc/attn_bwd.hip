@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
             if constexpr (DROP) {
               const bool z = (keep >> e) & 1u;
               sc[r] = z ? pv : 0.f;
-              dp[r] = pv * ((z ? dp[r] * p.drop.keep_inv : 0.f) - d4[e]);
+              dp[r] = pv * ((z ? dp[r] : 0.f) - d4[e]) * p.drop.keep_inv;  // d4 = D P(keep)
             } else {
               sc[r] = pv;
               dp[r] = pv * (dp[r] - d4[e]);

@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
             }
             if constexpr (DROP) {
               const bool z = (keep >> ((r + e) & 3)) & 1u;
-              ds[e] = pv * ((z ? dp[kb][r + e] * p.drop.keep_inv : 0.f) - Dq);
+              ds[e] = pv * ((z ? dp[kb][r + e] : 0.f) - Dq) * p.drop.keep_inv;  // Dq = D P(keep)
             } else {
               ds[e] = pv * (dp[kb][r + e] - Dq);
             }

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   if constexpr (MASK == kMaskBitmask) mbase = p.mask + b * p.mask_sb + h * p.mask_sh;
 
   // Per-lane row statistics of the two halves: L log2(e) (+inf for rows past
-  // n or with L = -inf, so that p = 0) and -D.
+  // n or with L = -inf, so that p = 0) and -D (with dropout -D P(keep)).
   float l2[2], dn[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -182,9 +182,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dinit[u][r] = dn[u];
   }
-  // Dropout (DROP): dS = P (Z dP / keep - D), the dP accumulators starting
-  // from zero, with the keep decisions Z of kern_common.h regenerated per
-  // 32-key chunk.  Per half u, lane (hh, quad position e) draws key block
+  // Dropout (DROP): dS = P (Z dP / keep - D) = P (Z dP - keep D) / keep.  The
+  // dP accumulators start from -keep D as they start from -D without
+  // dropout, a dropped pair takes -keep D instead (one bit select), and the
+  // 1 / keep joins c at the end.  The keep decisions Z of kern_common.h are
+  // regenerated per 32-key chunk.  Per half u, lane (hh, quad position e) draws key block
   // 4 hh + e of the chunk for its quad's query block (counter (key / 4,
   // query / 4, unit, 0)); the call's 16 keep bits are packed as bit
   // 8 (key % 4) + 4 + query % 4.  Register r = 4 g + e' of a half holds key
@@ -229,7 +231,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     const int g = r >> 2, e = r & 3;
     return (uint32_t)__builtin_amdgcn_sbfe((int)dM[u][g >> 1][e], dsh + 16u * (uint32_t)(g & 1), 1u);
   };
-  const float keep_inv = p.drop.keep_inv;
 
   // ---- tile fills ----------------------------------------------------------
   // Wave w copies a contiguous run of 1 KB windows of each tile: KB = KWINS /
@@ -403,8 +404,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (s == 0) {
-          if constexpr (DROP) mfma_vz(dp[u], a, of[u][s]);
-          else mfma_vc(dp[u], a, of[u][s], dinit[u]);
+          mfma_vc(dp[u], a, of[u][s], dinit[u]);
         } else {
           mfma_vacc(dp[u], a, of[u][s]);
         }
@@ -463,11 +463,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     auto w2 = [&](int pr) { pe[pr][1] = fast_exp2(pt[pr]); };
     auto w3 = [&](int pr) {
       const int u = pr >> 3, r = 2 * (pr & 7);
-      if constexpr (DROP) {  // dp = dP: dS = P Z dP / keep + P (-D)
-        const float z0 = __uint_as_float(__float_as_uint(pe[pr][0]) & keep_mask(u, r));
-        const float z1 = __uint_as_float(__float_as_uint(pe[pr][1]) & keep_mask(u, r + 1));
-        sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(__builtin_fmaf(z0, keep_inv * dp[u][r], pe[pr][0] * dn[u]),
-                                                  __builtin_fmaf(z1, keep_inv * dp[u][r + 1], pe[pr][1] * dn[u]));
+      if constexpr (DROP) {  // dp = dP - keep D: keep dS = P (Z ? dp : -keep D)
+        const uint32_t m0 = keep_mask(u, r), m1 = keep_mask(u, r + 1);
+        const float v0 = __uint_as_float((__float_as_uint(dp[u][r]) & m0) | (__float_as_uint(dn[u]) & ~m0));
+        const float v1 = __uint_as_float((__float_as_uint(dp[u][r + 1]) & m1) | (__float_as_uint(dn[u]) & ~m1));
+        sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0] * v0, pe[pr][1] * v1);
       } else {
         sk[u][r >> 3][(r >> 1) & 3] = pack_bf16x2(pe[pr][0] * dp[u][r], pe[pr][1] * dp[u][r + 1]);
       }
@@ -495,8 +495,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
       } else {
         const int vi = i - si;
         if (vi == 0) {
-          if constexpr (DROP) mfma_vz(ndp[u], afr[i % PF], of[u][0]);
-          else mfma_vc(ndp[u], afr[i % PF], of[u][vi], dinit[u]);
+          mfma_vc(ndp[u], afr[i % PF], of[u][vi], dinit[u]);
         } else {
           mfma_vacc(ndp[u], afr[i % PF], of[u][vi]);
         }
@@ -607,6 +606,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   }
   count_tiles(p.tile_count_dq, ntiles);
 
+  if constexpr (DROP) {  // the 1 / keep of dS
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < S::NDB; ++i) dq[u][i] *= p.drop.keep_inv;
+  }
   if (p.dq_splits > 1) {  // this split's unscaled fp32 partial, for bwd_dq_merge_kernel
 #pragma unroll
     for (int u = 0; u < 2; ++u) {

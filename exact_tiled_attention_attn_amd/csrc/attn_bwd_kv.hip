@@ -38,8 +38,9 @@
 //
 // Dropout (DROP; alphabetamath page, reverse procedure, closing remark: the
 // reverse pass replays the forward's realised mask): with keep decisions Z
-// and keep = P(kept), dV^T += dO^T (P o Z) (times 1 / keep at the end) and
-// dS = P (Z dP / keep - D); the dP accumulators then start from zero.  The
+// and keep = P(kept), dV^T += dO^T (P o Z) and keep dS = P (Z dP - keep D)
+// (both times 1 / keep at the end): the dP accumulators start from the
+// stored -keep D, and a dropped pair takes -keep D instead of dP.  The
 // decisions are the counter-based draws of kern_common.h, regenerated: the
 // chunk's 32 rows form 8 row blocks of 4, a lane's key one key block of 4
 // with its quad, so the 8 lanes sharing a key block (a quad in each half)
@@ -318,8 +319,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     for (int s = 0; s < S::NVF; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + orb + 32 * s);
       if (s == 0) {
-        if constexpr (DROP) mfma_vz(dp, a, vf[s]);
-        else mfma_vc(dp, a, vf[s], dn);
+        mfma_vc(dp, a, vf[s], dn);
       } else {
         mfma_vacc(dp, a, vf[s]);
       }
@@ -416,7 +416,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     const int g = r >> 2, e = r & 3;
     return (uint32_t)__builtin_amdgcn_sbfe((int)dM[g >> 1][e], dsh + 2u * (uint32_t)(g & 1), 1u);
   };
-  const float keep_inv = p.drop.keep_inv;
 
   // One pipeline step for chunk (st, c): cur holds its S and dP (masked);
   // nxt receives S and dP of the next chunk (stage nst, chunk nc), computed
@@ -439,7 +438,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // first kPrefetchA operands of the following step (its stage is already
   // visible), which then starts without waiting for them.
   bf16x8 afr[kPrefetchA];
-  // With DROP, dcur is -D of this chunk and nrow0 the first row of the next.
+  // With DROP, dcur is -keep D of this chunk and nrow0 the first row of the next.
   auto step = [&](auto dofill, f32x16& sc, f32x16& dp, f32x16& nsc, f32x16& ndp, int st, int c, int nst, int nc,
                   const f32x16& dni, auto dload, f32x16& dnx, auto hook, auto pre_a, const f32x16& dcur, int nrow0) {
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS + qtb;
@@ -488,11 +487,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     };
     auto weights_f = [&](int pr) {
       const int r = 2 * pr;
-      if constexpr (DROP) {  // dp = dP: dS = P Z dP / keep + P (-D)
-        const float z0 = __uint_as_float(__float_as_uint(pe[pr][0]) & keep_mask(r));
-        const float z1 = __uint_as_float(__float_as_uint(pe[pr][1]) & keep_mask(r + 1));
-        const float d0 = __builtin_fmaf(z0, keep_inv * dp[r], pe[pr][0] * dcur[r]);
-        const float d1 = __builtin_fmaf(z1, keep_inv * dp[r + 1], pe[pr][1] * dcur[r + 1]);
+      if constexpr (DROP) {  // dp = dP - keep D: keep dS = P (Z ? dp : -keep D)
+        const uint32_t m0 = keep_mask(r), m1 = keep_mask(r + 1);
+        const float z0 = __uint_as_float(__float_as_uint(pe[pr][0]) & m0);
+        const float z1 = __uint_as_float(__float_as_uint(pe[pr][1]) & m1);
+        const float v0 = __uint_as_float((__float_as_uint(dp[r]) & m0) | (__float_as_uint(dcur[r]) & ~m0));
+        const float v1 = __uint_as_float((__float_as_uint(dp[r + 1]) & m1) | (__float_as_uint(dcur[r + 1]) & ~m1));
+        const float d0 = pe[pr][0] * v0, d1 = pe[pr][1] * v1;
         pk[r >> 3][(r >> 1) & 3] = pack_bf16x2(z0, z1);
         sk[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
       } else {
@@ -512,8 +513,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         else mfma_vacc(nsc, afr[i % PF], kf[si]);
       } else {
         if (i - si == 0) {
-          if constexpr (DROP) mfma_vz(ndp, afr[i % PF], vf[0]);
-          else mfma_vc(ndp, afr[i % PF], vf[i - si], dni);
+          mfma_vc(ndp, afr[i % PF], vf[i - si], dni);
         } else {
           mfma_vacc(ndp, afr[i % PF], vf[i - si]);
         }
@@ -650,8 +650,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c0 = db * 32 + 8 * g + 4 * hh;
-        const float x0 = dk[db][4 * g] * p.scale, x1 = dk[db][4 * g + 1] * p.scale;
-        const float x2 = dk[db][4 * g + 2] * p.scale, x3 = dk[db][4 * g + 3] * p.scale;
+        const float sk = DROP ? p.scale * p.drop.keep_inv : p.scale;
+        const float x0 = dk[db][4 * g] * sk, x1 = dk[db][4 * g + 1] * sk;
+        const float x2 = dk[db][4 * g + 2] * sk, x3 = dk[db][4 * g + 3] * sk;
         *reinterpret_cast<u32x2*>(dKp + c0 * 2) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
       }
 #pragma unroll

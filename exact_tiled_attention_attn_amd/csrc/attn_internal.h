@@ -73,7 +73,7 @@ struct BwdParams {
   const void* O;
   const void* dO;
   const float* L;
-  float* Dn;     // -D_i = -<dO_i, O_i>, fp32 [B, H, n_pad]
+  float* Dn;     // -D_i = -<dO_i, O_i> (times P(keep) with dropout), fp32 [B, H, n_pad]
   float* L2;     // L_i log2(e) (+inf where L_i = -inf), fp32 [B, H, n_pad]
   int64_t n_pad;  // row stride of Dn and L2: n rounded up to kRowPad; rows >= n hold 0 and L2 = +inf
   float* dQacc;  // fp32 [B, H, n, d] accumulator (unscaled by c)
