@@ -635,6 +635,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (k < 10) philox_round(dc[j][0], dc[j][1], dc[j][2], dc[j][3], p.drop.seed_lo, p.drop.seed_hi, k);
     else dm[j] = pack_keep(dm[j], keep_flags(dc[j][k - 10], kq), k - 10);
   };
+  // The draw state is pinned after each slice of items: otherwise the
+  // compiler sinks the draws out of the second phase to their first use.
+  auto draw_pin = [&]() {
+    asm volatile("" : "+v"(dc[0][0]), "+v"(dc[0][1]), "+v"(dc[0][2]), "+v"(dc[0][3]), "+v"(dc[1][0]),
+                 "+v"(dc[1][1]), "+v"(dc[1][2]), "+v"(dc[1][3]), "+v"(dm[0]), "+v"(dm[1]));
+  };
   auto call_bits = [&](int c) -> uint32_t {  // the keep bits of call c = 4 kb + g of the quad
     const uint32_t x = dm[c & 1];
     switch (c >> 1) {
@@ -810,6 +816,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (DROP) {  // t1's two calls: 28 items over the NP slices
 #pragma unroll
           for (int tt = i * 28 / NP; tt < (i + 1) * 28 / NP; ++tt) draw_item(tt);
+          draw_pin();
         }
       }
       __builtin_amdgcn_sched_barrier(0);
