@@ -525,6 +525,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   float m_run = -INFINITY, l_run = 0.f;
+  float neg_m = 0.f;  // exponent offset of the weights: -m_run, 0 while m_run = -inf
+  float spec_lim = 0.f;  // kSpecBound, 0 while m_run = -inf (any weight then takes the exact path)
   f32x16 o[S::NVB];
 #pragma unroll
   for (int vb = 0; vb < S::NVB; ++vb) o[vb] = f32x16{};
@@ -556,6 +558,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             sc[kb][r] = __uint_as_float((__float_as_uint(sc[kb][r]) & keep) | (0xFF800000u & ~keep));
           }
         }
+        return;
+      }
+    }
+    if constexpr (MASK == kMaskCausal) {
+      if (k0 + S::BK <= nk) {  // every key of the tile exists: key <= q + coff alone decides
+        const int lim = q + coff - k0 - 4 * hh;  // register offset kk - 4 hh must not exceed it
+#pragma unroll
+        for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sc[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= lim ? sc[kb][r] : -INFINITY;
         return;
       }
     }
@@ -606,6 +619,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     l_run *= alpha;
     m_run = m_new;
+    neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    spec_lim = m_run == -INFINITY ? 0.f : kSpecBound;
   };
 
   // Dropout draws.  Register r of block kb holds key 32 kb + 8 g + 4 hh + e
@@ -761,7 +776,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         weights_e(pr, neg_m);
         weights_f(pr);
       };
-      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       bf16x8 kfr[PF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) kfr[i] = kread(i);
@@ -789,13 +803,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       __builtin_amdgcn_sched_barrier(0);
       float lt = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      if (__ballot(lt > kSpecBound || (m_run == -INFINITY && lt > 0.f)) != 0) {  // wave-uniform, rare
+      if (__ballot(lt > spec_lim) != 0) {  // wave-uniform, rare
         row_max(cur);
         if (__ballot(raise) != 0) {
           apply_rescale();
-          const float neg_m2 = (m_run == -INFINITY) ? 0.f : -m_run;
 #pragma unroll
-          for (int pr = 0; pr < NPAIR; ++pr) weights(pr, neg_m2);
+          for (int pr = 0; pr < NPAIR; ++pr) weights(pr, neg_m);
           lt = (ls[0] + ls[1]) + (ls[2] + ls[3]);
         }
       }
