@@ -733,7 +733,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // apart by scheduling barriers.
       constexpr int NS = S::NQF * S::NKB;      // score MFMAs
       constexpr int NP = S::NVB * S::BK / 16;  // PV MFMAs
-      constexpr int PF = 4;                    // K reads in flight
+      constexpr int PF = MASK == kMaskBitmask ? 4 : 8;  // K reads in flight (fewer where the mask words need registers)
       constexpr int NPAIR = S::NKB * 8;        // weight pairs of the tile
       auto kread = [&](int i) {  // K fragment of score MFMA i (ks = i / NKB, kb = i % NKB)
         return lds_read_b128(knxt, kbase + 32 * (i % S::NKB) * S::KS + 32 * (i / S::NKB));
