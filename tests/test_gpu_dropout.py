@@ -98,7 +98,7 @@ def test_dropout_parity(dtype, d, v, mask):
 
 
 @pytest.mark.parametrize("d,v", [(128, 128), (64, 128)])
-@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("mask", ["none", "causal", "bitmask"])
 def test_dropout_with_key_range_splits(d, v, mask):
     """Few query rows against many keys (the forward and the dQ kernel split
     their key range): the mask through the split O and dQ partials and their
@@ -110,16 +110,21 @@ def test_dropout_with_key_range_splits(d, v, mask):
     rng = np.random.default_rng(d + v + nk)
     Q, K, V, G = (W.round_bf16(rng.standard_normal((1, H, r, x), dtype=np.float32))
                   for r, x in ((n, d), (nk, d), (nk, v), (n, v)))
-    A = W.causal_allowed(n, nk=nk, offset=off) if mask == "causal" else None
+    A, mdev = None, None
+    if mask == "causal":
+        A = W.causal_allowed(n, nk=nk, offset=off)
+    elif mask == "bitmask":  # a quarter of the pairs
+        A = rng.random((n, nk)) < 0.25
+        mdev = torch.from_numpy(W.pack_bits(np.stack([A] * H)).view(np.int32)).to(DEV)
     q, k, val, g = (_dev(x, "bf16") for x in (Q, K, V, G))
     c = 1 / np.sqrt(d)
     kw = dict(dropout_p=p, dropout_seed=seed, causal_offset=off)
-    o, L = E.fwd(q, k, val, c, mask, None, **kw)
-    pb = E.make_problem(q, k, val, o, c, mask, None, True, off, p, seed)
+    o, L = E.fwd(q, k, val, c, mask, mdev, **kw)
+    pb = E.make_problem(q, k, val, o, c, mask, mdev, True, off, p, seed)
     assert E.workspace_size(pb, True) >= 2 * 4 * H * 128 + 2 * 4 * H * n * d, "dQ key-range splits expected"
     assert E.workspace_size(pb, False) >= 2 * 4 * H * n * (v + 1), "forward key-range splits expected"
-    det = E.bwd(q, k, val, o, g, L, c, mask, None, deterministic=True, **kw)
-    det2 = E.bwd(q, k, val, o, g, L, c, mask, None, deterministic=True, **kw)
+    det = E.bwd(q, k, val, o, g, L, c, mask, mdev, deterministic=True, **kw)
+    det2 = E.bwd(q, k, val, o, g, L, c, mask, mdev, deterministic=True, **kw)
     torch.cuda.synchronize()
     for x, y in zip(det, det2):
         assert torch.equal(x, y)
