@@ -239,11 +239,13 @@ def fwd(q, k, v, scale, mask_mode="none", mask=None, *, out=None, lse=None, work
 
 
 def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=None, dv=None,
-        workspace=None, deterministic=False, causal_offset=0, dropout_p=0.0, dropout_seed=0):
+        workspace=None, deterministic=True, causal_offset=0, dropout_p=0.0, dropout_seed=0):
     """dQ, dK, dV (dtype of q) from the forward's O and L and the upstream dO.
 
-    ``deterministic`` selects the query-tile-outer dQ kernel (bitwise
-    reproducible) instead of fp32 atomics in the key-tile-outer kernel.
+    ``deterministic`` (the default) selects the query-tile-outer dQ kernel
+    (bitwise reproducible, and the faster path: fp32 atomic adds run at
+    about 1.3 TB/s on MI355X, which doubles the backward); False selects
+    fp32 atomics in the key-tile-outer kernel.
     """
     lib = load_library()
     _on_gpu("q", q)
@@ -273,7 +275,7 @@ def bwd(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=
 
 
 def bwd_noalloc(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=None, dk=None, dv=None,
-                deterministic=False, causal_offset=0, dropout_p=0.0, dropout_seed=0):
+                deterministic=True, causal_offset=0, dropout_p=0.0, dropout_seed=0):
     """attn_bwd_noalloc: bwd() with the library's static scratch as the
     workspace.  The library allocates nothing; dQ, dK, dV are the caller's
     (allocated here only when not given)."""

@@ -57,7 +57,7 @@ def run_gpu(prob: W.Problem, want_bwd: bool = True):
     o, L = E.fwd(q, k, v, w.scale, w.mask, m)
     out = {"O": o, "L": L}
     if want_bwd:
-        dq, dk, dv = E.bwd(q, k, v, o, g, L, w.scale, w.mask, m)
+        dq, dk, dv = E.bwd(q, k, v, o, g, L, w.scale, w.mask, m, deterministic=False)
         out.update(dQ=dq, dK=dk, dV=dv)
         dq, dk, dv = E.bwd(q, k, v, o, g, L, w.scale, w.mask, m, deterministic=True)
         out.update(dQ_det=dq, dK_det=dk, dV_det=dv)

@@ -73,7 +73,7 @@ def test_dropout_parity(dtype, d, v, mask):
     c = 1 / np.sqrt(d)
     kw = dict(dropout_p=p, dropout_seed=seed)
     o, L = E.fwd(q, k, val, c, mask, mdev, **kw)
-    grads = {"atomic": E.bwd(q, k, val, o, g, L, c, mask, mdev, **kw),
+    grads = {"atomic": E.bwd(q, k, val, o, g, L, c, mask, mdev, deterministic=False, **kw),
              "det": E.bwd(q, k, val, o, g, L, c, mask, mdev, deterministic=True, **kw)}
     o2, L2 = E.fwd(q, k, val, c, mask, mdev, **kw)
     o3, _ = E.fwd(q, k, val, c, mask, mdev, dropout_p=p, dropout_seed=seed + 1)

@@ -103,7 +103,7 @@ def _run(i, dtype, d, v, n, nk, mask, off, p, scale, wide):
     q, k, val, g = (_dev(x, dtype) for x in (Q, K, V, G))
     kw = dict(causal_offset=off, dropout_p=p, dropout_seed=seed)
     o, L = E.fwd(q, k, val, scale, mask, mdev, **kw)
-    res = {"atomic": E.bwd(q, k, val, o, g, L, scale, mask, mdev, **kw),
+    res = {"atomic": E.bwd(q, k, val, o, g, L, scale, mask, mdev, deterministic=False, **kw),
            "det": E.bwd(q, k, val, o, g, L, scale, mask, mdev, deterministic=True, **kw)}
     torch.cuda.synchronize()
     got = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
