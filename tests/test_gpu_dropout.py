@@ -158,3 +158,68 @@ def test_autograd_passes_dropout_through():
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), ro)
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(val.grad, dv)
+
+
+@pytest.mark.parametrize("p", [1 / 256, 0.1, 0.5, 255 / 256])
+@pytest.mark.parametrize("d", [128, 64])
+def test_pipelined_kernels_keep_decisions_bit_exact(p, d):
+    """The pipelined kernels' own keep decisions, read off outputs built to
+    expose them, equal the oracle's bit for bit: all scores 0 (Q = 0) and a
+    bitmask that allows only a 128-key window KW (keys 1990..2117, across
+    three 64-key tiles) to every row, so P = 1/128 on the window, then
+      forward: V_j = e_(j - kw)    -> O_i[c] = Z_i,kw+c / (128 keep)
+      dK/dV:   dO_i = e_(i - rw) on a 128-row window RW (rows 1003..1130)
+                                   -> dV_j[c] = Z_rw+c,j / (128 keep)
+      dQ:      K_j = e_(j - kw), V_j = dO_i = e_0, so dP = 1
+                                   -> dQ_i[c] = (Z_i,kw+c / keep - D_i) / 128.
+    Both units, with the forward's and the dQ kernel's key-range splits."""
+    import exact_tiled_attention_attn_amd as E
+
+    H, n, nk, v, seed = 2, 1200, 2200, 128, 0xC0FFEE123456789
+    kw, rw = 1990, 1003
+    p8 = dropout.p8_of(p)
+    keep = (256 - p8) / 256.0
+    A = np.zeros((n, nk), bool)
+    A[:, kw:kw + 128] = True
+    mdev = torch.from_numpy(W.pack_bits(np.stack([A] * H)).view(np.int32)).to(DEV)
+    kw_ = dict(dropout_p=p, dropout_seed=seed)
+    zeros = lambda *s: np.zeros((1, H) + s, np.float32)  # noqa: E731
+    Z = [dropout.keep_mask(seed, h, n, nk, p8) for h in range(H)]
+
+    # Forward: one-hot V rows on the window.
+    Q, K, V = zeros(n, d), zeros(nk, d), zeros(nk, v)
+    V[0, :, kw + np.arange(128), np.arange(128)] = 1.0
+    q, k, val = (_dev(x, "bf16") for x in (Q, K, V))
+    o, L = E.fwd(q, k, val, 1.0, "bitmask", mdev, **kw_)
+    torch.cuda.synchronize()
+    ofl = o.float().cpu().numpy()
+    for h in range(H):
+        assert np.array_equal(ofl[0, h] != 0, Z[h][:, kw:kw + 128]), ("forward", h)
+        assert np.allclose(ofl[0, h][ofl[0, h] != 0], 1 / (128 * keep), rtol=2 ** -8)
+
+    # dK/dV kernel: one-hot dO rows on the row window.
+    G = zeros(n, v)
+    G[0, :, rw + np.arange(128), np.arange(128)] = 1.0
+    g = _dev(G, "bf16")
+    _, _, dv = E.bwd(q, k, val, o, g, L, 1.0, "bitmask", mdev, deterministic=True, **kw_)
+    torch.cuda.synchronize()
+    dvf = dv.float().cpu().numpy()
+    for h in range(H):
+        assert np.array_equal(dvf[0, h, kw:kw + 128].T != 0, Z[h][rw:rw + 128, kw:kw + 128]), ("dV", h)
+
+    # dQ kernel: one-hot K rows on the window, dP = 1.
+    K = zeros(nk, d)
+    cols = min(d, 128)
+    K[0, :, kw + np.arange(cols), np.arange(cols)] = 1.0
+    V, G = zeros(nk, v), zeros(n, v)
+    V[..., 0] = 1.0
+    G[..., 0] = 1.0
+    k, val, g = (_dev(x, "bf16") for x in (K, V, G))
+    o, L = E.fwd(q, k, val, 1.0, "bitmask", mdev, **kw_)
+    dq, _, _ = E.bwd(q, k, val, o, g, L, 1.0, "bitmask", mdev, deterministic=True, **kw_)
+    torch.cuda.synchronize()
+    dqf = dq.float().cpu().numpy()
+    D = o.float().cpu().numpy()[0, :, :, 0].astype(np.float64)  # D_i = <dO_i, O_i> from O as stored
+    for h in range(H):
+        mid = (0.5 / keep - D[h])[:, None] / 128  # halfway between the kept and the dropped value
+        assert np.array_equal(dqf[0, h][:, :cols] > mid, Z[h][:, kw:kw + cols]), ("dQ", h)
