@@ -632,7 +632,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // previous step's second phase, where the vector ALUs are otherwise idle.
   // The weights read them across the quad where they are applied.
   uint32_t dc[2][4] = {}, dm[2] = {0u, 0u};
-  const uint32_t dsh = 4u + (uint32_t)(lane & 3);
+  // A pair's keep mask for the packed bf16 weights comes from one byte
+  // permute: shifted left by 11 - query % 4 the call's bits put key 0's flag
+  // at bit 15 and key 2's at bit 31, shifted by 3 - query % 4 keys 1 and 3
+  // there, and v_perm_b32 replicates the top bit of bytes 1 and 3 of either.
+  const uint32_t shx = 11u - (uint32_t)(lane & 3), shy = 3u - (uint32_t)(lane & 3);
   const KeepConsts kq = keep_consts(p.drop.p8);
   auto draw_init = [&](int key0) {  // first key of the tile
 #pragma unroll
@@ -665,8 +669,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       default: return quad_bcast<3>(x);
     }
   };
-  auto keep_mask = [&](uint32_t bits, int r) -> uint32_t {  // all ones iff register r is kept
-    return (uint32_t)__builtin_amdgcn_sbfe((int)bits, dsh + 8u * (uint32_t)(r & 3), 1u);
+  // Mask of the bf16 pair of registers r, r + 1 (r % 4 in {0, 2}): each half
+  // all ones iff its key is kept.
+  auto pair_mask = [&](uint32_t bits, int r) -> uint32_t {
+    return __builtin_amdgcn_perm(bits << shy, bits << shx, (r & 3) == 0 ? 0x0A0A0808u : 0x0B0B0909u);
   };
 
   // This split's share of the key tiles [0, kt_end): [t0, kt_end).
@@ -764,10 +770,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int kb = pr / 8, r = 2 * (pr % 8);
         ls[pr % 4] = pr < 4 ? pe[pr][0] + pe[pr][1] : ls[pr % 4] + (pe[pr][0] + pe[pr][1]);
         if constexpr (DROP) {  // the PV product takes the kept weights; L the sum of all
-          const uint32_t bits = call_bits(4 * kb + r / 4);
-          const float z0 = __uint_as_float(__float_as_uint(pe[pr][0]) & keep_mask(bits, r));
-          const float z1 = __uint_as_float(__float_as_uint(pe[pr][1]) & keep_mask(bits, r + 1));
-          pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(z0, z1);
+          pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(pe[pr][0], pe[pr][1]) & pair_mask(call_bits(4 * kb + r / 4), r);
         } else {
           pk[kb][r / 8][(r / 2) % 4] = pack_bf16x2(pe[pr][0], pe[pr][1]);
         }
