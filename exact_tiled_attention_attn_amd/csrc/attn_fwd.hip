@@ -725,11 +725,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const __amdgpu_buffer_rsrc_t rv = make_rsrc_rows(Vb + (int64_t)k1 * vrow, nk - k1, vrow, vmax_rows);
       auto copy_item = [&](int i) {
         if (i < S::KWIN) {
-          const bool real = S::KWINS % S::NW == 0 || w + S::NW * i < S::KWINS;
+          // Every wave has a window for the first KWINS / NW copies: known at
+          // compile time, so only the last copy selects its source and target.
+          const bool real = S::KWINS % S::NW == 0 || i < S::KWINS / S::NW || w + S::NW * i < S::KWINS;
           dma16(real ? rk : rnone, real ? kcur + (w + S::NW * i) * 1024 : spare, koff[i]);
         } else if (i < S::KWIN + S::VWIN) {
           const int jv = i - S::KWIN;
-          const bool real = S::VWINS % S::NW == 0 || w + S::NW * jv < S::VWINS;
+          const bool real = S::VWINS % S::NW == 0 || jv < S::VWINS / S::NW || w + S::NW * jv < S::VWINS;
           dma16(real ? rv : rnone, real ? vnxt + (w + S::NW * jv) * 1024 : spare, voff[jv]);
         }
       };
