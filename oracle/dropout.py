@@ -68,6 +68,28 @@ def keep_mask(seed: int, unit: int, n: int, nk: int, p8: int) -> np.ndarray:
     return byte >= p8
 
 
+def keep_mask_at(seed: int, unit: int, rows, cols, p8: int) -> np.ndarray:
+    """Z at the pairs rows x cols of one unit (bool [len(rows), len(cols)]).
+
+    The decisions of ``keep_mask``, with one generator call per 4 x 4 block
+    of pairs the index sets touch instead of one per pair, for units too
+    large to draw pair by pair: block (a, b)'s word r holds the draws of row
+    4 a + r, byte e (least significant first) that of column 4 b + e.
+    """
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    bi, at_i = np.unique(rows // 4, return_inverse=True)
+    bj, at_j = np.unique(cols // 4, return_inverse=True)
+    words = np.stack(philox4x32_10(bj[None, :], bi[:, None], np.full((len(bi), len(bj)), unit), 0,
+                                   seed & _MASK32, seed >> 32))  # [word r, row block a, column block b]
+    draws = (words[:, :, :, None] >> (8 * np.arange(4, dtype=np.uint32))) & np.uint32(0xFF)  # [r, a, b, e]
+    kept = (draws >= p8).transpose(1, 0, 2, 3).reshape(4 * len(bi), 4 * len(bj))  # [4 a + r, 4 b + e]
+    ri, ci = 4 * at_i + rows % 4, 4 * at_j + cols % 4
+    if np.array_equal(ri, np.arange(kept.shape[0])) and np.array_equal(ci, np.arange(kept.shape[1])):
+        return kept
+    return kept[np.ix_(ri, ci)]
+
+
 def forward(Q, K, V, c, allowed, Z, p8):
     """Y, L of one unit with keep mask Z (L of the undropped softmax)."""
     Y0, m, ell, L = dense.forward(Q, K, V, c, allowed)
@@ -102,3 +124,40 @@ def vjp(Q, K, V, c, allowed, Z, p8, G, Y=None):
         D = np.sum(G * np.asarray(Y, np.float64), axis=1, keepdims=True)
     dS = P * (dPd - D)
     return c * (dS @ K), c * (dS.T @ Q), dV
+
+
+def output_rows(Q, K, V, c, allowed_rows, L, Z_rows, p8, rows):
+    """Rows of Y = (P o Z) V / keep, with P_ij = exp(c q_i.k_j - L_i) on A_i
+    and L the undropped softmax's logsumexp (from ``dense.forward``), for
+    units too large for ``forward``.  allowed_rows(r) and Z_rows(r) give
+    bool [len(r), nk]."""
+    Q, K, V, L = (np.asarray(x, np.float64) for x in (Q, K, V, L))
+    rows = np.asarray(rows)
+    A = allowed_rows(rows)
+    S = np.where(A, c * (Q[rows] @ K.T), -np.inf)
+    P = np.exp(S - L[rows, None])
+    keep = (256 - p8) / 256.0
+    return ((P * Z_rows(rows)) @ V) / keep
+
+
+def grads_sampled(Q, K, V, c, allowed_rows, G, L, Y, rows, cols, Z_r, Z_c, p8):
+    """dQ for sampled query rows and dK, dV for sampled key columns of <G, Y>
+    with the keep mask held fixed (the formulas of ``vjp``: dPd = (G V^T) o
+    Z / keep, dS = P o (dPd - D), D_i = <G_i, Y_i> from the given output of
+    every row), one output row or column at a time.  Z_r: Z[rows] (bool
+    [len(rows), nk]); Z_c: Z[:, cols] (bool [n, len(cols)])."""
+    Q, K, V, G, L, Y = (np.asarray(x, np.float64) for x in (Q, K, V, G, L, Y))
+    n = Q.shape[0]
+    rows, cols = np.asarray(rows), np.asarray(cols)
+    keep = (256 - p8) / 256.0
+    D = np.sum(G * Y, axis=1)
+    A = allowed_rows(rows)
+    P = np.exp(np.where(A, c * (Q[rows] @ K.T), -np.inf) - L[rows, None])
+    dS = P * ((G[rows] @ V.T) * Z_r / keep - D[rows, None])
+    dQ = c * (dS @ K)
+    Ac = allowed_rows(np.arange(n))[:, cols]
+    Pc = np.exp(np.where(Ac, c * (Q @ K[cols].T), -np.inf) - L[:, None])
+    dSc = Pc * ((G @ V[cols].T) * Z_c / keep - D[:, None])
+    dK = c * (dSc.T @ Q)
+    dV = (Pc * Z_c).T @ G / keep
+    return dQ, dK, dV

@@ -200,8 +200,10 @@ def allowance_full(Q, K, V, G, scale, A, Yd, L, dtype, Z=None, p8=0):
     return _allow(P, Pw, dS, _d_terms(G, Yd, E_O, dtype), V, G, K, Q, scale)
 
 
-def output_rounding_bound(Q, K, V, L, scale, A_rows, dtype, row_chunk=1024):
-    """allowance_full's O allowance for every row of a large unit, in row chunks."""
+def output_rounding_bound(Q, K, V, L, scale, A_rows, dtype, row_chunk=1024, Z_rows=None, p8=0):
+    """allowance_full's O allowance for every row of a large unit, in row
+    chunks (with dropout: the weights P Z / keep, Z_rows(r) the keep mask's
+    rows)."""
     if dtype != "bf16":
         return None
     Q, K, V, L = (np.asarray(x, np.float64) for x in (Q, K, V, L))
@@ -212,14 +214,17 @@ def output_rounding_bound(Q, K, V, L, scale, A_rows, dtype, row_chunk=1024):
         r = np.arange(r0, min(n, r0 + row_chunk))
         A = A_rows(r)
         P = np.where(A, np.exp(np.where(A, scale * (Q[r] @ K.T), 0.0) - L[r, None]), 0.0)
+        if Z_rows is not None:
+            P = P * Z_rows(r) * (256.0 / (256 - p8))
         out[r] = ROUND_LAMBDA * 2.0 ** -8 * np.sqrt(P ** 2 @ V2)
     return out
 
 
-def operand_rounding_bound(Q, K, V, G, Yd, L, E_O, scale, A_rows, rows, cols, dtype):
+def operand_rounding_bound(Q, K, V, G, Yd, L, E_O, scale, A_rows, rows, cols, dtype, Z_r=None, Z_c=None, p8=0):
     """allowance_full's dQ allowance for sampled rows and dK, dV allowances
-    for sampled key columns of a large unit (no dropout).  E_O: the O
-    allowance of every row (output_rounding_bound).  Returns {dQ, dK, dV}."""
+    for sampled key columns of a large unit.  E_O: the O allowance of every
+    row (output_rounding_bound).  With dropout Z_r = Z[rows], Z_c = Z[:, cols]
+    (allowance_full's weights and dS).  Returns {dQ, dK, dV}."""
     if dtype != "bf16":
         return {}
     Q, K, V, G, Yd, L = (np.asarray(x, np.float64) for x in (Q, K, V, G, Yd, L))
@@ -227,15 +232,17 @@ def operand_rounding_bound(Q, K, V, G, Yd, L, E_O, scale, A_rows, rows, cols, dt
     delta = np.sum(G * Yd, axis=1)
     T = _d_terms(G, Yd, E_O, dtype)
     rows, cols = np.asarray(rows), np.asarray(cols)
+    kr = 1.0 if Z_r is None else Z_r * (256.0 / (256 - p8))
+    kc = 1.0 if Z_c is None else Z_c * (256.0 / (256 - p8))
     Ar = A_rows(rows)
     Pr = np.where(Ar, np.exp(np.where(Ar, scale * (Q[rows] @ K.T), 0.0) - L[rows, None]), 0.0)
-    dSr = Pr * (G[rows] @ V.T - delta[rows, None])
-    out = {"dQ": _allow(Pr, Pr, dSr, T[rows], V, G, K, Q, scale, rows_only=True)["dQ"]}
+    dSr = Pr * (kr * (G[rows] @ V.T) - delta[rows, None])
+    out = {"dQ": _allow(Pr, Pr * kr, dSr, T[rows], V, G, K, Q, scale, rows_only=True)["dQ"]}
     Ac = A_rows(np.arange(n))[:, cols]
     Pc = np.where(Ac, np.exp(np.where(Ac, scale * (Q @ K[cols].T), 0.0) - L[:, None]), 0.0)
-    dSc = Pc * (G @ V[cols].T - delta[:, None])
+    dSc = Pc * (kc * (G @ V[cols].T) - delta[:, None])
     lam, c = ROUND_LAMBDA * 2.0 ** -8, abs(scale)
-    out["dV"] = lam * np.sqrt((Pc ** 2).T @ G ** 2)
+    out["dV"] = lam * np.sqrt(((Pc * kc) ** 2).T @ G ** 2)
     out["dK"] = lam * c * (np.sqrt((dSc ** 2).T @ Q ** 2) + np.sqrt((Pc * T[:, None]).T ** 2 @ Q ** 2))
     return out
 

@@ -223,3 +223,83 @@ def test_pipelined_kernels_keep_decisions_bit_exact(p, d):
     for h in range(H):
         mid = (0.5 / keep - D[h])[:, None] / 128  # halfway between the kept and the dropped value
         assert np.array_equal(dqf[0, h][:, :cols] > mid, Z[h][:, kw:kw + cols]), ("dQ", h)
+
+
+def test_dropout_full_size_headline():
+    """The headline workload (1 x 32 heads, n = 16384, d = v = 128, bf16,
+    causal) with dropout as `bench.py --dropout 0.1` runs it (seed 1234), in
+    that launch configuration: O and L on every row of three heads, dQ on
+    sampled rows and dK, dV on sampled key columns of those heads, against
+    the oracle's dropout forward and VJP with its own keep mask (drawn
+    block-wise: oracle/dropout.py keep_mask_at), D taken on the oracle's
+    output both as stored and exact."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import threadpoolctl
+
+    import exact_tiled_attention_attn_amd as E
+    from oracle import dense
+    from tests.gpu_common import margins_report, margins_scope, operand_rounding_bound, output_rounding_bound, to_dev
+
+    prob = W.generate("bf16_causal_h32_n16384_d128")
+    w = prob.w
+    n, p, seed = w.n, 0.1, 1234
+    p8 = dropout.p8_of(p)
+    heads = (0, 13, 31)
+    print("[dropout full size] device run", flush=True)
+    q, k, val, g = (to_dev(prob, x) for x in "QKVG")
+    kw = dict(dropout_p=p, dropout_seed=seed)
+    o, L = E.fwd(q, k, val, w.scale, "causal", None, **kw)
+    dq, dk, dv = E.bwd(q, k, val, o, g, L, w.scale, "causal", None, deterministic=True, **kw)
+    torch.cuda.synchronize()
+    got = {name: {h: t[0, h].float().cpu().numpy() for h in heads}
+           for name, t in (("O", o), ("L", L), ("dQ", dq), ("dK", dk), ("dV", dv))}
+    del q, k, val, g, o, L, dq, dk, dv
+    causal = prob.allowed(0)
+
+    def A_rows(r):
+        return causal[r]
+
+    def unit(h):
+        errs = {}
+
+        def check(name, gv, rv, extra=None):
+            errs[name] = max(errs.get(name, 0.0), compare(name[:2] if name != "L" else "L", gv, rv, "bf16",
+                                                          ("dropout full size", h, name), extra=extra))
+
+        Q, K, V, G = (getattr(prob, x)[0, h] for x in "QKVG")
+        L = dense.forward(Q, K, V, w.scale, causal)[3]  # the undropped softmax's logsumexp
+        Z = dropout.keep_mask_at(seed, h, np.arange(n), np.arange(n), p8)
+
+        def Z_rows(r):
+            return Z[r]
+
+        Y = np.concatenate([dropout.output_rows(Q, K, V, w.scale, A_rows, L, Z_rows, p8, np.arange(r0, min(n, r0 + 2048)))
+                            for r0 in range(0, n, 2048)])
+        E_O = output_rounding_bound(Q, K, V, L, w.scale, A_rows, "bf16", Z_rows=Z_rows, p8=p8)
+        check("O", got["O"][h], Y, E_O)
+        check("L", got["L"][h], L)
+        rng = np.random.default_rng(h)
+        rows = np.unique(np.concatenate([np.arange(128), np.arange(n - 128, n), rng.choice(n, 32, replace=False)]))
+        cols = np.unique(np.concatenate([np.arange(128), np.arange(n - 128, n), rng.choice(n, 32, replace=False)]))
+        Zr, Zc = Z[rows], Z[:, cols]
+        Ys = stored(Y, "bf16")
+        allow = operand_rounding_bound(Q, K, V, G, Ys, L, E_O, w.scale, A_rows, rows, cols, "bf16", Zr, Zc, p8)
+        for ref, Yd in (("stored", Ys), ("exact", Y)):
+            rq, rk, rv = dropout.grads_sampled(Q, K, V, w.scale, A_rows, G, L, Yd, rows, cols, Zr, Zc, p8)
+            check("dQ/" + ref, got["dQ"][h][rows], rq, allow.get("dQ"))
+            check("dK/" + ref, got["dK"][h][cols], rk, allow.get("dK"))
+            check("dV/" + ref, got["dV"][h][cols], rv, allow.get("dV"))
+        return errs
+
+    workers = max(1, min(len(heads), len(os.sched_getaffinity(0))))
+    threads = max(1, min(16, len(os.sched_getaffinity(0))) // workers)
+    print(f"[dropout full size] oracle on heads {heads}", flush=True)
+    total = {}
+    with margins_scope(), threadpoolctl.threadpool_limits(threads, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        for errs in ex.map(unit, heads):
+            for k_, v_ in errs.items():
+                total[k_] = max(total.get(k_, 0.0), v_)
+        print("dropout full size", {k_: f"{v_:.2e}" for k_, v_ in total.items()}, flush=True)
+        print(margins_report("dropout full size"), flush=True)

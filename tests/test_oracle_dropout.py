@@ -146,3 +146,44 @@ def test_dropout_vjp_row_term_from_a_forward_output(mask):
     Yp = Y0 * (1 + 1e-3 * rng.normal(size=Y0.shape))  # an output off by rounding-sized amounts
     for x, r in zip(dropout.vjp(Q, K, V, c, A, ones, 0, G, Yp), tiled.reverse(Q, K, V, c, A, nk, Yp, m, ell, G)):
         assert np.abs(x - r).max() <= 1e-12 * max(1.0, np.abs(r).max()), mask
+
+
+@pytest.mark.parametrize("n,nk", [(37, 53), (64, 96), (130, 70)])
+def test_keep_mask_at_index_sets(n, nk):
+    """The block-wise draw at arbitrary row and column sets (unsorted,
+    repeated blocks) gives keep_mask's decisions."""
+    rng = np.random.default_rng(n + nk)
+    for p8 in (1, 26, 128, 255):
+        Z = dropout.keep_mask(987654321987, 5, n, nk, p8)
+        r = rng.choice(n, 11, replace=False)
+        c = rng.choice(nk, 13, replace=False)
+        assert np.array_equal(dropout.keep_mask_at(987654321987, 5, r, c, p8), Z[r][:, c])
+    assert np.array_equal(dropout.keep_mask_at(3, 1, np.arange(n), np.arange(nk), 77),
+                          dropout.keep_mask(3, 1, n, nk, 77))
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "random"])
+def test_sampled_dropout_outputs_and_gradients(mask):
+    """output_rows and grads_sampled, one row or column at a time, equal the
+    whole-matrix forward and VJP (both taking D from the same Y)."""
+    rng = np.random.default_rng(11)
+    n, nk, d, v, p8, c = 41, 57, 8, 6, 40, 0.3
+    Q, K, V, G = (rng.standard_normal(s) for s in ((n, d), (nk, d), (nk, v), (n, v)))
+    A = None
+    if mask == "causal":
+        A = W.causal_allowed(n, nk=nk, offset=nk - n)
+    elif mask == "random":
+        A = rng.random((n, nk)) < 0.4
+        A[np.arange(n), rng.integers(0, nk, n)] = True
+    Z = dropout.keep_mask(42, 2, n, nk, p8)
+    Y, L = dropout.forward(Q, K, V, c, A, Z, p8)
+    Ah = np.ones((n, nk), bool) if A is None else A
+    rows, cols = np.array([0, 5, 17, 40]), np.array([1, 2, 30, 56])
+    Yr = dropout.output_rows(Q, K, V, c, lambda r: Ah[r], L, lambda r: Z[r], p8, rows)
+    assert np.allclose(Yr, Y[rows], rtol=1e-12, atol=1e-14)
+    Yd = Y + 1e-3 * rng.standard_normal(Y.shape)  # any output the reverse pass is handed
+    dQ, dK, dV = dropout.vjp(Q, K, V, c, A, Z, p8, G, Yd)
+    sQ, sK, sV = dropout.grads_sampled(Q, K, V, c, lambda r: Ah[r], G, L, Yd, rows, cols, Z[rows], Z[:, cols], p8)
+    assert np.allclose(sQ, dQ[rows], rtol=1e-10, atol=1e-13)
+    assert np.allclose(sK, dK[cols], rtol=1e-10, atol=1e-13)
+    assert np.allclose(sV, dV[cols], rtol=1e-10, atol=1e-13)
