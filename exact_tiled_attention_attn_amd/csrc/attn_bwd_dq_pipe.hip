@@ -149,6 +149,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     if constexpr (MASK == kMaskBitmask) return cls_s[kt];
     return classify_analytic(MASK, q0, S::BQ, (int64_t)kt * S::BK, S::BK, n, nk, coff);
   };
+  // Partially allowed among the visited (nonempty) tiles, with 32-bit scalar
+  // arithmetic: the first kt_full tiles are full (every key exists and, with
+  // the causal mask, is allowed for the tile's first row), later ones partial.
+  int kt_full = nk / S::BK;
+  if constexpr (MASK == kMaskCausal) {
+    const int r = q0 + coff - (S::BK - 1);  // last tile start a first-row-full tile can have
+    const int f = r < 0 ? 0 : r / S::BK + 1;
+    kt_full = f < kt_full ? f : kt_full;
+  }
+  auto tile_partial = [&](int kt) -> bool {
+    if constexpr (MASK == kMaskBitmask) return cls_s[kt] == kTilePartial;
+    return kt >= kt_full;
+  };
   auto next_tile = [&](int kt) -> int {  // next (higher) tile with an allowed pair, or -1
     if (kt < 0) return -1;
     if constexpr (MASK != kMaskBitmask) return kt + 1 < kt_end ? kt + 1 : -1;
@@ -277,7 +290,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     const bool real = !extra || w < nx;
     if (i % 4 == 0 || extra)  // group start, or the item that may be an empty copy
       set_m0(real ? tile + (first + 4 * (i / 4)) * 1024 : sp_l);  // an empty copy lands at sp_l + (i % 4) KB
-    fill16_off(real ? r : r_none, src[i], i % 4);
+    // An empty copy keeps the resource's address and takes an empty range.
+    fill16_off(i32x4{r[0], r[1], real ? r[2] : 0, r[3]}, src[i], i % 4);
   };
   auto kwin = [&](const i32x4& rk, int st, int i) { win_item(rk, ks_l + st * S::KTILE, kfirst, KB, KX, ksrc, i); };
   auto vwin = [&](const i32x4& rv, int st, int i) { win_item(rv, vs_l + st * S::VTILE, vfirst, VB, VX, vsrc, i); };
@@ -312,9 +326,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
   // The next in-step fill, planned in chunk 0's second phase (its scalar work
   // issues under the MFMAs): K / V resources, key tile and target stage.
   int fkt = -1;
+  // Without a bitmask the visited key tiles are consecutive (ascending): the
+  // next fill's resources follow from the previous ones by one tile's bytes.
+  // ak / av are the byte addresses of the planned tile's K and V rows, nkb /
+  // nvb the bytes from there to row nk, unclamped (they wrap once past the
+  // last tile, whose fills then take empty ranges, so neither value is used
+  // there; the resources take them clamped below 2^31).
+  uint64_t ak = 0, av = 0;
+  uint32_t nkb = 0, nvb = 0;
+  const uint32_t ck = (uint32_t)(S::BK * krow), cv = (uint32_t)(S::BK * vrow);
+  auto plan_start = [&](int kt) {  // state of tile kt (kt < 0 only ever precedes empty fills)
+    const int t = kt < 0 ? 0 : kt;
+    ak = reinterpret_cast<uint64_t>(Kb) + (uint64_t)((uint32_t)t * ck);
+    av = reinterpret_cast<uint64_t>(Vb) + (uint64_t)((uint32_t)t * cv);
+    nkb = (uint32_t)(nk - t * S::BK) * (uint32_t)krow;
+    nvb = (uint32_t)(nk - t * S::BK) * (uint32_t)vrow;
+  };
   auto plan_fill = [&](int kt, int st) {
-    frk = tile_words(Kb, kt, krow);
-    frv = tile_words(Vb, kt, vrow);
+    if constexpr (MASK == kMaskBitmask) {
+      frk = tile_words(Kb, kt, krow);
+      frv = tile_words(Vb, kt, vrow);
+    } else {  // kt is the tile above the previous plan's (or < 0)
+      ak += ck;
+      av += cv;
+      nkb -= ck;
+      nvb -= cv;
+      // Ranges are clamped below 2^31: padding slots read at offset 2^31
+      // (kPastEnd), which must stay out of range.
+      const bool live = kt >= 0;
+      const uint32_t bk = nkb < 0x7FFFFFFFu ? nkb : 0x7FFFFFFFu, bv = nvb < 0x7FFFFFFFu ? nvb : 0x7FFFFFFFu;
+      frk = i32x4{(int)(uint32_t)ak, (int)(uint32_t)(ak >> 32), live ? (int)bk : 0, 0x00020000};
+      frv = i32x4{(int)(uint32_t)av, (int)(uint32_t)(av >> 32), live ? (int)bv : 0, 0x00020000};
+    }
     fst = st;
     fkt = kt;
   };
@@ -558,6 +601,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     fill(t0, 0);
     fill(t1, 1);
     fill(t2, 2);
+    if constexpr (MASK != kMaskBitmask) plan_start(t2);
     wait_vm_n<2 * kF>();
     __syncthreads();
     f32x16 sa[2], pa[2], sb[2], pb[2];
@@ -574,7 +618,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_kernel(BwdParams p) {
     while (true) {
       const int st = (int)(j & (S::NSTAGE - 1)), nst = (int)((j + 1) & (S::NSTAGE - 1));
       const int k0 = t0 * S::BK;
-      const bool partial = tile_class(t0) == kTilePartial;
+      const bool partial = tile_partial(t0);
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, k0);
       step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1,

@@ -155,6 +155,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     if constexpr (MASK == kMaskBitmask) return cls_s[qt];
     return classify_analytic(MASK, (int64_t)qt * S::BQ, S::BQ, k0, S::BK, n, nk, coff);
   };
+  // Partially allowed among the visited (nonempty) tiles, with 32-bit scalar
+  // arithmetic: causal tiles from row t_full on are full when every key of
+  // the tile exists.
+  const bool keys_whole = k0 + S::BK <= nk;
+  int t_full = 0;
+  if constexpr (MASK == kMaskCausal) {
+    const int r_full = k0 + S::BK - 1 - coff;  // first query row that allows every key of the tile
+    t_full = r_full <= 0 ? 0 : (r_full + S::BQ - 1) / S::BQ;
+  }
+  auto tile_partial = [&](int qt) -> bool {
+    if constexpr (MASK == kMaskBitmask) return cls_s[qt] == kTilePartial;
+    if constexpr (MASK == kMaskCausal) return !(keys_whole && qt >= t_full);
+    return !keys_whole;
+  };
   auto next_tile = [&](int qt) -> int {  // next (lower) tile with an allowed pair, or -1
     if (qt < 0) return -1;
     if constexpr (MASK != kMaskBitmask) return qt - 1 >= qt_first ? qt - 1 : -1;
@@ -217,7 +231,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     const bool real = !extra || w < nx;
     if (i % 4 == 0 || extra)  // group start, or the item that may be an empty copy
       set_m0(real ? tile + (first + 4 * (i / 4)) * 1024 : sp_l);  // an empty copy lands at sp_l + (i % 4) KB
-    fill16_off(real ? r : r_none, src[i], i % 4);
+    // An empty copy keeps the resource's address and takes an empty range.
+    fill16_off(i32x4{r[0], r[1], real ? r[2] : 0, r[3]}, src[i], i % 4);
   };
   auto qwin = [&](const i32x4& rq, int st, int i) { win_item(rq, qs_l + st * S::QTILE, qfirst, QB, QX, qsrc, i); };
   auto owin = [&](const i32x4& ro, int st, int i) { win_item(ro, os_l + st * S::OTILE, ofirst, OB, OX, osrc, i); };
@@ -270,11 +285,49 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   // the query tile and the target stage.
   i32x4 frq, fro, frr;
   int fst = 0, fqt = -1;
+  // Without a bitmask the visited query tiles are consecutive (descending):
+  // the next fill's resources follow from the previous ones by one tile's
+  // bytes (a few scalar instructions per tile instead of a product and a
+  // clamp per tensor).  aq / ao / al are the byte addresses of the planned
+  // tile's Q, dO and row-statistic rows, nq / no the Q and dO bytes from
+  // there to row n (unsigned and unclamped: the host bounds (n - 1) rb + the
+  // row width by 2^31 - 1, so they stay below 2^32; the resources take them
+  // clamped); a planned tile below 0 gets empty ranges, so its address (then
+  // below the tensor) is never used.
+  uint64_t aq = 0, ao = 0, al = 0;
+  uint32_t nq = 0, no = 0;
+  const uint32_t cq = (uint32_t)(S::BQ * qrow), co = (uint32_t)(S::BQ * orow);
+  const uint32_t nl = w < 2 ? (uint32_t)(S::BQ * 4) : 0u;  // row statistics: waves 0 (L) and 1 (D)
+  auto plan_start = [&](int qt) {  // state of tile qt (any value; qt < 0 only ever precedes empty fills)
+    const int q = qt < 0 ? 0 : qt;
+    aq = reinterpret_cast<uint64_t>(Qb) + (uint64_t)((uint32_t)q * cq);
+    ao = reinterpret_cast<uint64_t>(dOb) + (uint64_t)((uint32_t)q * co);
+    al = reinterpret_cast<uint64_t>(w == 0 ? L2b : Dnb) + (uint64_t)q * (S::BQ * 4);
+    nq = (uint32_t)(n - q * S::BQ) * (uint32_t)qrow;
+    no = (uint32_t)(n - q * S::BQ) * (uint32_t)orow;
+  };
+  auto rsrc_at = [](uint64_t a, uint32_t nb) -> i32x4 {
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)nb, 0x00020000};
+  };
   auto plan_fill = [&](int qt, int st) {
-    frq = tile_words(Qb, qt, qrow);
-    fro = tile_words(dOb, qt, orow);
-    const float* src = (w == 0 ? L2b : Dnb) + (qt < 0 ? 0 : qt * S::BQ);
-    frr = (w < 2 && qt >= 0) ? rsrc_words(src, S::BQ * 4) : r_none;
+    if constexpr (MASK == kMaskBitmask) {
+      frq = tile_words(Qb, qt, qrow);
+      fro = tile_words(dOb, qt, orow);
+      const float* src = (w == 0 ? L2b : Dnb) + (qt < 0 ? 0 : qt * S::BQ);
+      frr = (w < 2 && qt >= 0) ? rsrc_words(src, S::BQ * 4) : r_none;
+    } else {  // qt is the tile below the previous plan's (or < 0)
+      aq -= cq;
+      ao -= co;
+      al -= S::BQ * 4;
+      nq += cq;
+      no += co;
+      // Ranges are clamped below 2^31: padding slots read at offset 2^31
+      // (kPastEnd), which must stay out of range.
+      const bool live = qt >= 0;
+      frq = rsrc_at(aq, live ? (nq < 0x7FFFFFFFu ? nq : 0x7FFFFFFFu) : 0u);
+      fro = rsrc_at(ao, live ? (no < 0x7FFFFFFFu ? no : 0x7FFFFFFFu) : 0u);
+      frr = rsrc_at(al, live ? nl : 0u);
+    }
     fst = st;
     fqt = qt;
   };
@@ -585,6 +638,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     fill(t0, 0);
     fill(t1, 1);
     fill(t2, 2);
+    if constexpr (MASK != kMaskBitmask) plan_start(t2);
     wait_vm_n<2 * kF>();
     __syncthreads();
     f32x16 sa, pa, sb, pb;
@@ -608,7 +662,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     while (true) {
       const int st = (int)(j & (S::NSTAGE - 1)), nst = (int)((j + 1) & (S::NSTAGE - 1));
       const int q0 = t0 * S::BQ;
-      const bool partial = tile_class(t0) == kTilePartial;
+      const bool partial = tile_partial(t0);
       // chunk 0 of t0
       if (partial) mask_chunk(sa, st, 0, q0);
       step(std::false_type{}, sa, pa, sb, pb, st, 0, st, 1, dnA, std::false_type{}, dnA,
