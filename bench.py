@@ -11,7 +11,11 @@ allowed (query, key) pairs; ``roofline`` reports the dominant kernel's
 algorithmic FLOPs per launch over its average launch duration (HIP events
 recorded by the library on the launch stream) against the dense MFMA peak
 of the dtype; ``cpu_baseline`` times the float64 oracle on the host cores on
-a bounded sample (one (batch, head) unit, sub-sized if needed).
+a bounded sample (one (batch, head) unit, sub-sized if needed);
+``sclk`` holds the engine clock and board power sampled over a separate run
+of the same steps, and ``gemm_ceiling`` the vendor GEMM's throughput on
+random operands of the same dtype on the same board (the practical ceiling
+under its power limit), against which ``roofline.frac_of_gemm`` is taken.
 """
 
 from __future__ import annotations
@@ -71,6 +75,7 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the engine-clock sampling run")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the vendor-GEMM ceiling measurement")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--deterministic", type=int, default=1, choices=(0, 1),
                     help="backward dQ path: 1 = query-tile-outer kernel (default), 0 = fp32 atomics")
@@ -184,18 +189,18 @@ def cpu_baseline(prob, budget_s: float) -> dict:
 
 
 class ClockSampler:
-    """Samples the GPU engine clock on a host thread: the mean over the XCDs
-    of amdsmi's current GFX clocks (the firmware's metrics table).  The table
-    refreshes slowly, so the bench samples a separate run of the same steps
-    lasting a second or more, after the timed steps, and keeps the samples
-    past its first half second.  A missing or failing amdsmi gives no
-    samples, not an error."""
+    """Samples the GPU engine clock and the board power on a host thread: the
+    mean over the XCDs of amdsmi's current GFX clocks and the socket power of
+    the firmware's metrics table.  The table refreshes slowly, so the bench
+    samples a separate run of the same work lasting a second or more, after
+    the timed steps, and keeps the samples past its first half second.  A
+    missing or failing amdsmi gives no samples, not an error."""
 
     def __init__(self, period_s: float = 0.01, settle_s: float = 0.5):
         import threading
 
         self.period, self.settle = period_s, settle_s
-        self.samples = []
+        self.samples = []  # (clock MHz, power W or None)
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
         self._handle = None
@@ -212,8 +217,16 @@ class ClockSampler:
         m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
         clks = [float(x) for x in m.get("current_gfxclks", []) if isinstance(x, (int, float))]
         if clks:
-            return sum(clks) / len(clks)
-        return float(self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)["clk"])
+            clk = sum(clks) / len(clks)
+        else:
+            clk = float(self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)["clk"])
+        pw = None
+        for key in ("current_socket_power", "average_socket_power"):
+            x = m.get(key)
+            if isinstance(x, (int, float)) and 0 < x < 65535:
+                pw = float(x)
+                break
+        return clk, pw
 
     def _run(self):
         t0 = time.perf_counter()
@@ -241,14 +254,56 @@ class ClockSampler:
             except Exception:
                 pass
 
-    def summary(self):
+    def summary(self, what="the same steps"):
         if not self.samples:
             return None
-        x = sorted(self.samples)
-        return {"median_mhz": round(x[len(x) // 2], 1), "min_mhz": round(x[0], 1), "max_mhz": round(x[-1], 1),
-                "samples": len(x),
-                "source": "amdsmi current GFX clocks (mean over XCDs), sampled every 10 ms past the first 0.5 s "
-                          "of a separate >= 1.5 s run of the same steps after the timed ones"}
+        x = sorted(c for c, _ in self.samples)
+        out = {"median_mhz": round(x[len(x) // 2], 1), "min_mhz": round(x[0], 1), "max_mhz": round(x[-1], 1),
+               "samples": len(x),
+               "source": "amdsmi current GFX clocks (mean over XCDs), sampled every 10 ms past the first 0.5 s "
+                         f"of a separate >= 1.5 s run of {what} after the timed ones"}
+        pw = sorted(p for _, p in self.samples if p is not None)
+        if pw:
+            out["power_w"] = {"median": round(pw[len(pw) // 2], 1), "max": round(pw[-1], 1),
+                              "source": "amdsmi socket power, same samples"}
+        return out
+
+
+def gemm_ceiling(torch, dtype_name: str, seconds: float = 1.5, size: int = 8192):
+    """A practical MFMA ceiling on this board: torch.matmul (the vendor GEMM
+    library) on N(0,1) operands of the workload's dtype, size^3, run for a
+    second or more with the same clock and power sampling.  The published
+    peak assumes the 2.4 GHz clock; with random operands the board's power
+    limit holds every MFMA-dense kernel below it."""
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(size, size, device="cuda:0", dtype=torch.float32, generator=g).to(dt)
+    b = torch.randn(size, size, device="cuda:0", dtype=torch.float32, generator=g).to(dt)
+    c = torch.empty(size, size, device="cuda:0", dtype=dt)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with ClockSampler() as clock:
+        n, start = 0, time.perf_counter()
+        t0.record()
+        while time.perf_counter() - start < seconds:
+            torch.matmul(a, b, out=c)
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        t1.record()
+        torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n
+    del a, b, c
+    out = {"kind": f"torch.matmul {dtype_name} {size}x{size}x{size}, N(0,1) operands",
+           "tflops": round(2.0 * size ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4)}
+    s = clock.summary("the same products")
+    if s:
+        out["sclk_mhz"] = s["median_mhz"]
+        if "power_w" in s:
+            out["power_w"] = s["power_w"]["median"]
+    return out
 
 
 def main():
@@ -393,6 +448,12 @@ def main():
         # clock measured during the steps:
         at = peak * sclk["median_mhz"] / 2400.0
         out["roofline"].update(peak_at_sclk=round(at, 1), frac_at_sclk=round(achieved / at, 4))
+    if not args.no_ceiling:
+        # The vendor GEMM on random operands, on the same board under the same
+        # power limit: the practical ceiling for MFMA-dense work here.
+        ceil = gemm_ceiling(torch, w.dtype)
+        out["gemm_ceiling"] = ceil
+        out["roofline"]["frac_of_gemm"] = round(achieved / ceil["tflops"], 4)
     if args.dropout:
         out["config"].update(dropout_p=args.dropout, dropout_seed=1234)
     if nq != w.n:

@@ -44,3 +44,18 @@ def test_recorded_traffic_follows_the_kernel_sources():
     assert any(line.startswith("bwd.source_sha256=") for line in lines)
     assert b.recorded_traffic("no_such_workload", 1, "bwd") is None
     assert len(b.source_sha("bwd")) == 16 and b.source_sha("bwd") != b.source_sha("fwd")
+
+
+def test_clock_and_power_summary():
+    b = _bench()
+    s = b.ClockSampler.__new__(b.ClockSampler)  # no amdsmi needed for the summary
+    s.samples = []
+    assert s.summary() is None
+    s.samples = [(1900.0, 1350.0), (2000.0, None), (1800.0, 1370.0)]
+    out = s.summary("the same products")
+    assert out["median_mhz"] == 1900.0 and out["min_mhz"] == 1800.0 and out["max_mhz"] == 2000.0
+    assert out["samples"] == 3 and "the same products" in out["source"]
+    # power: the median over the samples that carry one
+    assert out["power_w"]["median"] == 1370.0 and out["power_w"]["max"] == 1370.0
+    s.samples = [(1900.0, None)]
+    assert "power_w" not in s.summary()
