@@ -70,12 +70,13 @@ def recorded_traffic(workload: str, deterministic: int, kernel: str):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the engine-clock sampling run")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the vendor-GEMM ceiling measurement")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache pass (512 MiB scrub before each step)")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--deterministic", type=int, default=1, choices=(0, 1),
                     help="backward dQ path: 1 = query-tile-outer kernel (default), 0 = fp32 atomics")
@@ -376,14 +377,41 @@ def main():
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # Per-step events on the same stream give the median and spread; the
+    # value is the whole timed region over K steps.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     kern = E.timing_read()
     E.timing_enable(False)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    # Cold-cache pass (outside the timed region): a 512 MiB buffer is
+    # rewritten before each step, so that L2 and the memory-side cache hold
+    # none of the inputs when the step starts; each step timed on its own.
+    cold = None
+    if not args.no_cold:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ms = []
+        for _ in range(args.steps):
+            scrub.fill_(1)
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b_.record(stream)
+            b_.synchronize()
+            cold_ms.append(a.elapsed_time(b_))
+        del scrub
+        cold_ms.sort()
+        med = cold_ms[len(cold_ms) // 2]
+        cold = {"ms_per_step_median": round(med, 4), "ms_per_step_min": round(cold_ms[0], 4),
+                "value": round((f_fwd + f_bwd) / (med * 1e-3) / 1e12, 2), "steps": args.steps,
+                "scrub": "512 MiB device buffer rewritten before each step"}
     # Engine clock under this load (outside the timed region).
     sclk = None
     if not args.no_clock:
@@ -442,6 +470,9 @@ def main():
                      "traffic": (recorded_traffic(w.name, args.deterministic, dominant)
                                  if nq == w.n and not args.dropout else None)},
         "sclk": sclk,
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                    "max": round(per_step[-1], 4), "source": "HIP events between the timed steps"},
+        "cold": cold,
     }
     if sclk:
         # The published peak assumes the 2.4 GHz engine clock; against the
