@@ -36,7 +36,7 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc")
 # reported only while these are unchanged).
 KERNEL_SOURCES = {
     "fwd": ["attn_fwd.hip", "kern_common.h"],
-    "bwd": ["attn_bwd.hip", "attn_bwd_kv.hip", "kern_common.h"],
+    "bwd": ["attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_kv2.hip", "kern_common.h"],
     "bwd_dq": ["attn_bwd_dq.hip", "attn_bwd_dq_pipe.hip", "kern_common.h"],
     "bwd_pre": ["attn_aux.hip"],
     "bwd_post": ["attn_aux.hip"],

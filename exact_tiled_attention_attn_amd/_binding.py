@@ -302,14 +302,15 @@ def bwd_noalloc(q, k, v, o, do, lse, scale, mask_mode="none", mask=None, *, dq=N
     return dq, dk, dv
 
 
-def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=0, causal_offset=0):
+def debug_tile_map(q, k, v, scale, mask_mode="none", mask=None, is_bwd=0, causal_offset=0, deterministic=True):
     """The kernels' (query tile x key tile) classification as uint8 [units, tq, tk].
 
-    is_bwd: 0 forward, 1 key-tile-outer backward, 2 query-tile-outer dQ.
+    is_bwd: 0 forward, 1 key-tile-outer backward, 2 query-tile-outer dQ; the
+    key-tile-outer tiling depends on the dQ path (``deterministic``, as in bwd).
     """
     lib = load_library()
     o_like = torch.empty((*q.shape[:3], v.shape[-1]), device="meta")  # strides of a contiguous O
-    p = make_problem(q, k, v, o_like, scale, mask_mode, mask, causal_offset=causal_offset)
+    p = make_problem(q, k, v, o_like, scale, mask_mode, mask, deterministic, causal_offset)
     bq, bk, tq, tk = (ctypes.c_int32() for _ in range(4))
     _check(lib.attn_debug_tile_map(ctypes.byref(p), int(is_bwd), None, 0, ctypes.byref(bq),
                                    ctypes.byref(bk), ctypes.byref(tq), ctypes.byref(tk), None, 0,

@@ -20,8 +20,8 @@ OUT = os.path.join(HERE, "libattn.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_dq.hip", "attn_bwd_dq_pipe.hip",
-           "attn_aux.hip", "attn_scratch.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_kv.hip", "attn_bwd_kv2.hip", "attn_bwd_dq.hip",
+           "attn_bwd_dq_pipe.hip", "attn_aux.hip", "attn_scratch.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",

@@ -62,7 +62,10 @@ Tiles fwd_tiles(const attn_problem& p) {
 }
 Tiles bwd_tiles(const attn_problem& p) {
   const int bq = p.dtype == ATTN_BF16 ? eta::kBwdBq : 32;
-  return Tiles{bq, eta::kBwdBk, cdiv(p.n, bq), cdiv(nkeys(p), eta::kBwdBk)};
+  const int bk = eta::bwd_kv2_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, p.deterministic == 0, drop_p8(p))
+                     ? eta::kBwdKv2Bk
+                     : eta::kBwdBk;
+  return Tiles{bq, bk, cdiv(p.n, bq), cdiv(nkeys(p), bk)};
 }
 
 int64_t row_pad(int64_t n) { return cdiv(n, eta::kRowPad) * eta::kRowPad; }
@@ -78,7 +81,8 @@ Tiles dq_tiles(const attn_problem& p) {
 
 struct Layout {
   size_t total = 0;
-  size_t off_D = 0, off_L2 = 0, off_dQ = 0, off_map = 0, off_map_dq = 0;
+  size_t off_D = 0, off_L2 = 0, off_Ls = 0, off_dQ = 0, off_map = 0, off_map_dq = 0;
+  size_t ls_bytes = 0;
   size_t map_bytes = 0, map_dq_bytes = 0, dq_bytes = 0;
   int splits = 1;  // forward key-range splits
   size_t off_Op = 0, off_Lp = 0, op_bytes = 0, lp_bytes = 0;
@@ -100,7 +104,8 @@ int dq_split_count(const attn_problem& p) {
 }
 
 // Backward workspace: D and L log2(e) (fp32 [B,H,n_pad] each, n_pad = n
-// rounded up to kRowPad); the atomic path adds the fp32 dQ accumulator, the
+// rounded up to kRowPad), and -L log2(e) / (c log2(e)) alike for the
+// two-waves-per-SIMD dK / dV kernel; the atomic path adds the fp32 dQ accumulator, the
 // deterministic path the bitmask map at the dQ tiling and, when the dQ
 // kernel splits the key range, its fp32 partials (splits x [B,H,n,d]).
 Layout plan(const attn_problem& p, int is_bwd) {
@@ -113,7 +118,11 @@ Layout plan(const attn_problem& p, int is_bwd) {
     const size_t rows = size_t(units) * size_t(row_pad(p.n));
     l.off_D = 0;
     l.off_L2 = align_up(size_t(4) * rows);
-    l.off_dQ = l.off_L2 + align_up(size_t(4) * rows);
+    l.off_Ls = l.off_L2 + align_up(size_t(4) * rows);
+    l.ls_bytes = eta::bwd_kv2_supported(p.dtype == ATTN_BF16, p.d, p.v, p.mask_mode, !det, drop_p8(p))
+                     ? size_t(4) * rows
+                     : 0;
+    l.off_dQ = l.off_Ls + align_up(l.ls_bytes);
     l.dq_bytes = det ? 0 : size_t(4) * units * p.n * p.d;
     l.off_map = l.off_dQ + align_up(l.dq_bytes);
     l.map_bytes = bitmask ? size_t(mask_units(p) * t.tq * t.tk) : 0;
@@ -437,6 +446,7 @@ attn_status attn_bwd(const attn_problem* p, const void* Q, const void* K, const 
   b.L = L;
   b.Dn = reinterpret_cast<float*>(wsb + lay.off_D);
   b.L2 = reinterpret_cast<float*>(wsb + lay.off_L2);
+  b.Ls = lay.ls_bytes ? reinterpret_cast<float*>(wsb + lay.off_Ls) : nullptr;
   b.n_pad = row_pad(p->n);
   b.dQacc = lay.dq_bytes ? reinterpret_cast<float*>(wsb + lay.off_dQ) : nullptr;
   b.dQ = dQ;

@@ -7,8 +7,9 @@
 //   page, part 3).  Integer OR/AND over the mask words: HBM-bound.
 // * bwd_pre_kernel: D_i = <dO_i, O_i> in fp32 (HarshvardhanJ README,
 //   backward section: D costs O(n d) and replaces a pass over P; ob1 page,
-//   part 2), L_i log2(e) for the base-2 exponentials of the backward, and,
-//   on the atomic path, clears the fp32 dQ accumulator.
+//   part 2), L_i log2(e) for the base-2 exponentials of the backward (and
+//   -L_i log2(e) / (c log2(e)) for the kernel whose score products start
+//   from it), and, on the atomic path, clears the fp32 dQ accumulator.
 // * bwd_post_kernel: dQ = c * accumulator, converted to the output type.
 #include "../../include/attn.h"
 #include "attn_internal.h"
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t zero_
     // apply 1 / P(keep) at the end (P(keep) = 1 - p8 / 256, exact in fp32).
     p.Dn[row] = -acc * ((float)(256u - p.drop.p8) * (1.f / 256.f));
     p.L2[row] = l2;
+    if (p.Ls != nullptr) p.Ls[row] = -l2 / (p.scale2 == 0.f ? 1e-30f : p.scale2);
   }
   // Clear the dQ accumulator (grid-stride over float4s).
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;

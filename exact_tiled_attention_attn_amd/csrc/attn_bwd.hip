@@ -545,6 +545,7 @@ static int launch_dims(const BwdParams& p, int d, int v, int mask_mode, bool fus
 }
 
 int launch_bwd(const BwdParams& p, int bf16, int d, int v, int mask_mode, bool fused, void* stream) {
+  if (bwd_kv2_supported(bf16, d, v, mask_mode, fused, p.drop.p8)) return launch_bwd_kv2(p, d, v, mask_mode, stream);
   if (!fused && bwd_kv_supported(bf16, d, v, mask_mode, p.tq))
     return launch_bwd_kv(p, d, v, mask_mode, stream);
   hipStream_t st = (hipStream_t)stream;

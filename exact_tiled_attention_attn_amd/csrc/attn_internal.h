@@ -13,6 +13,9 @@ constexpr int kFwdBq = 128;
 constexpr int kFwdBk = 64;
 constexpr int kBwdBq = 64;
 constexpr int kBwdBk = 128;
+// dK / dV kernel at two waves per SIMD (bf16, no dropout, none / causal
+// mask): 256-key tiles.
+constexpr int kBwdKv2Bk = 256;
 // Backward dQ (query-tile outer): the forward's tiling.
 constexpr int kDqBq = 128;
 constexpr int kDqBk = 32;
@@ -75,6 +78,10 @@ struct BwdParams {
   const float* L;
   float* Dn;     // -D_i = -<dO_i, O_i> (times P(keep) with dropout), fp32 [B, H, n_pad]
   float* L2;     // L_i log2(e) (+inf where L_i = -inf), fp32 [B, H, n_pad]
+  // -L2_i / scale2 (scale2 = c log2(e), or 1e-30 for c = 0), fp32 [B, H,
+  // n_pad], for the two-waves-per-SIMD dK / dV kernel (its score products
+  // start from it); null otherwise.
+  float* Ls;
   int64_t n_pad;  // row stride of Dn and L2: n rounded up to kRowPad; rows >= n hold 0 and L2 = +inf
   float* dQacc;  // fp32 [B, H, n, d] accumulator (unscaled by c)
   void* dQ;
@@ -143,6 +150,14 @@ int launch_bwd_dq(const BwdParams& p, int bf16, int d, int v, int mask_mode, voi
 // Pipelined dK / dV kernel of the deterministic path (bf16, d and v in {64, 128}).
 bool bwd_kv_supported(int bf16, int d, int v, int mask_mode, int64_t tq);
 int launch_bwd_kv(const BwdParams& p, int d, int v, int mask_mode, void* stream);
+// The two-waves-per-SIMD dK / dV kernel of the deterministic path: bf16,
+// (d, v) in {(128, 128), (64, 128), (64, 64)}, no dropout, none or causal
+// mask.  The key-tile-outer tiling (and its bitmask map) follows this choice.
+inline bool bwd_kv2_supported(int bf16, int64_t d, int64_t v, int mask_mode, bool fused, uint32_t drop_p8) {
+  if (!bf16 || fused || drop_p8 != 0 || mask_mode == 2) return false;
+  return (d == 128 && v == 128) || (d == 64 && v == 128) || (d == 64 && v == 64);
+}
+int launch_bwd_kv2(const BwdParams& p, int d, int v, int mask_mode, void* stream);
 // Pipelined dQ kernel of the deterministic path; the tiling of the dQ pass
 // (and of its bitmask tile map) follows this choice.
 inline bool bwd_dq_pipe_supported(int bf16, int64_t d, int64_t v, int mask_mode, int64_t nk) {

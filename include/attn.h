@@ -142,7 +142,10 @@ typedef struct {
  * few query tiles face many key tiles (bf16, d and v in {64, 128}, no
  * dropout), the partial results of the key-range splits, S B H n (v + 1) * 4
  * bytes for S <= 16 splits (0 bytes if neither applies).  Backward: D and
- * L log2(e) (4 B H n_pad bytes each, n_pad = n rounded up to 128), plus the
+ * L log2(e) (4 B H n_pad bytes each, n_pad = n rounded up to 128), plus
+ * -L log2(e) / (c log2(e)) alike when deterministic = 1 with bf16, (d, v) in
+ * {(128,128), (64,128), (64,64)}, no dropout and a none or causal mask (the
+ * two-waves-per-SIMD dK / dV kernel starts its score products from it), plus the
  * fp32 dQ accumulator (4 B H n d bytes) when deterministic = 0, plus the
  * bitmask tile map(s), plus, when deterministic = 1 and few query tiles face
  * many key tiles (bf16 with (d, v) in {(128,128), (64,128), (64,64)}), the

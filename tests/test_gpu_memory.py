@@ -57,8 +57,8 @@ def _step_peak(n, H=32, d=128, dtype=torch.bfloat16, mask="causal", seed=3):
           f"free memory fell by {free0 - free1} B, torch reserved {res1 - res0} B more", flush=True)
     assert peak == expected, (n, peak, expected)
     assert free0 - free1 <= res1 - res0, (n, free0 - free1, res1 - res0)
-    # The workspace is linear in n: D and L log2(e) rows (fp32), no n x n term.
-    assert ws_b == 2 * 4 * H * ((n + 127) // 128 * 128), ws_b
+    # The workspace is linear in n: D, L log2(e) and -L/c rows (fp32), no n x n term.
+    assert ws_b == 3 * 4 * H * ((n + 127) // 128 * 128), ws_b
     del q, k, val, do, o, L, dq, dk, dv
     return peak
 

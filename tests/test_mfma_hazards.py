@@ -65,6 +65,19 @@ def test_checker_catches_planted_hazards():
     assert check(chain) == []
 
 
+@pytest.mark.parametrize("src", ["attn_bwd_kv2.hip"])
+def test_kernel_m0_writes(src):
+    """A kernel whose MFMAs are compiler builtins (the compiler spaces them)
+    but whose grouped direct copies keep M0 between set_m0 statements:
+    nothing else may write M0."""
+    with tempfile.TemporaryDirectory() as d:
+        asm = open(compile_to_asm(os.path.join(CSRC, src), os.path.join(d, "k.s"))).read()
+    kernels = {k: v for k, v in functions(asm).items() if "kernel" in k}
+    assert kernels, "no kernels in the listing"
+    other = {k: m0_writers(v)[:3] for k, v in kernels.items() if m0_writers(v)}
+    assert not other, other
+
+
 @pytest.mark.parametrize("src", ["attn_bwd_kv.hip", "attn_bwd_dq_pipe.hip"])
 def test_kernel_wait_states(src):
     with tempfile.TemporaryDirectory() as d:
