@@ -35,6 +35,13 @@
 
 namespace eta {
 
+#ifndef ETA_KV2_PREFETCH_A
+#define ETA_KV2_PREFETCH_A 2
+#endif
+#ifndef ETA_KV2_PREFETCH_C
+#define ETA_KV2_PREFETCH_C 2
+#endif
+
 template <int D, int DV>
 struct Kv2Shape {
   static constexpr int NW = 8;
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   //   C: dV^T and dK^T on the matrix cores (operands read PC products ahead).
   constexpr int NA = S::NQF + S::NVF;          // phase A products
   constexpr int NB = 2 * (S::NDB + S::NVB);    // phase C products
-  constexpr int PA = 3, PC = 3;                // operand reads in flight
+  constexpr int PA = ETA_KV2_PREFETCH_A, PC = ETA_KV2_PREFETCH_C;  // operand reads in flight
   auto chunk = [&](int st, int c, int q0, bool partial, bool copies) {
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS;
     const char* ob = os + st * S::OTILE + 32 * c * S::OS;
