@@ -41,6 +41,13 @@ namespace eta {
 #ifndef ETA_KV2_PREFETCH_C
 #define ETA_KV2_PREFETCH_C 2
 #endif
+// Score-product read-ahead of the (128, 128) kernel without a mask: at depth
+// 2 its register allocation spills a copy offset inside the main loop, and
+// the reload's wait for all outstanding loads also waits for the tile copies
+// just issued; at depth 1 nothing spills.
+#ifndef ETA_KV2_PREFETCH_A_NOMASK
+#define ETA_KV2_PREFETCH_A_NOMASK 1
+#endif
 
 template <int D, int DV>
 struct Kv2Shape {
@@ -247,7 +254,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   //   C: dV^T and dK^T on the matrix cores (operands read PC products ahead).
   constexpr int NA = S::NQF + S::NVF;          // phase A products
   constexpr int NB = 2 * (S::NDB + S::NVB);    // phase C products
-  constexpr int PA = ETA_KV2_PREFETCH_A, PC = ETA_KV2_PREFETCH_C;  // operand reads in flight
+  constexpr int PA = (MASK == 0 && D == 128) ? ETA_KV2_PREFETCH_A_NOMASK : ETA_KV2_PREFETCH_A;  // operand reads in flight
+  constexpr int PC = ETA_KV2_PREFETCH_C;
   auto chunk = [&](int st, int c, int q0, bool partial, bool copies) {
     const char* qb = qs + st * S::QTILE + 32 * c * S::QS;
     const char* ob = os + st * S::OTILE + 32 * c * S::OS;
